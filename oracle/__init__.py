@@ -1,0 +1,223 @@
+"""CPU oracle for the 4-bit paged KV cache (test infrastructure only).
+
+This package is the slow, plainly written reference the HIP library is checked
+against.  Only the test suite, the smoke check and the CPU-baseline leg of the
+benchmark may import it; the product path (``bit_quantized_kv_amd``) never
+does.  It shares no code with the HIP library: the arithmetic lives in
+``kvq_oracle.c`` (plain C, fp32 quantization decisions, fp64 attention), built
+with gcc into ``libkvq_oracle.so``, and this module only marshals numpy arrays.
+
+Formats follow the pages "SGLang's 4-bit KV cache: the 56% is exact, the 1.78x
+is untested" (Figure 2 caption; section "The 56% survives its own scale, and
+names the block size") for NVFP4 and "KV cache in 4 bits: 8.8 instead of 4.7
+full sessions on the same four RTX 5090s" (section "What we changed") for the
+INT4 per-token-head cache.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+NVFP4 = 1
+INT4 = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libkvq_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (IEEE fp32/fp64: no fast-math, no FMA
+    contraction) and return the path of the shared library."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    cmd = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
+           "-shared", _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64, f32, f64, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
+    sig = {
+        "kvqo_e2m1_value": (f64, [i32]),
+        "kvqo_e4m3_value": (f64, [i32]),
+        "kvqo_e2m1_encode": (i32, [f32]),
+        "kvqo_e4m3_encode": (i32, [f32]),
+        "kvqo_bf16_rne": (ctypes.c_uint16, [f32]),
+        "kvqo_nvfp4_quantize_row": (None, [P, i32, f32, P, P]),
+        "kvqo_int4_quantize_row": (None, [P, i32, P, P]),
+        "kvqo_nvfp4_dequant_row": (None, [P, P, i32, f32, P]),
+        "kvqo_int4_dequant_row": (None, [P, f32, i32, P]),
+        "kvqo_slab_bytes": (sz, [i32, i32, i32]),
+        "kvqo_token_head_bytes": (sz, [i32, i32]),
+        "kvqo_quantize_store": (None, [i32, P, i32, i32, i32, P, P, P, i32, P]),
+        "kvqo_decode_attention": (None, [i32, P, i32, i32, i32, P, P, i32, P, i32, P, i32, f64, i64, P, P]),
+        "kvqo_dequant_prefix": (None, [i32, P, i32, i32, i32, P, P, i64, P, P, i64]),
+        "kvqo_num_threads": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+# ---------------------------------------------------------------- codecs
+
+def e2m1_value(code: int) -> float:
+    return _load().kvqo_e2m1_value(int(code))
+
+
+def e4m3_value(code: int) -> float:
+    return _load().kvqo_e4m3_value(int(code))
+
+
+def e2m1_encode(r: float) -> int:
+    return _load().kvqo_e2m1_encode(float(np.float32(r)))
+
+
+def e4m3_encode(s: float) -> int:
+    return _load().kvqo_e4m3_encode(float(np.float32(s)))
+
+
+def bf16_rne(x: float) -> int:
+    return _load().kvqo_bf16_rne(float(np.float32(x)))
+
+
+def nvfp4_quantize_row(x, gs: float = 1.0):
+    """One row of D fp32 values -> (codes uint8[D/2], scale codes uint8[D/16])."""
+    x = _f32(x)
+    D = x.shape[0]
+    codes = np.zeros(D // 2, np.uint8)
+    scales = np.zeros(D // 16, np.uint8)
+    _load().kvqo_nvfp4_quantize_row(_ptr(x), D, float(np.float32(gs)), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def int4_quantize_row(x):
+    """One row of D fp32 values -> (codes uint8[D/2], fp32 scale)."""
+    x = _f32(x)
+    D = x.shape[0]
+    codes = np.zeros(D // 2, np.uint8)
+    s = np.zeros(1, np.float32)
+    _load().kvqo_int4_quantize_row(_ptr(x), D, _ptr(codes), _ptr(s))
+    return codes, np.float32(s[0])
+
+
+def nvfp4_dequant_row(codes, scales, gs: float = 1.0) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    D = codes.shape[0] * 2
+    out = np.zeros(D, np.float64)
+    _load().kvqo_nvfp4_dequant_row(_ptr(codes), _ptr(scales), D, float(np.float32(gs)), _ptr(out))
+    return out
+
+
+def int4_dequant_row(codes, scale) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    D = codes.shape[0] * 2
+    out = np.zeros(D, np.float64)
+    _load().kvqo_int4_dequant_row(_ptr(codes), float(np.float32(scale)), D, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- pool level
+
+def slab_bytes(fmt: int, page_size: int, head_dim: int) -> int:
+    return int(_load().kvqo_slab_bytes(fmt, page_size, head_dim))
+
+
+def token_head_bytes(fmt: int, head_dim: int) -> int:
+    return int(_load().kvqo_token_head_bytes(fmt, head_dim))
+
+
+class Pool:
+    """One layer's paged cache on the host: uint8 [num_pages][Hkv][slab]."""
+
+    def __init__(self, fmt: int, num_pages: int, page_size: int, num_kv_heads: int, head_dim: int,
+                 global_scale=(1.0, 1.0), fill: int = 0):
+        self.fmt, self.num_pages, self.page_size = fmt, num_pages, page_size
+        self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
+        self.slab = slab_bytes(fmt, page_size, head_dim)
+        self.data = np.full((num_pages, num_kv_heads, self.slab), fill, np.uint8)
+        self.gs = _f32(global_scale).reshape(2)
+
+    def quantize_store(self, k, v, slot_mapping):
+        """k, v: [n_tok][Hkv][D] (fp32, or bf16 values already widened)."""
+        k, v, slots = _f32(k), _f32(v), _i32(slot_mapping)
+        n = slots.shape[0]
+        assert k.shape == (n, self.num_kv_heads, self.head_dim) and v.shape == k.shape
+        _load().kvqo_quantize_store(self.fmt, _ptr(self.data), self.page_size, self.num_kv_heads, self.head_dim,
+                                    _ptr(self.gs), _ptr(k), _ptr(v), n, _ptr(slots))
+
+    def decode_attention(self, q, block_table, seq_lens, sm_scale: float | None = None, split_tokens: int = 0):
+        """q: [B][Hq][D] (bf16 values widened to fp32).  Returns (out fp64
+        [B][Hq][D], lse fp64 [B][Hq])."""
+        q, bt, sl = _f32(q), _i32(block_table), _i32(seq_lens)
+        B, Hq, D = q.shape
+        assert D == self.head_dim and bt.shape[0] == B and sl.shape == (B,)
+        if sm_scale is None or sm_scale <= 0:
+            sm_scale = 1.0 / np.sqrt(D)
+        out = np.zeros((B, Hq, D), np.float64)
+        lse = np.zeros((B, Hq), np.float64)
+        _load().kvqo_decode_attention(self.fmt, _ptr(self.data), self.page_size, self.num_kv_heads, D, _ptr(self.gs),
+                                      _ptr(q), Hq, _ptr(bt), bt.shape[1], _ptr(sl), B, float(sm_scale),
+                                      int(split_tokens), _ptr(out), _ptr(lse))
+        return out, lse
+
+    def dequant_prefix(self, pages, prefix_len: int, out_token_stride: int | None = None):
+        """Returns (k_out, v_out) as uint16 bf16 bit patterns [prefix_len][Hkv][D]
+        (or [prefix_len][out_token_stride] when a wider stride is given)."""
+        pages = _i32(pages)
+        Hkv, D = self.num_kv_heads, self.head_dim
+        stride = out_token_stride or Hkv * D
+        k_out = np.zeros((prefix_len, stride), np.uint16)
+        v_out = np.zeros((prefix_len, stride), np.uint16)
+        _load().kvqo_dequant_prefix(self.fmt, _ptr(self.data), self.page_size, Hkv, D, _ptr(self.gs), _ptr(pages),
+                                    int(prefix_len), _ptr(k_out), _ptr(v_out), int(stride))
+        if out_token_stride is None:
+            return k_out.reshape(prefix_len, Hkv, D), v_out.reshape(prefix_len, Hkv, D)
+        return k_out, v_out
+
+    def dequant_token(self, page: int, g: int, off: int, kv: int) -> np.ndarray:
+        """Exact fp64 value of one stored row (kv 0 = K, 1 = V)."""
+        P, D = self.page_size, self.head_dim
+        slab = self.data[page, g]
+        half = slab[: self.slab // 2] if kv == 0 else slab[self.slab // 2:]
+        codes = half[off * (D // 2):(off + 1) * (D // 2)]
+        if self.fmt == NVFP4:
+            sc0 = P * (D // 2) + off * (D // 16)
+            return nvfp4_dequant_row(codes, half[sc0:sc0 + D // 16], float(self.gs[kv]))
+        sc0 = P * (D // 2) + off * 4
+        return int4_dequant_row(codes, half[sc0:sc0 + 4].view(np.float32)[0])
+
+
+def num_threads() -> int:
+    return int(_load().kvqo_num_threads())

@@ -1,0 +1,475 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one oracle function to a value the pages print, a library
+routine (torch's float8_e4m3fn / bfloat16 casts, torch's fp64 attention), a
+closed form worked out by hand, an invariant, or brute force on tiny inputs,
+so that a dropped term, a wrong sign, a wrong index or a transposed operand
+in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_kv_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------- footprints
+
+def test_footprint_matches_page_figures(oracle):
+    g = golden("footprint_pages.json")
+    D = 256
+    nv = oracle.token_head_bytes(oracle.NVFP4, D)
+    fp8 = 2 * D  # one byte per K and V value
+    assert nv / fp8 == g["nvfp4_ratio_vs_fp8"]["value"]
+    # bits per element = 4 + 8/B with an 8-bit block scale -> B
+    slab = oracle.slab_bytes(oracle.NVFP4, 16, D)
+    bits_per_elem = Fraction(8 * slab, 2 * 16 * D)
+    B = Fraction(8) / (bits_per_elem - 4)
+    assert B == g["nvfp4_block_size_from_ratio"]["value"]
+    # and the oracle really writes one scale byte per 16 elements
+    codes, scales = oracle.nvfp4_quantize_row(np.ones(D, np.float32))
+    assert codes.size == D // 2 and scales.size == D // 16 and scales.dtype == np.uint8
+    t = g["qwen38_27b_per_token_elements"]
+    per_token_nv = t["layers"] * t["kv_heads"] * nv
+    per_token_fp8 = t["layers"] * t["kv_heads"] * fp8
+    assert t["layers"] * t["kv_heads"] * t["head_dim"] * 2 == t["value"]
+    assert per_token_fp8 == g["qwen38_27b_per_token_fp8_bytes"]["value"]
+    assert per_token_nv == g["qwen38_27b_per_token_nvfp4_bytes"]["value"]
+    assert oracle.token_head_bytes(oracle.INT4, D) == g["int4_bytes_per_head_token_d256"]["value"]
+    for key in ("int4_page_bytes_800", "int4_page_bytes_1600"):
+        assert oracle.slab_bytes(oracle.INT4, g[key]["page_size"], D) == g[key]["value"]
+
+
+# ----------------------------------------------------------------- E4M3
+
+def test_e4m3_decode_all_codes_match_torch(oracle):
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        v = oracle.e4m3_value(c)
+        if np.isnan(ref[c]):
+            assert math.isnan(v), c
+        else:
+            assert v == ref[c], c
+    assert oracle.e4m3_value(0x7E) == 448.0
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9
+
+
+def _torch_e4m3_code(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_encode_matches_torch_rne(oracle):
+    r = np.random.default_rng(7)
+    vals = [np.float32(0.0)]
+    # log-uniform sweep over the whole range including subnormals and below
+    vals += list((2.0 ** r.uniform(-12, np.log2(448.0), 4000)).astype(np.float32))
+    # every midpoint between neighbouring finite codes (exact ties)
+    for c in range(0x7E):
+        a, b = oracle.e4m3_value(c), oracle.e4m3_value(c + 1)
+        vals.append(np.float32((a + b) / 2))
+        vals.append(np.nextafter(np.float32((a + b) / 2), np.float32(0)))
+        vals.append(np.nextafter(np.float32((a + b) / 2), np.float32(1e9)))
+    # below the smallest subnormal: 2^-10 ties to 0, 1.5*2^-10 rounds up
+    vals += [np.float32(2.0 ** -10), np.float32(1.5 * 2.0 ** -10), np.float32(2.0 ** -11)]
+    vals = np.array(vals, np.float32)
+    ref = _torch_e4m3_code(vals)
+    got = np.array([oracle.e4m3_encode(v) for v in vals])
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(vals[i], got[i], ref[i]) for i in bad[:5]]
+
+
+def test_e4m3_encode_saturates(oracle):
+    for v in (448.0, 449.0, 464.0, 500.0, 1e20, float("inf")):
+        assert oracle.e4m3_encode(v) == 0x7E
+
+
+# ----------------------------------------------------------------- E2M1
+
+def test_e2m1_decode_value_set(oracle):
+    # the OCP FP4 (E2M1) value set: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for c in range(8):
+        assert oracle.e2m1_value(c) == mags[c]
+        assert oracle.e2m1_value(c | 8) == -mags[c]
+    assert math.copysign(1.0, oracle.e2m1_value(8)) == -1.0
+    # every E2M1 value is exactly an E4M3 value (torch's cast reproduces it)
+    allv = np.array([oracle.e2m1_value(c) for c in range(16)], np.float32)
+    back = torch.from_numpy(allv).to(torch.float8_e4m3fn).to(torch.float32).numpy()
+    assert np.array_equal(back, allv)
+
+
+def test_e2m1_encode_ties_to_even_code(oracle):
+    # midpoints between neighbouring magnitudes go to the neighbour whose code
+    # has a zero mantissa bit (IEEE round-half-to-even on a 1-bit mantissa)
+    ties = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0}
+    for r, want in ties.items():
+        assert oracle.e2m1_value(oracle.e2m1_encode(r)) == want
+        assert oracle.e2m1_value(oracle.e2m1_encode(-r)) == -want
+
+
+def test_e2m1_encode_nearest_brute_force(oracle):
+    # brute force: no code is strictly nearer than the chosen one
+    r = np.random.default_rng(3)
+    xs = np.concatenate([r.uniform(-8, 8, 3000), np.arange(-7, 7.01, 0.125)]).astype(np.float32)
+    for x in xs:
+        c = oracle.e2m1_encode(x)
+        d = abs(float(x) - oracle.e2m1_value(c))
+        for cc in range(16):
+            assert d <= abs(float(x) - oracle.e2m1_value(cc)) + 0.0
+        if x != 0:
+            assert (c >> 3) == (1 if x < 0 else 0)
+
+
+def test_e2m1_encode_saturation_and_signed_zero(oracle):
+    for x in (6.0, 6.5, 7.0, 100.0, 1e30, float("inf")):
+        assert oracle.e2m1_encode(x) == 0x7
+        assert oracle.e2m1_encode(-x) == 0xF
+    assert oracle.e2m1_encode(0.0) == 0x0
+    assert oracle.e2m1_encode(-0.0) == 0x8
+
+
+def test_e2m1_grid_roundtrip(oracle):
+    for c in range(16):
+        assert oracle.e2m1_encode(oracle.e2m1_value(c)) == c
+
+
+# ----------------------------------------------------------------- NVFP4 rows
+
+def test_nvfp4_worked_example_by_hand(oracle):
+    # Block {1, 0.5, -1, 0, ...}: amax 1, s_raw = fp32(1/6); the nearest E4M3
+    # value is 11/64 = 0.171875 (neighbours 10/64 and 12/64); elements become
+    # round(64/11) = 6, round(32/11) = 3 -> 6*11/64 = 1.03125, 3*11/64 = 0.515625.
+    x = np.zeros(16, np.float32)
+    x[:3] = [1.0, 0.5, -1.0]
+    codes, scales = oracle.nvfp4_quantize_row(x)
+    assert oracle.e4m3_value(int(scales[0])) == 11 / 64
+    out = oracle.nvfp4_dequant_row(codes, scales)
+    assert list(out[:4]) == [1.03125, 0.515625, -1.03125, 0.0]
+    assert np.all(out[4:] == 0)
+    # with a 6 in the block the same values come back exactly
+    x[3] = 6.0
+    codes, scales = oracle.nvfp4_quantize_row(x)
+    assert list(oracle.nvfp4_dequant_row(codes, scales)[:4]) == [1.0, 0.5, -1.0, 6.0]
+
+
+def test_nvfp4_scale_code_matches_torch_cast(oracle):
+    # with gs = 1 the block scale code is the E4M3 cast of fp32(amax / 6)
+    r = np.random.default_rng(11)
+    for trial in range(200):
+        x = (r.standard_normal(256) * np.exp(r.normal(0, 2))).astype(np.float32)
+        codes, scales = oracle.nvfp4_quantize_row(x)
+        amax = np.abs(x.reshape(16, 16)).max(axis=1).astype(np.float32)
+        s_raw = (amax / np.float32(6.0)).astype(np.float32)
+        s_raw = np.minimum(s_raw, np.float32(448.0))
+        assert np.array_equal(scales, _torch_e4m3_code(s_raw)), trial
+
+
+def test_nvfp4_grid_roundtrip_exact(oracle):
+    # rows already on the grid: x = S * g with g an E2M1 value, a |g| = 6 in
+    # every block and S an E4M3 value (gs = 1) or E4M3 * power of two (gs)
+    r = np.random.default_rng(5)
+    grid = np.array([oracle.e2m1_value(c) for c in range(16)])
+    for gs in (1.0, 0.25, 8.0):
+        for trial in range(50):
+            g = grid[r.integers(0, 16, 256)].reshape(16, 16)
+            g[np.arange(16), r.integers(0, 16, 16)] = 6.0 * r.choice([-1, 1], 16)
+            S = np.array([oracle.e4m3_value(int(c)) for c in r.integers(1, 0x7F, 16)]) * gs
+            x = (g * S[:, None]).astype(np.float32).ravel()
+            assert np.array_equal((g * S[:, None]).ravel(), x.astype(np.float64))
+            codes, scales = oracle.nvfp4_quantize_row(x, gs)
+            assert np.array_equal(oracle.nvfp4_dequant_row(codes, scales, gs), x.astype(np.float64))
+
+
+def test_nvfp4_error_bound_and_nearest(oracle):
+    # brute force per element: the stored code is the grid point nearest
+    # fp32(x/S) under the stored scale S = fp32(e4m3 * gs), a tie taking the
+    # even code; hence |x - xhat| <= S (half the widest gap, 4..6) for
+    # unsaturated elements, plus the saturation excess past 6*S
+    r = np.random.default_rng(9)
+    grid = np.array([oracle.e2m1_value(c) for c in range(8)])
+    for trial in range(60):
+        x = (r.standard_normal(256) * np.exp(r.normal(0, 1, 256))).astype(np.float32)
+        gs = [1.0, 0.37][trial % 2]
+        codes, scales = oracle.nvfp4_quantize_row(x, gs)
+        xh = oracle.nvfp4_dequant_row(codes, scales, gs)
+        nib = np.stack([codes & 15, codes >> 4], 1).ravel()
+        for b in range(16):
+            S = np.float32(np.float32(oracle.e4m3_value(int(scales[b]))) * np.float32(gs))
+            for i in range(16):
+                j = 16 * b + i
+                rr = abs(float(np.float32(x[j] / S)))
+                d = np.abs(rr - grid)
+                c = int(nib[j]) & 7
+                assert d[c] == d.min()
+                if np.count_nonzero(d == d.min()) > 1:
+                    assert c % 2 == 0
+                assert (int(nib[j]) >> 3) == (1 if np.signbit(x[j]) else 0)
+            xb = np.abs(x[16 * b:16 * b + 16]).astype(np.float64)
+            excess = max(0.0, float(xb.max()) - 6 * float(S))
+            assert np.all(np.abs(x[16 * b:16 * b + 16] - xh[16 * b:16 * b + 16]) <= (float(S) + excess) * (1 + 1e-6))
+
+
+def test_nvfp4_nibble_order_and_block_independence(oracle):
+    x = np.zeros(256, np.float32)
+    x[0], x[1] = 6.0, -3.0          # block 0: element 0 low nibble, element 1 high nibble
+    x[16 * 5 + 2] = 1.5             # block 5 only
+    codes, scales = oracle.nvfp4_quantize_row(x)
+    assert codes[0] == (0x7 | (0xD << 4))  # +6 -> 0x7, -3 -> 0xD
+    assert oracle.e4m3_value(int(scales[0])) == 1.0
+    nz = [b for b in range(16) if scales[b] != 0]
+    assert nz == [0, 5]
+    # changing block 5 leaves every other byte untouched
+    y = x.copy()
+    y[16 * 5 + 7] = -40.0
+    codes2, scales2 = oracle.nvfp4_quantize_row(y)
+    keep = np.ones(128, bool)
+    keep[40:48] = False
+    assert np.array_equal(codes[keep], codes2[keep])
+    assert np.array_equal(np.delete(scales, 5), np.delete(scales2, 5))
+
+
+def test_nvfp4_zero_and_underflow_blocks(oracle):
+    codes, scales = oracle.nvfp4_quantize_row(np.zeros(32, np.float32))
+    assert np.all(codes == 0) and np.all(scales == 0)
+    # s_raw = 2^-10 ties to E4M3 code 0 (S = 0): the block stores zeros
+    x = np.zeros(16, np.float32)
+    x[0] = np.float32(6 * 2.0 ** -10)
+    codes, scales = oracle.nvfp4_quantize_row(x)
+    assert scales[0] == 0 and np.all(codes == 0)
+
+
+# ----------------------------------------------------------------- INT4 rows
+
+def test_int4_roundtrip_exact(oracle):
+    r = np.random.default_rng(4)
+    for trial in range(100):
+        k = r.integers(-7, 8, 256)
+        k[r.integers(0, 256)] = 7 * r.choice([-1, 1])
+        s = np.float32(2.0 ** r.integers(-8, 8) * r.choice([1.0, 0.75, 1.25]))
+        x = (k * s).astype(np.float32)
+        codes, scale = oracle.int4_quantize_row(x)
+        assert scale == s
+        assert np.array_equal(oracle.int4_dequant_row(codes, scale), x.astype(np.float64))
+
+
+def test_int4_codes_and_bound(oracle):
+    x = np.array([-7, -3, 0, 1, 7, 2, -1, 5] * 32, np.float32) * np.float32(0.5)
+    codes, scale = oracle.int4_quantize_row(x)
+    assert scale == np.float32(3.5) / np.float32(7)
+    # two's-complement nibbles, even element low
+    assert codes[0] == ((-7 & 0xF) | ((-3 & 0xF) << 4))
+    assert codes[2] == ((7 & 0xF) | (2 << 4))
+    r = np.random.default_rng(8)
+    for _ in range(100):
+        x = (r.standard_t(4, 256)).astype(np.float32)
+        codes, scale = oracle.int4_quantize_row(x)
+        nib = np.stack([codes & 15, codes >> 4], 1).ravel()
+        assert not np.any(nib == 8)  # -8 is never produced
+        xh = oracle.int4_dequant_row(codes, scale)
+        assert np.all(np.abs(x - xh) <= 0.5 * scale * (1 + 1e-6))
+    codes, scale = oracle.int4_quantize_row(np.zeros(256, np.float32))
+    assert scale == 0 and np.all(codes == 0)
+
+
+def test_int4_half_integer_ties_to_even(oracle):
+    # x/s exactly k + 1/2 rounds to the even integer
+    s = np.float32(1.0)
+    x = np.array([7.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5] * 32, np.float32)
+    codes, scale = oracle.int4_quantize_row(x)
+    assert scale == s
+    xh = oracle.int4_dequant_row(codes, scale)
+    assert list(xh[:8]) == [7.0, 0.0, 2.0, 2.0, -0.0, -2.0, -2.0, 4.0]
+
+
+# ----------------------------------------------------------------- bf16
+
+def test_bf16_rne_matches_torch(oracle):
+    r = np.random.default_rng(12)
+    bits = r.integers(0, 2 ** 32, 20000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) < 3e38)]
+    # exact ties
+    ties = (np.arange(1000, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    ties = np.concatenate([ties, -ties, (np.arange(1000, dtype=np.uint32) << 17 | 0x18000).view(np.float32)])
+    x = np.concatenate([x, ties, np.float32([0.0, -0.0, 1.0, 3.0e38])])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_rne(v) for v in x], np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# ----------------------------------------------------------------- pool + attention
+
+def _gather(pool, bt, L, b, kv):
+    P, Hkv, D = pool.page_size, pool.num_kv_heads, pool.head_dim
+    out = np.zeros((L, Hkv, D))
+    for t in range(L):
+        for g in range(Hkv):
+            out[t, g] = pool.dequant_token(int(bt[b, t // P]), g, t % P, kv)
+    return out
+
+
+def _torch_attention(q, K, V, G, sm_scale):
+    # q [Hq][D], K, V [L][Hkv][D] fp64; query head h reads KV head h // G
+    qt = torch.from_numpy(q).double()
+    Kt = torch.from_numpy(K).double().repeat_interleave(G, dim=1).transpose(0, 1)  # [Hq][L][D]
+    Vt = torch.from_numpy(V).double().repeat_interleave(G, dim=1).transpose(0, 1)
+    s = torch.einsum("hd,hld->hl", qt, Kt) * sm_scale
+    o = torch.softmax(s, dim=-1).unsqueeze(1).bmm(Vt).squeeze(1)
+    return o.numpy(), torch.logsumexp(s, dim=-1).numpy()
+
+
+@pytest.mark.parametrize("fmt,P,G,Hkv,L", [(1, 16, 4, 1, 70), (1, 3, 6, 2, 40), (1, 1, 1, 2, 9),
+                                            (2, 16, 6, 2, 45), (2, 4, 4, 1, 33)])
+def test_attention_matches_torch_fp64(oracle, fmt, P, G, Hkv, L):
+    D, B = 64 if fmt == 1 else 32, 2
+    Hq = G * Hkv
+    n_pages_seq = -(-L // P)
+    bt = inputs.page_tables(99, B, n_pages_seq, num_pages=B * n_pages_seq + 5, shuffled=True)
+    pool = oracle.Pool(fmt, B * n_pages_seq + 5, P, Hkv, D, global_scale=(0.5, 2.0) if fmt == 1 else (1, 1))
+    seq_lens = np.array([L, L - 5], np.int32)
+    for b in range(B):
+        k, v = inputs.kv_outlier_channels(7, b, int(seq_lens[b]), Hkv, D)
+        pool.quantize_store(k, v, inputs.slots_for(bt, P, b, 0, int(seq_lens[b])))
+    q = inputs.query(7, 0, B, Hq, D)
+    out, lse = pool.decode_attention(q, bt, seq_lens)
+    for b in range(B):
+        K = _gather(pool, bt, int(seq_lens[b]), b, 0)
+        V = _gather(pool, bt, int(seq_lens[b]), b, 1)
+        o_ref, lse_ref = _torch_attention(q[b].astype(np.float64), K, V, G, 1.0 / np.sqrt(D))
+        np.testing.assert_allclose(out[b], o_ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[b], lse_ref, rtol=1e-12, atol=1e-12)
+
+
+def _small_pool(oracle, fmt=1, P=16, Hkv=2, D=64, L=50, B=1, seed=1, shuffled=False):
+    n = -(-L // P)
+    bt = inputs.page_tables(seed, B, n, num_pages=B * n, shuffled=shuffled)
+    pool = oracle.Pool(fmt, B * n, P, Hkv, D)
+    for b in range(B):
+        k, v = inputs.kv_outlier_channels(seed, b, L, Hkv, D)
+        pool.quantize_store(k, v, inputs.slots_for(bt, P, b, 0, L))
+    return pool, bt
+
+
+def test_attention_closed_forms(oracle):
+    D = 64
+    pool, bt = _small_pool(oracle, L=40, D=D)
+    V = _gather(pool, bt, 40, 0, 1)
+    # L = 1: the output is v_0 exactly and lse is the single score
+    q = inputs.query(3, 0, 1, 4, D)
+    out, lse = pool.decode_attention(q, bt, np.array([1], np.int32))
+    for h in range(4):
+        assert np.array_equal(out[0, h], V[0, h // 2])
+    # q = 0: uniform weights, o = mean(V), lse = log L
+    out, lse = pool.decode_attention(np.zeros((1, 4, D), np.float32), bt, np.array([40], np.int32))
+    for h in range(4):
+        np.testing.assert_allclose(out[0, h], V[:, h // 2].mean(axis=0), rtol=0, atol=1e-13)
+        assert abs(lse[0, h] - math.log(40)) < 1e-13
+    # identical keys: every token gets the same score, o = mean(V)
+    ident = oracle.Pool(1, 3, 16, 1, D)
+    k = np.tile(inputs.kv_outlier_channels(5, 0, 1, 1, D)[0], (40, 1, 1))
+    v = inputs.kv_outlier_channels(6, 0, 40, 1, D)[1]
+    ident.quantize_store(k, v, np.arange(40, dtype=np.int32))
+    out, _ = ident.decode_attention(inputs.query(4, 0, 1, 2, D), np.arange(3, dtype=np.int32)[None], np.array([40], np.int32))
+    Vi = _gather(ident, np.arange(3, dtype=np.int32)[None], 40, 0, 1)
+    np.testing.assert_allclose(out[0, 0], Vi[:, 0].mean(axis=0), rtol=0, atol=1e-13)
+
+
+def test_attention_split_partition_invariance(oracle):
+    pool, bt = _small_pool(oracle, L=77, D=64, P=16)
+    q = inputs.query(5, 0, 1, 4, 64)
+    sl = np.array([77], np.int32)
+    base, lse0 = pool.decode_attention(q, bt, sl)
+    for split in (1, 7, 16, 32, 76, 100):
+        out, lse = pool.decode_attention(q, bt, sl, split_tokens=split)
+        np.testing.assert_allclose(out, base, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, lse0, rtol=0, atol=1e-12)
+
+
+def test_attention_page_permutation_invariance(oracle):
+    a, bta = _small_pool(oracle, L=64, shuffled=False)
+    b, btb = _small_pool(oracle, L=64, shuffled=True)
+    assert not np.array_equal(bta, btb)
+    q = inputs.query(6, 0, 1, 4, 64)
+    sl = np.array([64], np.int32)
+    oa, la = a.decode_attention(q, bta, sl)
+    ob, lb = b.decode_attention(q, btb, sl)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def test_attention_empty_sequence(oracle):
+    pool, bt = _small_pool(oracle, L=16)
+    out, lse = pool.decode_attention(inputs.query(1, 0, 1, 4, 64), bt, np.array([0], np.int32))
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_store_addressing_and_skip(oracle):
+    P, Hkv, D = 4, 2, 32
+    pool = oracle.Pool(2, 6, P, Hkv, D, fill=0xAB)
+    k, v = inputs.kv_student_t(2, 0, 5, Hkv, D)
+    slots = np.array([13, -1, 0, 22, 7], np.int32)
+    pool.quantize_store(k, v, slots)
+    touched = set()
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        page, off = divmod(int(s), P)
+        touched.add((page, off))
+        for g in range(Hkv):
+            for kv, x in ((0, k), (1, v)):
+                xh = pool.dequant_token(page, g, off, kv)
+                codes, scale = oracle.int4_quantize_row(x[i, g])
+                assert np.array_equal(xh, oracle.int4_dequant_row(codes, scale))
+    # bytes of rows that were not written keep the fill pattern
+    half = pool.slab // 2
+    for page in range(6):
+        for off in range(P):
+            if (page, off) in touched:
+                continue
+            for g in range(Hkv):
+                for base in (0, half):
+                    assert np.all(pool.data[page, g, base + off * 16: base + off * 16 + 16] == 0xAB)
+
+
+def test_dequant_prefix_exact_when_gs_is_one(oracle):
+    pool, bt = _small_pool(oracle, L=50, D=64, P=16, Hkv=2)
+    k_out, v_out = pool.dequant_prefix(bt[0], 50)
+    K = _gather(pool, bt, 50, 0, 0)
+    V = _gather(pool, bt, 50, 0, 1)
+    for got, ref in ((k_out, K), (v_out, V)):
+        ref_bits = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, ref_bits)
+        # exactness: bf16 holds e2m1 * e4m3 products without rounding
+        back = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).double().numpy()
+        assert np.array_equal(back, ref)
+
+
+def test_dequant_prefix_gs_and_int4_rounding(oracle):
+    D, P = 32, 4
+    for fmt, gs in ((1, (0.3, 3.7)), (2, (1.0, 1.0))):
+        pool = oracle.Pool(fmt, 4, P, 1, D, global_scale=gs)
+        k, v = inputs.kv_lognormal_channels(9, fmt, 13, 1, D)
+        pool.quantize_store(k, v, np.arange(13, dtype=np.int32))
+        k_out, v_out = pool.dequant_prefix(np.arange(4, dtype=np.int32), 13)
+        for kv, got in ((0, k_out), (1, v_out)):
+            for t in range(13):
+                exact = pool.dequant_token(t // P, 0, t % P, kv)
+                if fmt == 1:
+                    # fp32(e2m1 * e4m3) is exact; one fp32 multiply by gs, then bf16
+                    unscaled = (exact / gs[kv]).astype(np.float32)
+                    val = unscaled * np.float32(gs[kv])
+                else:
+                    val = exact.astype(np.float32)  # q * s rounded once to fp32
+                ref = torch.from_numpy(val.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+                assert np.array_equal(got[t, 0], ref)

@@ -1,0 +1,212 @@
+// kvq_api.cpp -- the extern "C" boundary of libkvq: argument validation, the
+// split plan and kernel dispatch.  Every host-checkable condition is tested
+// before anything touches the GPU, so a rejected call launches nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+#include "kvq_device.h"
+#include "kvq_launch.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int kTargetWaves = 2048;     // wavefronts per decode launch to fill 256 CUs
+constexpr int kMinChunksPerSplit = 4;  // 128 tokens: keeps the partials small
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+kvq_status check_cache(const kvq_cache* c) {
+  if (c == nullptr || c->pool == nullptr) return KVQ_ERR_NULL;
+  if (c->fmt != KVQ_FMT_NVFP4 && c->fmt != KVQ_FMT_INT4_TOKHEAD) return KVQ_ERR_UNSUPPORTED;
+  if (c->fmt == KVQ_FMT_NVFP4 && c->global_scale == nullptr) return KVQ_ERR_NULL;
+  if (c->num_pages <= 0 || c->num_kv_heads <= 0 || c->page_size <= 0) return KVQ_ERR_SHAPE;
+  if (c->head_dim != 128 && c->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  if (c->page_size % 16 != 0) return KVQ_ERR_UNSUPPORTED;
+  if (!aligned16(c->pool)) return KVQ_ERR_ALIGN;
+  return KVQ_OK;
+}
+
+kvq_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return KVQ_OK;
+  g_last_hip_error = (int32_t)e;
+  return KVQ_ERR_HIP;
+}
+
+int32_t auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
+  const int64_t chunks = ((int64_t)max_seq_len + 31) / 32;
+  if (chunks <= 0) return 1;
+  const int64_t units = (int64_t)batch * num_kv_heads;
+  int64_t s = (kTargetWaves + units - 1) / units;
+  const int64_t cap = (chunks + kMinChunksPerSplit - 1) / kMinChunksPerSplit;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
+kvq_status decode_shape(const kvq_cache* c, int32_t batch, int32_t num_q_heads, int32_t max_seq_len) {
+  kvq_status st = check_cache(c);
+  if (st != KVQ_OK) return st;
+  if (batch <= 0 || num_q_heads <= 0 || max_seq_len < 0) return KVQ_ERR_SHAPE;
+  if (num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_SHAPE;
+  if (num_q_heads / c->num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+size_t workspace_bytes(const kvq_cache* c, int32_t batch, int32_t num_q_heads, int32_t splits) {
+  const size_t G = (size_t)(num_q_heads / c->num_kv_heads);
+  const size_t parts = (size_t)batch * c->num_kv_heads * splits;
+  return parts * G * ((size_t)c->head_dim + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_slab_bytes(int32_t fmt, int32_t page_size, int32_t head_dim) {
+  if ((fmt != KVQ_FMT_NVFP4 && fmt != KVQ_FMT_INT4_TOKHEAD) || page_size <= 0 || head_dim <= 0 || head_dim % 16)
+    return 0;
+  return (size_t)kvq::slab_layout(fmt, page_size, head_dim).slab;
+}
+
+kvq_status kvq_quantize_store(const kvq_cache* cache, const void* k, const void* v, int32_t in_dtype,
+                              int64_t in_token_stride, const int32_t* slot_mapping, int32_t num_tokens,
+                              void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (num_tokens < 0) return KVQ_ERR_SHAPE;
+  if (in_dtype != KVQ_DT_F32 && in_dtype != KVQ_DT_BF16) return KVQ_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return KVQ_OK;
+  if (k == nullptr || v == nullptr || slot_mapping == nullptr) return KVQ_ERR_NULL;
+  if (in_token_stride < (int64_t)cache->num_kv_heads * cache->head_dim) return KVQ_ERR_SHAPE;
+  const int64_t esize = in_dtype == KVQ_DT_F32 ? 4 : 2;
+  if (!aligned16(k) || !aligned16(v) || (in_token_stride * esize) % 16 != 0) return KVQ_ERR_ALIGN;
+  const kvq::SlabLayout lay = kvq::slab_layout(cache->fmt, cache->page_size, cache->head_dim);
+  kvq::StoreParams p;
+  p.pool = (uint8_t*)cache->pool;
+  p.gs = cache->global_scale;
+  p.k = k;
+  p.v = v;
+  p.slots = slot_mapping;
+  p.in_stride = in_token_stride;
+  p.slab = lay.slab;
+  p.half = lay.half;
+  p.scales_off = lay.scales_off;
+  p.num_tokens = num_tokens;
+  p.page_size = cache->page_size;
+  p.num_kv_heads = cache->num_kv_heads;
+  return hip_status(kvq::launch_quantize_store(p, cache->fmt, cache->head_dim, in_dtype == KVQ_DT_BF16,
+                                               (hipStream_t)stream));
+}
+
+kvq_status kvq_decode_num_splits(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
+                                 int32_t* num_splits) {
+  if (num_splits == nullptr) return KVQ_ERR_NULL;
+  kvq_status st = decode_shape(cache, batch, num_q_heads, max_seq_len);
+  if (st != KVQ_OK) return st;
+  *num_splits = auto_splits(batch, cache->num_kv_heads, max_seq_len);
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_workspace_size(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
+                                     int32_t max_seq_len, int32_t num_splits, size_t* bytes) {
+  if (bytes == nullptr) return KVQ_ERR_NULL;
+  kvq_status st = decode_shape(cache, batch, num_q_heads, max_seq_len);
+  if (st != KVQ_OK) return st;
+  const int32_t s = num_splits > 0 ? num_splits : auto_splits(batch, cache->num_kv_heads, max_seq_len);
+  *bytes = workspace_bytes(cache, batch, num_q_heads, s);
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t num_q_heads,
+                                const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                                int32_t batch, int32_t max_seq_len, float sm_scale, int32_t num_splits, void* out,
+                                int32_t out_dtype, float* lse_out, void* workspace, size_t workspace_bytes_,
+                                void* stream) {
+  kvq_status st = decode_shape(cache, batch, num_q_heads, max_seq_len);
+  if (st != KVQ_OK) return st;
+  if (q == nullptr || block_table == nullptr || seq_lens == nullptr || out == nullptr || workspace == nullptr)
+    return KVQ_ERR_NULL;
+  if (out_dtype != KVQ_DT_F32 && out_dtype != KVQ_DT_BF16) return KVQ_ERR_UNSUPPORTED;
+  if (max_pages <= 0 || (int64_t)max_pages * cache->page_size < max_seq_len) return KVQ_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) || (lse_out && ((uintptr_t)lse_out & 3u)))
+    return KVQ_ERR_ALIGN;
+  const int32_t splits = num_splits > 0 ? num_splits : auto_splits(batch, cache->num_kv_heads, max_seq_len);
+  if (splits > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (workspace_bytes_ < workspace_bytes(cache, batch, num_q_heads, splits)) return KVQ_ERR_WORKSPACE;
+  if (batch > 65535) return KVQ_ERR_UNSUPPORTED;
+
+  const kvq::SlabLayout lay = kvq::slab_layout(cache->fmt, cache->page_size, cache->head_dim);
+  const int64_t chunks = ((int64_t)max_seq_len + 31) / 32;
+  kvq::DecodeParams p;
+  p.pool = (const uint8_t*)cache->pool;
+  p.gs = cache->global_scale;
+  p.q = (const uint16_t*)q;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  const int32_t G = num_q_heads / cache->num_kv_heads;
+  const size_t parts = (size_t)batch * cache->num_kv_heads * splits;
+  p.part_o = (float*)workspace;
+  p.part_ml = (float*)workspace + parts * G * cache->head_dim;
+  p.out = out;
+  p.lse = lse_out;
+  p.slab = lay.slab;
+  p.half = lay.half;
+  p.scales_off = lay.scales_off;
+  p.sm_scale = sm_scale > 0.0f ? sm_scale : 1.0f / __builtin_sqrtf((float)cache->head_dim);
+  p.max_pages = max_pages;
+  p.batch = batch;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.num_q_heads = num_q_heads;
+  p.group = G;
+  p.page_size = cache->page_size;
+  p.num_splits = splits;
+  p.chunks_per_split = (int32_t)((chunks + splits - 1) / splits);
+  if (p.chunks_per_split < 1) p.chunks_per_split = 1;
+  p.out_bf16 = out_dtype == KVQ_DT_BF16;
+  return hip_status(kvq::launch_decode(p, cache->fmt, cache->head_dim, (hipStream_t)stream));
+}
+
+kvq_status kvq_dequant_prefix(const kvq_cache* cache, const int32_t* block_table_row, int32_t prefix_len,
+                              void* k_out, void* v_out, int64_t out_token_stride, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (prefix_len < 0) return KVQ_ERR_SHAPE;
+  if (prefix_len == 0) return KVQ_OK;
+  if (block_table_row == nullptr || k_out == nullptr || v_out == nullptr) return KVQ_ERR_NULL;
+  if (out_token_stride < (int64_t)cache->num_kv_heads * cache->head_dim) return KVQ_ERR_SHAPE;
+  if (!aligned16(k_out) || !aligned16(v_out) || (out_token_stride * 2) % 16 != 0) return KVQ_ERR_ALIGN;
+  const kvq::SlabLayout lay = kvq::slab_layout(cache->fmt, cache->page_size, cache->head_dim);
+  kvq::DequantParams p;
+  p.pool = (const uint8_t*)cache->pool;
+  p.gs = cache->global_scale;
+  p.pages = block_table_row;
+  p.k_out = (uint16_t*)k_out;
+  p.v_out = (uint16_t*)v_out;
+  p.out_stride = out_token_stride;
+  p.slab = lay.slab;
+  p.half = lay.half;
+  p.scales_off = lay.scales_off;
+  p.prefix_len = prefix_len;
+  p.page_size = cache->page_size;
+  p.num_kv_heads = cache->num_kv_heads;
+  return hip_status(kvq::launch_dequant_prefix(p, cache->fmt, cache->head_dim, (hipStream_t)stream));
+}
+
+const char* kvq_status_string(int32_t status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "a required pointer is NULL";
+    case KVQ_ERR_SHAPE: return "inconsistent sizes or strides";
+    case KVQ_ERR_UNSUPPORTED: return "format or shape outside the supported limits";
+    case KVQ_ERR_ALIGN: return "a pointer or stride is not 16-byte aligned";
+    case KVQ_ERR_WORKSPACE: return "workspace smaller than kvq_decode_workspace_size";
+    case KVQ_ERR_HIP: return "HIP launch failed (see kvq_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int32_t kvq_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

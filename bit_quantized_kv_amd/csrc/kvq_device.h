@@ -1,0 +1,129 @@
+// kvq_device.h -- device-side types and codecs shared by the gfx950 kernels.
+//
+// Formats (see include/kvq.h): NVFP4 = E2M1 elements, one OCP E4M3 scale per
+// 16 head-dim elements of a token row, FP32 per-layer global scale; INT4 =
+// symmetric -7..7 two's-complement nibbles with one FP32 scale per token and
+// head.  Even element in the low nibble.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+enum { FMT_NVFP4 = 1, FMT_INT4 = 2 };
+
+// Byte layout of one slab (one page of one KV head).
+struct SlabLayout {
+  int64_t code_row;    // bytes per row of codes (head_dim / 2)
+  int64_t scale_row;   // bytes per row of scales (head_dim / 16, or 4)
+  int64_t half;        // bytes of the K half (codes + scales)
+  int64_t scales_off;  // offset of the scales within a half
+  int64_t slab;        // bytes of the whole slab
+};
+
+__host__ __device__ inline SlabLayout slab_layout(int fmt, int page_size, int head_dim) {
+  SlabLayout s;
+  s.code_row = head_dim / 2;
+  s.scale_row = fmt == FMT_NVFP4 ? head_dim / 16 : 4;
+  s.scales_off = (int64_t)page_size * s.code_row;
+  s.half = (int64_t)page_size * (s.code_row + s.scale_row);
+  s.slab = 2 * s.half;
+  return s;
+}
+
+// ---------------------------------------------------------------- bit casts
+__device__ inline uint32_t as_u32(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ inline float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+__device__ inline uint32_t h2_as_u32(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ inline half2_t u32_as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
+
+// (x & mask) | (y & ~mask): one v_bfi_b32.
+__device__ inline uint32_t bitfield_insert(uint32_t mask, uint32_t x, uint32_t y) {
+  return (x & mask) | (y & ~mask);
+}
+
+// Byte permute of {hi, lo} (v_perm_b32): selector byte i picks byte sel_i of
+// the 8-byte value (lo = bytes 0..3, hi = bytes 4..7); 0x0C yields 0x00.
+__device__ inline uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// ---------------------------------------------------------------- encoders
+
+// fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
+__device__ inline uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = as_u32(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Non-negative fp32 -> E4M3 (OCP) code: round to nearest, ties to even,
+// saturating at 448 (0x7E).  Integer rounding of the fp32 significand for the
+// normal range; the subnormal range (below 2^-6) is a multiple of 2^-9 and is
+// rounded with rint(s * 2^9), which is exact scaling followed by RNE.
+__device__ inline uint32_t e4m3_encode(float s) {
+  if (s != s) return 0x7Fu;
+  if (!(s < 448.0f)) return 0x7Eu;
+  uint32_t u = as_u32(s);
+  int e = (int)(u >> 23) - 127;
+  if (e >= -6) {
+    uint32_t mant = u & 0x7FFFFFu;
+    uint32_t q = mant >> 20;
+    uint32_t rem = mant & 0xFFFFFu;
+    uint32_t code = ((uint32_t)(e + 7) << 3) | q;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) code += 1;
+    return code;
+  }
+  return (uint32_t)__builtin_rintf(s * 512.0f);
+}
+
+// E4M3 code -> fp32 (exact).  Hardware OCP E4M3 conversion (v_cvt_pk_f32_fp8).
+__device__ inline float e4m3_decode(uint32_t code) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(code, false)[0];
+}
+
+// fp32 ratio r = x / S -> E2M1 code: nearest grid value {0,.5,1,1.5,2,3,4,6},
+// a midpoint going to the code with an even mantissa bit, |r| >= 6 -> 6, the
+// sign bit of r kept.
+__device__ inline uint32_t e2m1_encode(float r) {
+  float a = __builtin_fabsf(r);
+  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+               (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return c | ((as_u32(r) >> 28) & 8u);
+}
+
+// E2M1 magnitude (3-bit code) -> fp32.
+__device__ inline float e2m1_magnitude(uint32_t c3) {
+  // values 0, 0.5, 1, 1.5, 2, 3, 4, 6: exponent field e = c3 >> 1, mantissa m = c3 & 1
+  uint32_t e = c3 >> 1, m = c3 & 1u;
+  float v = e == 0 ? 0.5f * (float)m : (1.0f + 0.5f * (float)m) * (float)(1u << (e - 1));
+  return v;
+}
+
+// ---------------------------------------------------------------- decoders for the attention kernels
+
+// Two E2M1 nibbles (byte `sel` of w: low nibble -> element 0, high -> element
+// 1) as exact fp16 (v_cvt_scalef32_pk_f16_fp4 with a unit scale; that
+// instruction applies only the exponent of its scale operand).
+template <int SEL>
+__device__ inline half2_t e2m1x2_to_h2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+// Two-nibble INT4 pairs: given w' = w ^ 0x88888888 (offset-8 nibbles), the
+// nibbles at positions p and p + 4 become fp16 (q_p, q_{p+4}) exactly: the
+// nibble u is placed in the low mantissa bits of 1024 (0x6400), then 1032 is
+// subtracted.
+template <int P>
+__device__ inline half2_t int4x2_to_h2(uint32_t wbiased) {
+  uint32_t t = ((wbiased >> (4 * P)) & 0x000F000Fu) | 0x64006400u;
+  return u32_as_h2(t) - (half2_t){(_Float16)1032.0f, (_Float16)1032.0f};
+}
+
+}  // namespace kvq

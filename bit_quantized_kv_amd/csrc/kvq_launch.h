@@ -1,0 +1,52 @@
+// kvq_launch.h -- kernel parameter blocks and launchers (internal to libkvq).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct StoreParams {
+  uint8_t* pool;
+  const float* gs;  // {gs_K, gs_V} (NVFP4)
+  const void* k;
+  const void* v;
+  const int32_t* slots;
+  int64_t in_stride;  // elements between tokens
+  int64_t slab, half, scales_off;
+  int32_t num_tokens, page_size, num_kv_heads;
+};
+
+struct DequantParams {
+  const uint8_t* pool;
+  const float* gs;
+  const int32_t* pages;
+  uint16_t* k_out;
+  uint16_t* v_out;
+  int64_t out_stride;
+  int64_t slab, half, scales_off;
+  int32_t prefix_len, page_size, num_kv_heads;
+};
+
+struct DecodeParams {
+  const uint8_t* pool;
+  const float* gs;
+  const uint16_t* q;  // bf16 [B][Hq][D]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* part_o;   // [B][Hkv][S][G][D]
+  float* part_ml;  // [B][Hkv][S][G][2]
+  void* out;
+  float* lse;
+  int64_t slab, half, scales_off;
+  float sm_scale;
+  int32_t max_pages, batch, num_kv_heads, num_q_heads, group, page_size;
+  int32_t num_splits, chunks_per_split;
+  int32_t out_bf16;
+};
+
+hipError_t launch_quantize_store(const StoreParams& p, int fmt, int head_dim, int in_bf16, hipStream_t stream);
+hipError_t launch_dequant_prefix(const DequantParams& p, int fmt, int head_dim, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream_t stream);
+
+}  // namespace kvq

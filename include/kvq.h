@@ -1,0 +1,177 @@
+/*
+ * kvq.h -- C ABI of libkvq, a 4-bit paged KV cache for MI355X (gfx950).
+ *
+ * Three operations make up the hot path, as the pages describe it:
+ *   kvq_quantize_store    quantize new K/V rows into cache pages on write
+ *   kvq_decode_attention  decode attention that reads the 4-bit pages
+ *                         directly and dequantizes inside the kernel
+ *   kvq_dequant_prefix    expand a cached prefix into a bf16 workspace
+ * ("SGLang's 4-bit KV cache: the 56% is exact, the 1.78x is untested",
+ * Figure 2 caption: one shared pool, prefill quantizes and stores into it,
+ * decode reads NVFP4 directly, chunked prefill/extend dequantizes the cached
+ * prefix into a reused workspace.)
+ *
+ * Formats
+ *   KVQ_FMT_NVFP4: E2M1 elements packed two per byte, one E4M3 (OCP, max 448)
+ *     scale per 16 consecutive head-dim elements of a token row, and one FP32
+ *     global scale per layer for K and one for V -- 9 bytes per 16 values,
+ *     0.5625 of FP8 (same page, section "The 56% survives its own scale, and
+ *     names the block size").
+ *   KVQ_FMT_INT4_TOKHEAD: symmetric int4 (range -7..7, two's-complement
+ *     nibbles) with one FP32 scale per token and KV head, for K and for V --
+ *     264 bytes per head and token at head dim 256 ("KV cache in 4 bits: 8.8
+ *     instead of 4.7 full sessions on the same four RTX 5090s", section "What
+ *     we changed").
+ *   Quantization rules (both formats): block/row amax; NVFP4 scale
+ *   E4M3(fp32(amax / fp32(6 * gs))), elements rounded to nearest-even under the
+ *   stored scale fp32(E4M3 * gs), |x| >= 6 saturating; INT4 scale
+ *   fp32(amax / 7), q = clamp(rint(fp32(x / s)), -7, 7).  Even element in the
+ *   low nibble.  All decisions in IEEE fp32, so packed bytes are bit-exact.
+ *
+ * Pool layout (one layer): uint8 [num_pages][num_kv_heads][slab], where a
+ * slab is one page of one KV head:
+ *   [K codes: page_size rows of head_dim/2 bytes][K scales]
+ *   [V codes: page_size rows of head_dim/2 bytes][V scales]
+ * Scales are page_size rows of head_dim/16 E4M3 bytes (NVFP4) or page_size
+ * fp32 values (INT4).  Cache token t of a sequence lives in page
+ * block_table[t / page_size] at row t % page_size; a write slot is
+ * page * page_size + row.
+ *
+ * Conventions
+ *   - The caller owns all memory.  The library allocates and frees nothing and
+ *     keeps no state between calls.
+ *   - All work is enqueued on the caller's HIP stream (`stream`, a
+ *     hipStream_t; NULL = the default stream) and is asynchronous.
+ *   - Every host-checkable condition is validated before any launch; a
+ *     failing call returns a negative kvq_status and launches nothing.  A
+ *     failed launch returns KVQ_ERR_HIP; kvq_last_hip_error() then gives the
+ *     hipError_t of the calling thread.  Nothing throws and nothing prints.
+ *   - Contents of device arrays (slots, page ids, sequence lengths) are not
+ *     validated: out-of-range values are undefined behaviour, as an
+ *     out-of-bounds index would be.  Two tokens written to one slot in one call
+ *     leave an unspecified winner.
+ *   - Limits: head_dim in {128, 256}; page_size a positive multiple of 16;
+ *     num_q_heads a multiple of num_kv_heads with group size <= 16; device
+ *     pointers 16-byte aligned; token strides keep rows 16-byte aligned.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = -1,        /* a required pointer is NULL */
+  KVQ_ERR_SHAPE = -2,       /* inconsistent sizes or strides */
+  KVQ_ERR_UNSUPPORTED = -3, /* outside the supported formats / limits */
+  KVQ_ERR_ALIGN = -4,       /* a pointer or stride breaks 16-byte alignment */
+  KVQ_ERR_WORKSPACE = -5,   /* workspace smaller than kvq_decode_workspace_size */
+  KVQ_ERR_HIP = -6          /* a HIP launch failed; see kvq_last_hip_error() */
+} kvq_status;
+
+typedef enum { KVQ_FMT_NVFP4 = 1, KVQ_FMT_INT4_TOKHEAD = 2 } kvq_format;
+
+typedef enum { KVQ_DT_F32 = 0, KVQ_DT_BF16 = 1 } kvq_dtype;
+
+/* One layer's cache.  A host struct, read only during a call. */
+typedef struct {
+  int32_t fmt;                /* kvq_format */
+  int32_t num_pages;          /* pages in the pool */
+  int32_t page_size;          /* tokens per page (multiple of 16) */
+  int32_t num_kv_heads;
+  int32_t head_dim;           /* 128 or 256 */
+  void* pool;                 /* device, uint8 [num_pages][num_kv_heads][slab] */
+  const float* global_scale;  /* device float[2] = {gs_K, gs_V}, positive and
+                                 finite; NVFP4 only (ignored for INT4) */
+} kvq_cache;
+
+/* Bytes of one slab (one page of one KV head, K and V with their scales);
+ * 0 for an unknown format or a head_dim not divisible by 16.
+ * NVFP4: 2 * page_size * (head_dim/2 + head_dim/16); INT4: 2 * page_size *
+ * (head_dim/2 + 4), i.e. 422,400 bytes for a 1,600-token page at head dim
+ * 256, the page size "KV cache in 4 bits ..." ("What we changed") prints. */
+size_t kvq_slab_bytes(int32_t fmt, int32_t page_size, int32_t head_dim);
+
+/* Quantize-on-write ("SGLang's 4-bit KV cache ...", Figure 2 caption: prefill
+ * quantizes and stores into the cache; decode writes the new token's K/V).
+ *   k, v            device, [num_tokens][token stride] rows; head g of token i
+ *                   starts at element i * in_token_stride + g * head_dim
+ *   in_dtype        KVQ_DT_F32 or KVQ_DT_BF16 (bf16 is widened exactly)
+ *   in_token_stride elements between tokens, >= num_kv_heads * head_dim
+ *   slot_mapping    device int32 [num_tokens]; slot < 0 skips the token
+ * Writes each (token, head) K row and V row -- codes and scales -- into its
+ * slot.  NVFP4 reads cache->global_scale.  num_tokens == 0 is a no-op. */
+kvq_status kvq_quantize_store(const kvq_cache* cache, const void* k, const void* v, int32_t in_dtype,
+                              int64_t in_token_stride, const int32_t* slot_mapping, int32_t num_tokens,
+                              void* stream);
+
+/* The split count kvq_decode_attention uses when num_splits <= 0: each
+ * (sequence, KV head) is cut into that many token ranges of whole 32-token
+ * chunks, sized from (batch, num_kv_heads, max_seq_len) to fill the GPU. */
+kvq_status kvq_decode_num_splits(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
+                                 int32_t max_seq_len, int32_t* num_splits);
+
+/* Workspace bytes kvq_decode_attention needs for this shape and split count
+ * (num_splits <= 0: the automatic count).  Per (sequence, KV head, split) it
+ * holds the unnormalised partial output and (max, sum) of each query head. */
+kvq_status kvq_decode_workspace_size(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
+                                     int32_t max_seq_len, int32_t num_splits, size_t* bytes);
+
+/* Paged decode attention over the 4-bit cache ("SGLang's 4-bit KV cache ...",
+ * Figure 2 caption: decode reads NVFP4 directly and dequantizes inside the
+ * kernel).  For each sequence b and query head h (KV head h / G, G =
+ * num_q_heads / num_kv_heads):
+ *     o = softmax(sm_scale * q K^T) V,   lse = log sum exp(sm_scale * q K^T)
+ * over the seq_lens[b] cached tokens, all read back from the 4-bit pages (no
+ * causal mask: one decode query sees every cached token).  The token range is
+ * split into num_splits parts (<= 0: automatic); each part yields a partial
+ * (o, max, sum) and a second kernel merges them by the log-sum-exp rule in a
+ * fixed order, so results are bitwise reproducible for a fixed split count.
+ *   q            device bf16 [batch][num_q_heads][head_dim]
+ *   block_table  device int32 [batch][max_pages]; only the first
+ *                ceil(seq_lens[b] / page_size) entries of a row are read
+ *   seq_lens     device int32 [batch], each in [0, max_seq_len]; 0 gives o = 0
+ *                and lse = -inf
+ *   max_seq_len  host upper bound of seq_lens, fixes the split plan
+ *   sm_scale     softmax scale; <= 0 means 1/sqrt(head_dim)
+ *   out          device [batch][num_q_heads][head_dim], bf16 (round to nearest
+ *                even) or fp32 per out_dtype
+ *   lse_out      device fp32 [batch][num_q_heads] (natural log), or NULL
+ *   workspace    device scratch of at least kvq_decode_workspace_size bytes,
+ *                16-byte aligned; its contents need no initialisation */
+kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t num_q_heads,
+                                const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                                int32_t batch, int32_t max_seq_len, float sm_scale, int32_t num_splits, void* out,
+                                int32_t out_dtype, float* lse_out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Prefix dequantization for chunked prefill / extend ("SGLang's 4-bit KV cache
+ * ...", Figure 2 caption: the cached prefix is dequantized into a reused
+ * workspace -- bf16 here).  Cache tokens [0, prefix_len) of the sequence whose
+ * page list is block_table_row become rows of k_out and v_out:
+ *     NVFP4: bf16_rne(fp32(fp32(e2m1 * e4m3) * gs))   (exact when gs == 1)
+ *     INT4:  bf16_rne(fp32(q * s))
+ *   block_table_row  device int32 [ceil(prefix_len / page_size)]
+ *   k_out, v_out     device bf16; head g of token t at element
+ *                    t * out_token_stride + g * head_dim
+ *   out_token_stride elements, >= num_kv_heads * head_dim
+ * prefix_len == 0 is a no-op. */
+kvq_status kvq_dequant_prefix(const kvq_cache* cache, const int32_t* block_table_row, int32_t prefix_len,
+                              void* k_out, void* v_out, int64_t out_token_stride, void* stream);
+
+/* Static description of a status code. */
+const char* kvq_status_string(int32_t status);
+
+/* hipError_t of the last failed launch on the calling thread (0 if none). */
+int32_t kvq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,158 @@
+"""Shared helpers of the GPU parity tests: build the same cache on the GPU
+(through the C ABI) and in the CPU oracle from the same seeded inputs, and
+compare the two."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from bit_quantized_kv_amd import inputs, kvq
+
+# Attention tolerance.  The oracle attends in fp64 over the exactly
+# dequantized cache; the kernel computes scores in fp32 from exact fp16 K,
+# rounds probabilities to fp16 for the PV product and accumulates in fp32.
+# fp32 output: |gpu - oracle| <= 2e-3 everywhere.  bf16 output adds the
+# unavoidable output rounding: |gpu - oracle| <= 2e-3 + half a bf16 ulp of
+# the oracle value.
+ATOL = 2e-3
+LSE_ATOL = 1e-3
+MIN_COS = 0.9995
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
+
+
+def kv_rows(kind: str, seed: int, layer: int, n: int, H: int, D: int):
+    if kind == "outliers":
+        return inputs.kv_outlier_channels(seed, layer, n, H, D)
+    if kind == "lognormal":
+        return inputs.kv_lognormal_channels(seed, layer, n, H, D)
+    if kind == "student_t":
+        return inputs.kv_student_t(seed, layer, n, H, D)
+    raise ValueError(kind)
+
+
+class Case:
+    """One layer cache with B sequences of lengths `lens`, stored on both sides."""
+
+    def __init__(self, fmt, D, Hkv, G, P, lens, kind="outliers", in_dtype=torch.float32, gs=(1.0, 1.0),
+                 shuffled=True, seed=1, poison=0xFF, extra_pages=3, drop_every=0):
+        self.fmt, self.D, self.Hkv, self.G, self.P = fmt, D, Hkv, G, P
+        self.lens = np.array(lens, np.int32)
+        self.B = len(lens)
+        self.Hq = Hkv * G
+        self.max_len = int(self.lens.max()) if self.B else 0
+        self.pages_per_seq = max(1, -(-self.max_len // P))
+        self.num_pages = self.B * self.pages_per_seq + extra_pages
+        self.bt = inputs.page_tables(seed, self.B, self.pages_per_seq, self.num_pages, shuffled=shuffled)
+        ks, vs, slots = [], [], []
+        for b in range(self.B):
+            L = int(self.lens[b])
+            k, v = kv_rows(kind, seed, b, L, Hkv, D)
+            ks.append(k)
+            vs.append(v)
+            slots.append(inputs.slots_for(self.bt, P, b, 0, L))
+        self.k = np.concatenate(ks) if ks else np.zeros((0, Hkv, D), np.float32)
+        self.v = np.concatenate(vs) if vs else np.zeros((0, Hkv, D), np.float32)
+        self.slots = np.concatenate(slots).astype(np.int32)
+        if drop_every:
+            self.slots[::drop_every] = -1  # skipped tokens keep the poison bytes
+        self.in_dtype = in_dtype
+        self.gs = gs
+        # GPU side
+        dev = torch.device("cuda")
+        self.cache = kvq.Cache(fmt, self.num_pages, P, Hkv, D, device=dev, global_scale=gs)
+        self.cache.pool.fill_(poison)
+        self.k_dev = torch.from_numpy(self.k).to(dev).to(in_dtype)
+        self.v_dev = torch.from_numpy(self.v).to(dev).to(in_dtype)
+        self.slots_dev = torch.from_numpy(self.slots).to(dev)
+        kvq.kvq_quantize_store(self.cache, self.k_dev, self.v_dev, self.slots_dev)
+        # oracle side (bf16 inputs are handed over as their exact fp32 values)
+        self.ref = oracle.Pool(fmt, self.num_pages, P, Hkv, D, global_scale=gs, fill=poison)
+        k_in = self.k_dev.float().cpu().numpy()
+        v_in = self.v_dev.float().cpu().numpy()
+        self.ref.quantize_store(k_in, v_in, self.slots)
+        self.q = inputs.query(seed, 99, self.B, self.Hq, D)
+        self.q_dev = torch.from_numpy(self.q).to(dev).to(torch.bfloat16)
+        self.bt_dev = torch.from_numpy(self.bt).to(dev)
+        self.lens_dev = torch.from_numpy(self.lens).to(dev)
+
+    def gpu_pool(self) -> np.ndarray:
+        torch.cuda.synchronize()
+        return self.cache.pool.cpu().numpy()
+
+    def decode(self, out_dtype=torch.float32, num_splits=0, bt=None, want_lse=True):
+        lse = torch.empty((self.B, self.Hq), dtype=torch.float32, device="cuda") if want_lse else None
+        out = kvq.kvq_decode_attention(self.cache, self.q_dev, self.bt_dev if bt is None else bt, self.lens_dev,
+                                       self.max_len, lse=lse, num_splits=num_splits, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy(), (lse.cpu().numpy() if want_lse else None)
+
+    def oracle_decode(self):
+        return self.ref.decode_attention(self.q, self.bt, self.lens)
+
+
+def check_pool_bitexact(case: Case):
+    got = case.gpu_pool()
+    ref = case.ref.data
+    if not np.array_equal(got, ref):
+        diff = np.argwhere(got != ref)
+        raise AssertionError(f"{len(diff)} pool bytes differ; first at {diff[:5].tolist()}: "
+                             f"gpu {got[tuple(diff[0])]:#x} oracle {ref[tuple(diff[0])]:#x}")
+
+
+def cosine(a: np.ndarray, b: np.ndarray) -> float:
+    na, nb = np.linalg.norm(a), np.linalg.norm(b)
+    if na == 0 and nb == 0:
+        return 1.0
+    return float(np.dot(a.ravel(), b.ravel()) / (na * nb))
+
+
+def check_attention(out, ref, lens, bf16=False, lse=None, ref_lse=None, label=""):
+    """Element-wise tolerance, per-(sequence, head) cosine, lse."""
+    assert np.all(np.isfinite(out)), f"{label}: non-finite output"
+    err = np.abs(out.astype(np.float64) - ref)
+    tol = ATOL + (bf16_half_ulp(ref) if bf16 else 0.0)
+    bad = err > tol
+    assert not bad.any(), (f"{label}: {bad.sum()} elements out of tolerance, max err {err.max():.3g} "
+                           f"at {np.unravel_index(err.argmax(), err.shape)}")
+    for b in range(out.shape[0]):
+        if lens[b] == 0:
+            assert np.all(out[b] == 0), f"{label}: empty sequence must give zeros"
+            continue
+        for h in range(out.shape[1]):
+            c = cosine(out[b, h], ref[b, h])
+            assert c >= MIN_COS, f"{label}: cosine {c} at ({b},{h})"
+    if lse is not None:
+        for b in range(out.shape[0]):
+            if lens[b] == 0:
+                assert np.all(np.isneginf(lse[b])), f"{label}: lse of an empty sequence must be -inf"
+            else:
+                d = np.abs(lse[b] - ref_lse[b]).max()
+                assert d <= LSE_ATOL, f"{label}: lse differs by {d}"
+    return float(err.max())
+
+
+def check_dequant_prefix(case: Case, stride_extra: int = 0):
+    for b in range(case.B):
+        L = int(case.lens[b])
+        stride = case.Hkv * case.D + stride_extra
+        k_out = torch.full((max(L, 1), stride), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        v_out = torch.full((max(L, 1), stride), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        kvq.kvq_dequant_prefix(case.cache, case.bt_dev[b], L, k_out, v_out)
+        torch.cuda.synchronize()
+        if L == 0:
+            continue
+        rk, rv = case.ref.dequant_prefix(case.bt[b], L, out_token_stride=stride)
+        for got, ref in ((k_out, rk), (v_out, rv)):
+            g = got.view(torch.int16).cpu().numpy().view(np.uint16)[:L]
+            used = np.zeros(stride, bool)
+            used[: case.Hkv * case.D] = True
+            assert np.array_equal(g[:, used], ref[:, used]), f"prefix dequant differs for sequence {b}"
+            assert np.all(g[:, ~used] == 0x7FC0), "prefix dequant wrote outside its rows"

@@ -1,0 +1,145 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the
+header declares, sizes its buffers as the formats dictate, and rejects bad
+arguments before any launch (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_quantized_kv_amd import kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kvq.LIB_PATH):
+        from bit_quantized_kv_amd import build
+        build.build()
+    return kvq.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"kvq_quantize_store", "kvq_decode_attention", "kvq_dequant_prefix"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_slab_bytes_match_oracle_and_pages(lib, oracle):
+    for fmt in (1, 2):
+        for P in (16, 48, 800, 1600):
+            for D in (128, 256):
+                assert kvq.kvq_slab_bytes(fmt, P, D) == oracle.slab_bytes(fmt, P, D)
+    assert kvq.kvq_slab_bytes(2, 1600, 256) == 422400
+    assert kvq.kvq_slab_bytes(2, 800, 256) == 211200
+    assert kvq.kvq_slab_bytes(1, 16, 256) == 16 * 2 * (128 + 16)
+    assert kvq.kvq_slab_bytes(3, 16, 256) == 0
+
+
+FAKE = 0x10000  # a 16-byte-aligned host address that is never dereferenced
+
+
+def cache(fmt=1, pages=64, P=16, H=4, D=256, pool=FAKE, gs=FAKE):
+    return kvq.kvq_cache(fmt, pages, P, H, D, pool, gs)
+
+
+def q_store(lib, c, k=FAKE, v=FAKE, dt=1, stride=1024, slots=FAKE, n=4):
+    return lib.kvq_quantize_store(ctypes.byref(c), k, v, dt, stride, slots, n, None)
+
+
+def test_quantize_store_validation(lib):
+    assert lib.kvq_quantize_store(None, FAKE, FAKE, 1, 1024, FAKE, 4, None) == ERR_NULL
+    assert q_store(lib, cache(pool=0)) == ERR_NULL
+    assert q_store(lib, cache(gs=0)) == ERR_NULL            # NVFP4 needs global scales
+    assert q_store(lib, cache(fmt=3)) == ERR_UNSUPPORTED
+    assert q_store(lib, cache(D=64)) == ERR_UNSUPPORTED
+    assert q_store(lib, cache(P=24)) == ERR_UNSUPPORTED
+    assert q_store(lib, cache(pages=0)) == ERR_SHAPE
+    assert q_store(lib, cache(pool=FAKE + 8)) == ERR_ALIGN
+    assert q_store(lib, cache(), dt=7) == ERR_UNSUPPORTED
+    assert q_store(lib, cache(), n=-1) == ERR_SHAPE
+    assert q_store(lib, cache(), k=0) == ERR_NULL
+    assert q_store(lib, cache(), slots=0) == ERR_NULL
+    assert q_store(lib, cache(), stride=1000) == ERR_SHAPE     # < Hkv * D
+    assert q_store(lib, cache(), stride=1028) == ERR_ALIGN     # 2056 bytes
+    assert q_store(lib, cache(), k=FAKE + 2) == ERR_ALIGN
+    # INT4 ignores the global scale; zero tokens is a no-op before any launch
+    assert q_store(lib, cache(fmt=2, gs=0), n=0) == OK
+    assert q_store(lib, cache(), n=0) == OK
+
+
+def decode(lib, c, q=FAKE, hq=24, bt=FAKE, maxp=2048, sl=FAKE, B=32, L=32768, ns=0, out=FAKE, odt=1, lse=None,
+           ws=FAKE, wsb=1 << 40):
+    return lib.kvq_decode_attention(ctypes.byref(c), q, hq, bt, maxp, sl, B, L, 0.0, ns, out, odt, lse, ws, wsb, None)
+
+
+def test_decode_validation(lib):
+    c = cache()
+    assert decode(lib, c, q=0) == ERR_NULL
+    assert decode(lib, c, ws=0) == ERR_NULL
+    assert decode(lib, c, hq=26) == ERR_SHAPE                  # not a multiple of Hkv
+    assert decode(lib, c, hq=4 * 17) == ERR_UNSUPPORTED        # group of 17
+    assert decode(lib, c, maxp=100) == ERR_SHAPE               # table too short for max_seq_len
+    assert decode(lib, c, odt=5) == ERR_UNSUPPORTED
+    assert decode(lib, c, out=FAKE + 4) == ERR_ALIGN
+    assert decode(lib, c, lse=FAKE + 2) == ERR_ALIGN
+    assert decode(lib, c, B=0) == ERR_SHAPE
+    assert decode(lib, c, L=-1) == ERR_SHAPE
+    assert decode(lib, c, wsb=16) == ERR_WORKSPACE
+    assert decode(lib, cache(D=96)) == ERR_UNSUPPORTED
+
+
+def test_workspace_and_split_plan(lib):
+    c = cache()
+    splits = ctypes.c_int32(0)
+    size = ctypes.c_size_t(0)
+    assert lib.kvq_decode_num_splits(ctypes.byref(c), 32, 24, 32768, ctypes.byref(splits)) == OK
+    S = splits.value
+    assert S >= 1 and 32 * 4 * S >= 1024                      # enough wavefronts for 256 CUs
+    assert lib.kvq_decode_workspace_size(ctypes.byref(c), 32, 24, 32768, 0, ctypes.byref(size)) == OK
+    assert size.value == 32 * 4 * S * 6 * (256 + 2) * 4
+    assert lib.kvq_decode_workspace_size(ctypes.byref(c), 2, 8, 100, 3, ctypes.byref(size)) == OK
+    assert size.value == 2 * 4 * 3 * 2 * (256 + 2) * 4
+    # short contexts never get more splits than 4-chunk (128-token) pieces
+    assert lib.kvq_decode_num_splits(ctypes.byref(c), 1, 4, 200, ctypes.byref(splits)) == OK
+    assert splits.value == 2
+    assert lib.kvq_decode_num_splits(ctypes.byref(c), 1, 4, 0, ctypes.byref(splits)) == OK
+    assert splits.value == 1
+    assert lib.kvq_decode_num_splits(ctypes.byref(c), 1, 4, 10, None) == ERR_NULL
+
+
+def test_dequant_prefix_validation(lib):
+    c = cache()
+    f = lib.kvq_dequant_prefix
+    assert f(ctypes.byref(c), FAKE, 0, FAKE, FAKE, 1024, None) == OK
+    assert f(ctypes.byref(c), FAKE, -1, FAKE, FAKE, 1024, None) == ERR_SHAPE
+    assert f(ctypes.byref(c), 0, 16, FAKE, FAKE, 1024, None) == ERR_NULL
+    assert f(ctypes.byref(c), FAKE, 16, FAKE, 0, 1024, None) == ERR_NULL
+    assert f(ctypes.byref(c), FAKE, 16, FAKE, FAKE, 512, None) == ERR_SHAPE
+    assert f(ctypes.byref(c), FAKE, 16, FAKE, FAKE, 1028, None) == ERR_ALIGN
+    assert f(ctypes.byref(c), FAKE, 16, FAKE + 8, FAKE, 1024, None) == ERR_ALIGN
+
+
+def test_status_strings(lib):
+    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP):
+        assert kvq.status_string(s) and kvq.status_string(s) != "unknown status"
+    assert kvq.status_string(42) == "unknown status"
+    assert lib.kvq_last_hip_error() == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kvq, "_lib", None)
+    monkeypatch.setattr(kvq, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        kvq.lib()

@@ -1,0 +1,365 @@
+"""Benchmark of the 4-bit paged KV cache decode path on one MI355X.
+
+One step = one decode step of a Qwen3.8-27B-shaped attention stack ("SGLang's
+4-bit KV cache: the 56% is exact, the 1.78x is untested", per-token table: 16
+full-attention layers x 4 KV heads x head dim 256; 24 query heads as a stated
+workload choice): for each of the 16 layers, quantize-store the new token's
+K/V of every sequence into its NVFP4 cache (kvq_quantize_store), then run paged
+decode attention over the whole cached context (kvq_decode_attention: split
+decode kernel + log-sum-exp merge).  Each layer has its own 1.2 GB pool, so no
+pool stays in the 256 MB Infinity Cache between uses.
+
+Printed: one JSON line.  value = effective KV GB/s of the step (packed codes +
+scales of every cached token attended, summed over the 16 layers, divided by
+the step time); tokens/s = batch / step time (attention only: no weights).
+`roofline` prices the decode-attention call (decode + merge kernels) against
+the 8 TB/s HBM peak with its algorithmic bytes; `cpu_baseline` times the CPU
+oracle on a sample of the same cache.  Secondary workloads (160K shuffled
+pages with chunked-prefill store, 1M split-context with prefix dequant, INT4
+at 220K) are reported under "secondary".
+
+Inputs are synthetic and seeded: K, V = exp(N(0,1)) per-(head, channel)
+scale x N(0,1) in bf16 (t4 / sqrt(2) for INT4), q ~ N(0,1) bf16, generated on
+the GPU with torch's generator.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn effective KV GB/s & % HBM roofline; tokens/s at 32K/160K/1M ctx"
+
+# fmt, batch, context, page size, shuffled pages, query heads, KV heads, head dim
+WORKLOADS = {
+    "ctx32k": dict(fmt=1, batch=32, ctx=32768, page=16, shuffled=False, kind="lognormal",
+                   desc="Qwen3.8-27B-shaped NVFP4 decode step: 16 layers x 4 KV heads x D256, 24 q heads, "
+                        "batch 32, context 32,768, 16-token pages"),
+    "ctx160k": dict(fmt=1, batch=4, ctx=160000, page=16, shuffled=True, kind="lognormal", chunk=64,
+                    desc="NVFP4, batch 4, context 160,000, shuffled page tables, plus a 64-token "
+                         "chunked-prefill quantize-store per sequence"),
+    "ctx1m": dict(fmt=1, batch=1, ctx=1048576, page=16, shuffled=False, kind="lognormal", prefix=True,
+                  desc="NVFP4, batch 1, context 1,048,576, split-context decode; plus kvq_dequant_prefix of "
+                       "the full prefix into a bf16 workspace of 1,048,576 + 4,096 rows"),
+    "int4_220k": dict(fmt=2, batch=8, ctx=220000, page=1600, shuffled=False, kind="student_t",
+                      desc="INT4 per-token-head, batch 8, context 220,000, 1,600-token pages (last page half "
+                           "full); 16 layers assumed"),
+}
+LAYERS, HKV, HQ, D = 16, 4, 24, 256
+
+
+def token_head_bytes(fmt: int) -> int:
+    # packed codes + scales of one token in one KV head, K and V
+    return 2 * (D // 2 + (D // 16 if fmt == 1 else 4))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ctx32k", choices=sorted(WORKLOADS))
+    ap.add_argument("--secondary", default="ctx160k,ctx1m,int4_220k",
+                    help="comma-separated extra workloads to report ('' for none)")
+    ap.add_argument("--secondary-steps", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                    help="also run a plain device copy of this many GiB (profiler counter calibration)")
+    return ap.parse_args()
+
+
+class Layer:
+    """One layer: its cache, the decode-step inputs and outputs."""
+
+    def __init__(self, torch, kvq, w, layer, bt, workload_id):
+        dev = "cuda"
+        B, L, P = w["batch"], w["ctx"], w["page"]
+        self.pages_per_seq = -(-L // P)
+        num_pages = B * self.pages_per_seq
+        self.cache = kvq.Cache(w["fmt"], num_pages, P, HKV, D, device=dev)
+        self.bt = bt
+        self.lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+        g = torch.Generator(device=dev)
+        from bit_quantized_kv_amd import inputs
+        g.manual_seed(inputs.seed_int(workload_id, layer, inputs.STREAM_Q))
+        self.q = torch.randn((B, HQ, D), generator=g, device=dev).to(torch.bfloat16)
+        g.manual_seed(inputs.seed_int(workload_id, layer, inputs.STREAM_K + 32))
+        self.k_new = torch.randn((B, HKV, D), generator=g, device=dev).to(torch.bfloat16)
+        self.v_new = torch.randn((B, HKV, D), generator=g, device=dev).to(torch.bfloat16)
+        # the new token is the last cached one: position L - 1 of each sequence
+        last = L - 1
+        self.slots_new = (bt[:, last // P] * P + last % P).to(torch.int32).contiguous()
+        self.out = torch.empty((B, HQ, D), dtype=torch.bfloat16, device=dev)
+
+
+def student_t4(torch, g, shape):
+    z = torch.randn(shape, generator=g, device="cuda")
+    chi2 = torch.zeros(shape, device="cuda")
+    for _ in range(4):
+        chi2 += torch.randn(shape, generator=g, device="cuda") ** 2
+    return z / torch.sqrt(chi2 / 4.0) / math.sqrt(2.0)
+
+
+def populate(torch, kvq, inputs, w, layer_obj, layer, workload_id, chunk_tokens=1 << 16):
+    """Fill every cached token of every sequence: K/V generated on the GPU in
+    chunks and bulk quantize-stored.  Returns (seconds, bytes read, bytes
+    written) of the quantize-store launches."""
+    dev = "cuda"
+    B, L, P = w["batch"], w["ctx"], w["page"]
+    g = torch.Generator(device=dev)
+    if w["kind"] == "lognormal":
+        g.manual_seed(inputs.seed_int(workload_id, layer, inputs.STREAM_KSCALE))
+        kscale = torch.exp(torch.randn((HKV, D), generator=g, device=dev))
+        g.manual_seed(inputs.seed_int(workload_id, layer, inputs.STREAM_VSCALE))
+        vscale = torch.exp(torch.randn((HKV, D), generator=g, device=dev))
+    g.manual_seed(inputs.seed_int(workload_id, layer, inputs.STREAM_K))
+    tok = torch.arange(L, device=dev, dtype=torch.int64)
+    total_s, nbytes_in = 0.0, 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for b in range(B):
+        for t0 in range(0, L, chunk_tokens):
+            t1 = min(L, t0 + chunk_tokens)
+            n = t1 - t0
+            if w["kind"] == "lognormal":
+                k = (torch.randn((n, HKV, D), generator=g, device=dev) * kscale).to(torch.bfloat16)
+                v = (torch.randn((n, HKV, D), generator=g, device=dev) * vscale).to(torch.bfloat16)
+            else:  # Student-t, nu = 4 (z / sqrt(chi2_4 / 4)), scaled to unit variance
+                k = student_t4(torch, g, (n, HKV, D)).to(torch.bfloat16)
+                v = student_t4(torch, g, (n, HKV, D)).to(torch.bfloat16)
+            t = tok[t0:t1]
+            slots = (layer_obj.bt[b, t // P].to(torch.int64) * P + t % P).to(torch.int32)
+            e0.record()
+            kvq.kvq_quantize_store(layer_obj.cache, k, v, slots)
+            e1.record()
+            e1.synchronize()
+            total_s += e0.elapsed_time(e1) / 1e3
+            nbytes_in += 2 * k.numel() * 2
+    nbytes_out = B * L * HKV * token_head_bytes(w["fmt"])
+    return total_s, nbytes_in, nbytes_out
+
+
+def block_tables(torch, inputs, w, workload_id):
+    B, L, P = w["batch"], w["ctx"], w["page"]
+    pps = -(-L // P)
+    bt = inputs.page_tables(workload_id, B, pps, B * pps, shuffled=w["shuffled"])
+    return torch.from_numpy(bt).to("cuda")
+
+
+def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu=False):
+    w = WORKLOADS[name]
+    wid = sorted(WORKLOADS).index(name) + 2
+    B, L, P, fmt = w["batch"], w["ctx"], w["page"], w["fmt"]
+    bt = block_tables(torch, inputs, w, wid)
+    layers, pop_s, pop_in, pop_out = [], 0.0, 0, 0
+    for l in range(n_layers):
+        lay = Layer(torch, kvq, w, l, bt, wid)
+        s, bi, bo = populate(torch, kvq, inputs, w, lay, l, wid)
+        pop_s, pop_in, pop_out = pop_s + s, pop_in + bi, pop_out + bo
+        layers.append(lay)
+    splits = kvq.kvq_decode_num_splits(layers[0].cache, B, HQ, L)
+    ws = torch.empty(kvq.kvq_decode_workspace_size(layers[0].cache, B, HQ, L), dtype=torch.uint8, device="cuda")
+    # chunked-prefill store (160K): 64 new tokens per sequence at positions L..L+63
+    chunk = None
+    if w.get("chunk"):
+        n = w["chunk"]
+        g = torch.Generator(device="cuda")
+        g.manual_seed(inputs.seed_int(wid, 0, 40))
+        kc = torch.randn((B * n, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+        vc = torch.randn((B * n, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+        # write into the sequences' own last pages (rows 0..63 of spare capacity are not
+        # needed: the chunk overwrites the final 64 cached positions of each sequence)
+        t = torch.arange(L - n, L, device="cuda")
+        slots = torch.cat([(bt[b, t // P].to(torch.int64) * P + t % P) for b in range(B)]).to(torch.int32)
+        chunk = (kc, vc, slots)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(timed_pairs=None):
+        for lay in layers:
+            a, b_, c = (ev(), ev(), ev()) if timed_pairs is not None else (None, None, None)
+            if a is not None:
+                a.record(stream)
+            kvq.kvq_quantize_store(lay.cache, lay.k_new, lay.v_new, lay.slots_new)
+            if a is not None:
+                b_.record(stream)
+            kvq.kvq_decode_attention(lay.cache, lay.q, lay.bt, lay.lens, L, out=lay.out, workspace=ws)
+            if a is not None:
+                c.record(stream)
+                timed_pairs.append((a, b_, c))
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-step timing
+    t_start, t_end = ev(), ev()
+    t_start.record(stream)
+    for _ in range(steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t_start.elapsed_time(t_end) / steps
+    # per-call timing (events between launches on the same stream)
+    pairs = []
+    for _ in range(steps):
+        step(pairs)
+    torch.cuda.synchronize()
+    store_ms = sum(a.elapsed_time(b) for a, b, _ in pairs) / len(pairs)
+    decode_ms = sum(b.elapsed_time(c) for _, b, c in pairs) / len(pairs)
+    kv_bytes_layer = B * L * HKV * token_head_bytes(fmt)
+    res = {
+        "workload": name, "desc": w["desc"], "format": "nvfp4" if fmt == 1 else "int4_per_token_head",
+        "batch": B, "context": L, "page_size": P, "layers": n_layers, "num_splits": splits,
+        "step_ms": step_ms, "decode_call_us": decode_ms * 1e3, "store_call_us": store_ms * 1e3,
+        "kv_bytes_per_layer": kv_bytes_layer,
+        "effective_kv_gbs": n_layers * kv_bytes_layer / (step_ms * 1e-3) / 1e9,
+        "decode_call_gbs": kv_bytes_layer / (decode_ms * 1e-3) / 1e9,
+        "tokens_per_s": B / (step_ms * 1e-3),
+        "tokens_per_s_16_layers": B / (step_ms * 1e-3 * LAYERS / n_layers),
+        "populate": {"seconds": pop_s, "read_bytes": pop_in, "write_bytes": pop_out,
+                     "gbs": (pop_in + pop_out) / pop_s / 1e9 if pop_s > 0 else None},
+    }
+    res["decode_call_frac_hbm"] = res["decode_call_gbs"] / HBM_PEAK_GBS
+    if chunk is not None:
+        kc, vc, slots = chunk
+        for _ in range(3):
+            kvq.kvq_quantize_store(layers[0].cache, kc, vc, slots)
+        a, b_ = ev(), ev()
+        a.record(stream)
+        for _ in range(steps):
+            kvq.kvq_quantize_store(layers[0].cache, kc, vc, slots)
+        b_.record(stream)
+        torch.cuda.synchronize()
+        res["chunk_store_us"] = a.elapsed_time(b_) / steps * 1e3
+        res["chunk_store_tokens"] = int(slots.numel())
+    if w.get("prefix"):
+        rows = L + 4096
+        k_ws = torch.empty((rows, HKV * D), dtype=torch.bfloat16, device="cuda")
+        v_ws = torch.empty((rows, HKV * D), dtype=torch.bfloat16, device="cuda")
+        times = []
+        for i in range(steps + 2):
+            lay = layers[i % n_layers]
+            a, b_ = ev(), ev()
+            a.record(stream)
+            kvq.kvq_dequant_prefix(lay.cache, lay.bt[0], L, k_ws, v_ws)
+            b_.record(stream)
+            times.append((a, b_))
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in times[2:]) / steps * 1e3
+        rd = L * HKV * token_head_bytes(fmt)
+        wr = 2 * L * HKV * D * 2
+        res["dequant_prefix"] = {"us": us, "read_bytes": rd, "write_bytes": wr,
+                                 "gbs": (rd + wr) / (us * 1e-6) / 1e9,
+                                 "frac_hbm": (rd + wr) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        del k_ws, v_ws
+    keep = layers[0] if keep_for_cpu else None
+    del layers, ws, chunk
+    torch.cuda.empty_cache()
+    return res, keep
+
+
+def cpu_baseline(torch, lay, w, target_s):
+    """The CPU oracle on a sample of the same cache: whole sequences of layer 0
+    (their packed pages copied to the host), all 24 query heads."""
+    import numpy as np
+    import oracle
+    P, L = w["page"], w["ctx"]
+    pps = -(-L // P)
+
+    def run(nseq):
+        pages = lay.bt[:nseq].reshape(-1).long()
+        pool = oracle.Pool(w["fmt"], nseq * pps, P, HKV, D)
+        pool.data[:] = lay.cache.pool[pages].cpu().numpy()
+        bt = np.arange(nseq * pps, dtype=np.int32).reshape(nseq, pps)
+        q = lay.q[:nseq].float().cpu().numpy()
+        t = time.perf_counter()
+        pool.decode_attention(q, bt, np.full(nseq, L, np.int32))
+        return time.perf_counter() - t
+
+    t1 = run(1)
+    n = int(max(1, min(w["batch"], round(target_s / max(t1, 1e-3)))))
+    t = run(n) if n > 1 else t1
+    nbytes = n * L * HKV * token_head_bytes(w["fmt"])
+    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"1 layer, {n} of {w['batch']} sequences x {L} tokens, all {HQ} query heads, fp64 attention "
+                      f"over the same packed pages ({t:.1f} s)",
+            "seconds": t, "tokens_per_s_16_layers_extrapolated": n / (t * LAYERS)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the split-context path is "
+              f"single-GPU by design", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from bit_quantized_kv_amd import inputs, kvq
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    kvq.lib()  # fail loudly if the HIP library is missing
+    t0 = time.time()
+    main_res, keep = run_workload(torch, kvq, inputs, args.workload, args.steps, args.warmup, args.layers,
+                                  keep_for_cpu=not args.no_cpu_baseline)
+    print(f"[bench] {args.workload}: step {main_res['step_ms']:.3f} ms, decode call {main_res['decode_call_us']:.1f} us "
+          f"({main_res['decode_call_gbs']:.0f} GB/s), {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    secondary = {}
+    for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
+        t1 = time.time()
+        r, _ = run_workload(torch, kvq, inputs, name, args.secondary_steps, 2, args.layers)
+        secondary[name] = r
+        print(f"[bench] {name}: step {r['step_ms']:.3f} ms, decode call {r['decode_call_us']:.1f} us "
+              f"({r['decode_call_gbs']:.0f} GB/s), {time.time() - t1:.1f} s", file=sys.stderr, flush=True)
+    if args.copy_calibration_gib > 0:
+        n = int(args.copy_calibration_gib * (1 << 30))
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    cpu = None
+    if keep is not None:
+        cpu = cpu_baseline(torch, keep, WORKLOADS[args.workload], args.cpu_seconds)
+        print(f"[bench] cpu oracle: {cpu['value']:.4f} GB/s on {cpu['cores']} threads", file=sys.stderr, flush=True)
+    w = WORKLOADS[args.workload]
+    r = main_res
+    line = {
+        "metric": METRIC,
+        "value": r["effective_kv_gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 mfma / f32 accumulate over u8-packed e2m1+e4m3" if w["fmt"] == 1 else
+                 "f16 mfma / f32 accumulate over u8-packed int4+f32",
+        "data": "synthetic",
+        "config": {"workload": r["desc"], "batch": r["batch"], "context": r["context"], "layers": r["layers"],
+                   "kv_heads": HKV, "q_heads": HQ, "head_dim": D, "page_size": r["page_size"],
+                   "num_splits": r["num_splits"]},
+        "tokens_per_s": r["tokens_per_s"],
+        "pct_hbm_roofline_step": 100.0 * r["effective_kv_gbs"] / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": r["decode_call_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["decode_call_frac_hbm"], "traffic": None,
+                     "kernel": "kvq_decode_attention call (decode_kernel + merge_kernel)",
+                     "algorithmic_bytes_per_launch": r["kv_bytes_per_layer"],
+                     "avg_launch_us": r["decode_call_us"]},
+        "cpu_baseline": cpu,
+        "store_call_us": r["store_call_us"],
+        "populate": r["populate"],
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -48,12 +48,12 @@ template <int D, int FMT>
 struct ChunkRegs {
   static constexpr int VEC = D / 128;  // 16-byte K vectors per lane and token
   static constexpr int VW = D / 128;   // V dwords per lane and token (D/32 bytes)
-  uint4 kw[2][VEC];
-  uint32_t ks[2][VEC];  // NVFP4: two E4M3 block-scale bytes
-  float4 ksc[2];        // INT4: K scales of tokens 4j..4j+3
+  u32x4_t kw[2][VEC];
+  uint32_t ks[2][VEC];  // NVFP4: dword holding the lane's two E4M3 block scales
+  float4_t ksc[2];      // INT4: K scales of tokens 4j..4j+3
   uint32_t vw[2][4][VW];
-  uint32_t vs[2][4];  // NVFP4: V block-scale byte of token 4j+i
-  float4 vsc[2];      // INT4: V scales of tokens 4j..4j+3
+  uint32_t vs[2];     // NVFP4: one dword of the half's V scales (see load)
+  float4_t vsc[2];    // INT4: V scales of tokens 4j..4j+3
 };
 
 template <int D, int FMT>
@@ -68,59 +68,72 @@ struct Decoder {
   const int lane, j, r, b, g, L;
   const uint8_t* head_base;  // pool + g * slab
   const int32_t* pages;      // block_table row of sequence b
+  int vo_k, vo_ks, vo_vs, vo_sc, vo_v;  // per-lane byte offsets inside a slab
 
   __device__ Decoder(const DecodeParams& p_, int lane_, int b_, int g_, int L_)
       : p(p_), lane(lane_), j(lane_ >> 4), r(lane_ & 15), b(b_), g(g_), L(L_) {
     head_base = p.pool + (int64_t)g * p.slab;
     pages = p.block_table + (int64_t)b * p.max_pages;
+    vo_k = r * (D / 2) + 16 * j;                           // K code row r
+    vo_ks = r * (D / 16) + 4 * (j >> 1);                   // K scale row r
+    vo_vs = (4 * j + (r & 3)) * (D / 16) + 4 * (((r >> 2) * D) / 256);
+    vo_sc = 4 * j * 4;                                     // INT4 scales of rows 4j..4j+3
+    vo_v = 4 * j * (D / 2) + r * (D / 32);                 // V code rows 4j + i
   }
 
-  // Slab address of the half-chunk starting at token tok0 (a multiple of 16);
-  // a half past the end of the sequence reuses the first half's address.
-  __device__ inline const uint8_t* half_base(int tok0, int& off) const {
-    const int64_t page = pages[tok0 / p.page_size];
-    off = tok0 % p.page_size;
-    return head_base + page * p.num_kv_heads * p.slab;
-  }
-
-  __device__ inline void load(Regs& R, int c) const {
+  // Page-table entries of the two 16-token halves of chunk c, fetched with a
+  // vector load (kept out of the scalar counter) well before they are used.
+  // A half past the end of the sequence repeats the first half's entry.
+  __device__ inline int2 fetch_pages(int c) const {
     const int T = c * 32;
-    int off[2];
-    const uint8_t* base[2];
-    base[0] = half_base(T, off[0]);
-    if (T + 16 < L) {
-      base[1] = half_base(T + 16, off[1]);
-    } else {
-      base[1] = base[0];
-      off[1] = off[0];
-    }
+    int i0 = T / p.page_size;
+    int i1 = (T + 16 < L) ? (T + 16) / p.page_size : i0;
+    asm volatile("" : "+v"(i0), "+v"(i1));
+    return make_int2(ld_global<int32_t>(pages + i0), ld_global<int32_t>(pages + i1));
+  }
+
+  // Buffer descriptor of one slab: base address in SGPRs, range-checked to
+  // the slab, so every load below is one loop-invariant VGPR offset plus
+  // uniform (SGPR / immediate) offsets.
+  __device__ inline __amdgpu_buffer_rsrc_t slab_rsrc(int page) const {
+    const uint8_t* base = head_base + (int64_t)page * p.num_kv_heads * p.slab;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)p.slab, 0x00020000);
+  }
+
+  __device__ inline void load(Regs& R, int c, int2 pg) const {
+    const int T = c * 32;
+    const int off0 = T % p.page_size;
+    const int off1 = (T + 16 < L) ? (T + 16) % p.page_size : off0;
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-      const uint8_t* kb = base[h];
-      const uint8_t* vb = base[h] + p.half;
-      const int krow = off[h] + r;
+      const __amdgpu_buffer_rsrc_t rs = slab_rsrc(__builtin_amdgcn_readfirstlane(h == 0 ? pg.x : pg.y));
+      const int off = h == 0 ? off0 : off1;
+      // K codes: row off + r, bytes 64v + 16j
 #pragma unroll
-      for (int v = 0; v < VEC; v++) R.kw[h][v] = *(const uint4*)(kb + (int64_t)krow * (D / 2) + 64 * v + 16 * j);
+      for (int v = 0; v < VEC; v++)
+        R.kw[h][v] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo_k + 64 * v, off * (D / 2), 0);
       if (FMT == FMT_NVFP4) {
 #pragma unroll
         for (int v = 0; v < VEC; v++)
-          R.ks[h][v] = *(const uint16_t*)(kb + p.scales_off + (int64_t)krow * (D / 16) + 8 * v + 2 * j);
+          R.ks[h][v] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_ks + 8 * v, (int)p.scales_off + off * (D / 16), 0);
+        // Lane (j, r) with quad Q = r / 4 loads the dword of V-scale row 4j + r%4
+        // that holds block (r * D / 256), the block every lane of quad Q needs;
+        // compute() broadcasts row i of the quad with a DPP quad_perm.
+        R.vs[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_vs, (int)(p.half + p.scales_off) + off * (D / 16), 0);
       } else {
-        R.ksc[h] = *(const float4*)(kb + p.scales_off + (int64_t)(off[h] + 4 * j) * 4);
-        R.vsc[h] = *(const float4*)(vb + p.scales_off + (int64_t)(off[h] + 4 * j) * 4);
+        R.ksc[h] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo_sc, (int)p.scales_off + off * 4, 0));
+        R.vsc[h] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo_sc, (int)(p.half + p.scales_off) + off * 4, 0));
       }
+      // V codes: rows off + 4j + i, the lane's D/32-byte segment r
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const int vrow = off[h] + 4 * j + i;
-        const uint8_t* vp = vb + (int64_t)vrow * (D / 2) + r * (D / 32);
         if (VW == 2) {
-          uint2 w = *(const uint2*)vp;
+          const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo_v + i * (D / 2), (int)p.half + off * (D / 2), 0);
           R.vw[h][i][0] = w.x;
           R.vw[h][i][VW - 1] = w.y;
         } else {
-          R.vw[h][i][0] = *(const uint32_t*)vp;
+          R.vw[h][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_v + i * (D / 2), (int)p.half + off * (D / 2), 0);
         }
-        if (FMT == FMT_NVFP4) R.vs[h][i] = vb[p.scales_off + (int64_t)vrow * (D / 16) + (r * (D / 16)) / 16];
       }
     }
   }
@@ -156,7 +169,7 @@ struct Decoder {
 // low-order fp16 part of the probabilities, so P = hi + lo costs no extra
 // MFMA; otherwise the low part takes a second MFMA per tile.
 template <int D, int FMT, bool DUP>
-__global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(const DecodeParams p) {
   using Dec = Decoder<D, FMT>;
   using Regs = typename Dec::Regs;
   constexpr int VEC = Dec::VEC, VW = Dec::VW, KCH = Dec::KCH, VT = Dec::VT;
@@ -225,6 +238,10 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   }
   const float sm = p.sm_scale * kLog2e * ldexpf(1.0f, -kq) * (FMT == FMT_NVFP4 ? p.gs[0] : 1.0f);
 
+  // byte of block (n * D / 256) within its scale dword, from two dwords -> bytes 0, 1
+  const uint32_t vb_byte = ((n * D) / 256) & 3;
+  const uint32_t vsel = vb_byte | ((4 + vb_byte) << 8) | 0x0C0C0000u;
+
   float4_t oacc[VT];
 #pragma unroll
   for (int t = 0; t < VT; t++) oacc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
@@ -242,7 +259,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
       for (int v = 0; v < VEC; v++) {
         half2_t s_lo = {}, s_hi = {};
         if (FMT == FMT_NVFP4) {
-          const float2_t s01 = __builtin_amdgcn_cvt_pk_f32_fp8(R.ks[h][v], false);
+          const float2_t s01 = __builtin_amdgcn_cvt_pk_f32_fp8(R.ks[h][v] >> (16 * (j & 1)), false);
           s_lo = (half2_t){(_Float16)s01[0], (_Float16)s01[0]};
           s_hi = (half2_t){(_Float16)s01[1], (_Float16)s01[1]};
         }
@@ -330,7 +347,10 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
         }
         if (FMT == FMT_NVFP4) {
           const bool va = T + 16 * h + 4 * j + 2 * pp < L, vb = T + 16 * h + 4 * j + 2 * pp + 1 < L;
-          const float2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(R.vs[h][2 * pp] | (R.vs[h][2 * pp + 1] << 8), false);
+          // dwords of scale rows 4j + 2pp and 4j + 2pp + 1 (quad lanes 2pp, 2pp+1)
+          const uint32_t d0 = pp == 0 ? quad_bcast<0>(R.vs[h]) : quad_bcast<2>(R.vs[h]);
+          const uint32_t d1 = pp == 0 ? quad_bcast<1>(R.vs[h]) : quad_bcast<3>(R.vs[h]);
+          const float2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(byte_perm(d1, d0, vsel), false);
           vsc2[h][pp] = (half2_t){(_Float16)(va ? f[0] : 0.0f), (_Float16)(vb ? f[1] : 0.0f)};
         }
       }
@@ -373,14 +393,23 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     }
   };
 
-  // ---- main loop, software-pipelined by one chunk
+  // ---- main loop, software-pipelined: chunk data one chunk ahead, page-table
+  // entries two chunks ahead.  Loads are unconditional (past the end they
+  // repeat the last chunk, an L2 hit) so the wait counts stay exact.
+  // Each page-table fetch is issued before the chunk loads that precede its
+  // use, so waiting for it never waits for chunk data (the counter is in order).
+  const int clast = c1 - 1;
   Regs RA, RB;
-  dec.load(RA, c0);
+  const int2 pg0 = dec.fetch_pages(c0);
+  int2 pg1 = dec.fetch_pages(min(c0 + 1, clast));
+  dec.load(RA, c0, pg0);
   for (int c = c0; c < c1; c += 2) {
-    if (c + 1 < c1) dec.load(RB, c + 1);
+    const int2 pg2 = dec.fetch_pages(min(c + 2, clast));
+    dec.load(RB, min(c + 1, clast), pg1);
     compute(RA, c);
     if (c + 1 >= c1) break;
-    if (c + 2 < c1) dec.load(RA, c + 2);
+    pg1 = dec.fetch_pages(min(c + 3, clast));
+    dec.load(RA, min(c + 2, clast), pg2);
     compute(RB, c + 1);
   }
 
@@ -416,37 +445,69 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 
 // Merge the splits of one (sequence, query head): M = max m_s,
 // o = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s, lse = (M + log2 sum) ln 2.
-// Splits are visited in order, so the result is reproducible.
+// One workgroup per (sequence, query head, 64-channel block): its 256 threads
+// scan the (m, l) pairs together, then 4 groups of 64 threads accumulate
+// interleaved splits for their channel and are summed in LDS.  Every sum runs
+// in a fixed order, so the result is reproducible.
 template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(const DecodeParams p) {
-  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+__global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
+  constexpr int CW = 64, SG = 4, NCB = D / CW;
+  const int cb = blockIdx.x % NCB, h = blockIdx.x / NCB, b = blockIdx.y;
+  const int tid = threadIdx.x, sg = tid / CW, c = cb * CW + tid % CW;
   const int G = p.group, g = h / G, n = h % G, S = p.num_splits;
   const int64_t part0 = ((int64_t)b * p.num_kv_heads + g) * S;
-  float M = -__builtin_inff();
-  for (int s = 0; s < S; s++) M = fmaxf(M, p.part_ml[((part0 + s) * G + n) * 2]);
-  float o = 0.0f, den = 0.0f;
-  if (M != -__builtin_inff()) {
-    for (int s = 0; s < S; s++) {
-      const float ms = p.part_ml[((part0 + s) * G + n) * 2];
-      if (ms == -__builtin_inff()) continue;
-      const float w = exp2f(ms - M);
-      den += w * p.part_ml[((part0 + s) * G + n) * 2 + 1];
-      o += w * p.part_o[((part0 + s) * G + n) * D + c];
-    }
-    o = o / den;
+  __shared__ float red[256];
+  __shared__ float acc_s[SG][CW];
+
+  float m = -__builtin_inff();
+  for (int s = tid; s < S; s += 256) m = fmaxf(m, p.part_ml[((part0 + s) * G + n) * 2]);
+  red[tid] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
   }
+  const float M = red[0];
+  __syncthreads();
+
+  float den = 0.0f;
+  for (int s = tid; s < S; s += 256) {
+    const float ms = p.part_ml[((part0 + s) * G + n) * 2];
+    if (ms != -__builtin_inff()) den += exp2f(ms - M) * p.part_ml[((part0 + s) * G + n) * 2 + 1];
+  }
+  red[tid] = den;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  den = red[0];
+
+  float o = 0.0f;
+  if (M != -__builtin_inff()) {
+#pragma unroll 4
+    for (int s = sg; s < S; s += SG) {
+      const float ms = p.part_ml[((part0 + s) * G + n) * 2];
+      if (ms != -__builtin_inff()) o += exp2f(ms - M) * p.part_o[((part0 + s) * G + n) * D + c];
+    }
+  }
+  acc_s[sg][tid % CW] = o;
+  __syncthreads();
+  if (sg != 0) return;
+  o = acc_s[0][tid] + acc_s[1][tid] + acc_s[2][tid] + acc_s[3][tid];
+  o = den > 0.0f ? o / den : 0.0f;
   const int64_t oi = ((int64_t)b * p.num_q_heads + h) * D + c;
   if (p.out_bf16)
     ((uint16_t*)p.out)[oi] = f32_to_bf16_rne(o);
   else
     ((float*)p.out)[oi] = o;
-  if (p.lse != nullptr && c == 0)
+  if (p.lse != nullptr && cb == 0 && tid == 0)
     p.lse[(int64_t)b * p.num_q_heads + h] = den > 0.0f ? (M + log2f(den)) * kLn2 : -__builtin_inff();
 }
 
 hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream_t stream) {
   const dim3 grid(p.num_splits, p.num_kv_heads, p.batch), block(64);
-  const dim3 mgrid(p.num_q_heads, p.batch);
+  const dim3 mgrid(p.num_q_heads * (head_dim / 64), p.batch);
   const bool dup = p.group <= 8;
 #define KVQ_DECODE(D, F)                                                                        \
   do {                                                                                          \
@@ -460,7 +521,7 @@ hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream
   } else {
     if (fmt == FMT_NVFP4) KVQ_DECODE(128, FMT_NVFP4);
     else KVQ_DECODE(128, FMT_INT4);
-    hipLaunchKernelGGL((merge_kernel<128>), mgrid, dim3(128), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<128>), mgrid, dim3(256), 0, stream, p);
   }
 #undef KVQ_DECODE
   return hipGetLastError();

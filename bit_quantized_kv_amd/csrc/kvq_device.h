@@ -15,6 +15,8 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 enum { FMT_NVFP4 = 1, FMT_INT4 = 2 };
 
@@ -37,6 +39,16 @@ __host__ __device__ inline SlabLayout slab_layout(int fmt, int page_size, int he
   return s;
 }
 
+// ---------------------------------------------------------------- global loads
+// Loads through an explicitly global (address space 1) pointer, so the
+// compiler emits global_load rather than flat_load (flat loads also count
+// against the scalar/LDS counter and would serialize the prefetch).
+// T is a scalar or a clang ext_vector type.
+template <typename T>
+__device__ inline T ld_global(const void* ptr) {
+  return *(const __attribute__((address_space(1))) T*)ptr;
+}
+
 // ---------------------------------------------------------------- bit casts
 __device__ inline uint32_t as_u32(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ inline float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
@@ -52,6 +64,12 @@ __device__ inline uint32_t bitfield_insert(uint32_t mask, uint32_t x, uint32_t y
 // the 8-byte value (lo = bytes 0..3, hi = bytes 4..7); 0x0C yields 0x00.
 __device__ inline uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Value of lane I of each quad (DPP quad_perm broadcast, no LDS traffic).
+template <int I>
+__device__ inline uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, I * 0x55, 0xF, 0xF, false);
 }
 
 // ---------------------------------------------------------------- encoders

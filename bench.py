@@ -67,6 +67,7 @@ def parse():
                     help="comma-separated extra workloads to report ('' for none)")
     ap.add_argument("--secondary-steps", type=int, default=5)
     ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--num-splits", type=int, default=0, help="decode split count (0 = the library's plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the CPU-oracle sample")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
@@ -151,7 +152,7 @@ def block_tables(torch, inputs, w, workload_id):
     return torch.from_numpy(bt).to("cuda")
 
 
-def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu=False):
+def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu=False, num_splits=0):
     w = WORKLOADS[name]
     wid = sorted(WORKLOADS).index(name) + 2
     B, L, P, fmt = w["batch"], w["ctx"], w["page"], w["fmt"]
@@ -162,8 +163,9 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
         s, bi, bo = populate(torch, kvq, inputs, w, lay, l, wid)
         pop_s, pop_in, pop_out = pop_s + s, pop_in + bi, pop_out + bo
         layers.append(lay)
-    splits = kvq.kvq_decode_num_splits(layers[0].cache, B, HQ, L)
-    ws = torch.empty(kvq.kvq_decode_workspace_size(layers[0].cache, B, HQ, L), dtype=torch.uint8, device="cuda")
+    splits = num_splits or kvq.kvq_decode_num_splits(layers[0].cache, B, HQ, L)
+    ws = torch.empty(kvq.kvq_decode_workspace_size(layers[0].cache, B, HQ, L, splits), dtype=torch.uint8,
+                     device="cuda")
     # chunked-prefill store (160K): 64 new tokens per sequence at positions L..L+63
     chunk = None
     if w.get("chunk"):
@@ -188,7 +190,8 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
             kvq.kvq_quantize_store(lay.cache, lay.k_new, lay.v_new, lay.slots_new)
             if a is not None:
                 b_.record(stream)
-            kvq.kvq_decode_attention(lay.cache, lay.q, lay.bt, lay.lens, L, out=lay.out, workspace=ws)
+            kvq.kvq_decode_attention(lay.cache, lay.q, lay.bt, lay.lens, L, out=lay.out, workspace=ws,
+                                     num_splits=splits)
             if a is not None:
                 c.record(stream)
                 timed_pairs.append((a, b_, c))
@@ -305,7 +308,7 @@ def main():
     kvq.lib()  # fail loudly if the HIP library is missing
     t0 = time.time()
     main_res, keep = run_workload(torch, kvq, inputs, args.workload, args.steps, args.warmup, args.layers,
-                                  keep_for_cpu=not args.no_cpu_baseline)
+                                  keep_for_cpu=not args.no_cpu_baseline, num_splits=args.num_splits)
     print(f"[bench] {args.workload}: step {main_res['step_ms']:.3f} ms, decode call {main_res['decode_call_us']:.1f} us "
           f"({main_res['decode_call_gbs']:.0f} GB/s), {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     secondary = {}

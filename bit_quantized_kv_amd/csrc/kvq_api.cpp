@@ -12,8 +12,8 @@ namespace {
 
 thread_local int32_t g_last_hip_error = 0;
 
-constexpr int kTargetWaves = 2048;     // wavefronts per decode launch to fill 256 CUs
-constexpr int kMinChunksPerSplit = 4;  // 128 tokens: keeps the partials small
+constexpr int kTargetWaves = 2048;  // wavefronts per decode launch: 8 per CU on 256 CUs
+constexpr int kMinChunksPerWave = 4;  // 128 tokens per wavefront at least
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -37,9 +37,10 @@ kvq_status hip_status(hipError_t e) {
 int32_t auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
   const int64_t chunks = ((int64_t)max_seq_len + 31) / 32;
   if (chunks <= 0) return 1;
-  const int64_t units = (int64_t)batch * num_kv_heads;
+  const int64_t units = (int64_t)batch * num_kv_heads * kvq::kDecodeWaves;
   int64_t s = (kTargetWaves + units - 1) / units;
-  const int64_t cap = (chunks + kMinChunksPerSplit - 1) / kMinChunksPerSplit;
+  const int64_t per_split = (int64_t)kMinChunksPerWave * kvq::kDecodeWaves;
+  const int64_t cap = (chunks + per_split - 1) / per_split;
   if (s > cap) s = cap;
   if (s < 1) s = 1;
   return (int32_t)s;

@@ -43,6 +43,7 @@ namespace kvq {
 static constexpr float kLog2e = 1.4426950408889634f;
 static constexpr float kLn2 = 0.6931471805599453f;
 static constexpr float kRescaleSlack = 8.0f;  // log2 of the largest unnormalised p
+static constexpr int kWaves = kDecodeWaves;   // wavefronts per decode workgroup
 
 template <int D, int FMT>
 struct ChunkRegs {
@@ -50,10 +51,10 @@ struct ChunkRegs {
   static constexpr int VW = D / 128;   // V dwords per lane and token (D/32 bytes)
   u32x4_t kw[2][VEC];
   uint32_t ks[2][VEC];  // NVFP4: dword holding the lane's two E4M3 block scales
-  float4_t ksc[2];      // INT4: K scales of tokens 4j..4j+3
+  uint32_t ksc[2];      // INT4: K scale (fp32 bits) of token 4j + r%4 (quad-broadcast later)
   uint32_t vw[2][4][VW];
   uint32_t vs[2];     // NVFP4: one dword of the half's V scales (see load)
-  float4_t vsc[2];    // INT4: V scales of tokens 4j..4j+3
+  uint32_t vsc[2];    // INT4: V scale (fp32 bits) of token 4j + r%4
 };
 
 template <int D, int FMT>
@@ -77,19 +78,53 @@ struct Decoder {
     vo_k = r * (D / 2) + 16 * j;                           // K code row r
     vo_ks = r * (D / 16) + 4 * (j >> 1);                   // K scale row r
     vo_vs = (4 * j + (r & 3)) * (D / 16) + 4 * (((r >> 2) * D) / 256);
-    vo_sc = 4 * j * 4;                                     // INT4 scales of rows 4j..4j+3
+    vo_sc = (4 * j + (r & 3)) * 4;                         // INT4 scale of row 4j + r%4
     vo_v = 4 * j * (D / 2) + r * (D / 32);                 // V code rows 4j + i
   }
 
-  // Page-table entries of the two 16-token halves of chunk c, fetched with a
-  // vector load (kept out of the scalar counter) well before they are used.
-  // A half past the end of the sequence repeats the first half's entry.
-  __device__ inline int2 fetch_pages(int c) const {
-    const int T = c * 32;
-    int i0 = T / p.page_size;
-    int i1 = (T + 16 < L) ? (T + 16) / p.page_size : i0;
+  // Position of a chunk in the page table, advanced without division: the
+  // chunk's first token T = page_idx * page_size + row.
+  struct Cursor {
+    int c, page_idx, row;
+  };
+
+  __device__ inline Cursor cursor_at(int c) const {
+    const int T = __builtin_amdgcn_readfirstlane(c * 32);
+    return Cursor{__builtin_amdgcn_readfirstlane(c), T / p.page_size, T % p.page_size};
+  }
+
+  // Move the cursor `stride` chunks on (at most up to chunk `clast`), with
+  // the precomputed quotient and remainder of 32 * stride by the page size.
+  __device__ inline void advance(Cursor& k, int stride, int clast, int dq, int dr) const {
+    if (k.c + stride > clast) return;
+    k.c += stride;
+    k.page_idx += dq;
+    k.row += dr;
+    if (k.row >= p.page_size) {
+      k.row -= p.page_size;
+      k.page_idx += 1;
+    }
+  }
+
+  // Where a chunk's two 16-token halves live: page ids (read with a vector
+  // load, kept out of the scalar counter, well before use) and rows.  A half
+  // past the end of the sequence repeats the first half.
+  struct ChunkRef {
+    int2 pg;
+    int row0, row1;
+  };
+
+  __device__ inline ChunkRef fetch(const Cursor& k) const {
+    int i0 = k.page_idx, i1 = k.page_idx, row1 = k.row;
+    if (k.c * 32 + 16 < L) {
+      row1 = k.row + 16;
+      if (row1 >= p.page_size) {
+        row1 -= p.page_size;
+        i1 += 1;
+      }
+    }
     asm volatile("" : "+v"(i0), "+v"(i1));
-    return make_int2(ld_global<int32_t>(pages + i0), ld_global<int32_t>(pages + i1));
+    return ChunkRef{make_int2(ld_global<int32_t>(pages + i0), ld_global<int32_t>(pages + i1)), k.row, row1};
   }
 
   // Buffer descriptor of one slab: base address in SGPRs, range-checked to
@@ -100,39 +135,40 @@ struct Decoder {
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)p.slab, 0x00020000);
   }
 
-  __device__ inline void load(Regs& R, int c, int2 pg) const {
-    const int T = c * 32;
-    const int off0 = T % p.page_size;
-    const int off1 = (T + 16 < L) ? (T + 16) % p.page_size : off0;
+  __device__ inline void load(Regs& R, const ChunkRef& ref) const {
+    const int2 pg = ref.pg;
+    const int off0 = ref.row0, off1 = ref.row1;
 #pragma unroll
     for (int h = 0; h < 2; h++) {
+      // the descriptor is uniform (page id read from lane 0); all per-chunk
+      // offsets go through the VGPR offset so no operand needs to be uniform
       const __amdgpu_buffer_rsrc_t rs = slab_rsrc(__builtin_amdgcn_readfirstlane(h == 0 ? pg.x : pg.y));
       const int off = h == 0 ? off0 : off1;
+      const int ko = off * (D / 2), so = (int)p.scales_off + off * (FMT == FMT_NVFP4 ? D / 16 : 4);
       // K codes: row off + r, bytes 64v + 16j
 #pragma unroll
-      for (int v = 0; v < VEC; v++)
-        R.kw[h][v] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo_k + 64 * v, off * (D / 2), 0);
+      for (int v = 0; v < VEC; v++) R.kw[h][v] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo_k + ko + 64 * v, 0, 0);
       if (FMT == FMT_NVFP4) {
 #pragma unroll
-        for (int v = 0; v < VEC; v++)
-          R.ks[h][v] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_ks + 8 * v, (int)p.scales_off + off * (D / 16), 0);
+        for (int v = 0; v < VEC; v++) R.ks[h][v] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_ks + so + 8 * v, 0, 0);
         // Lane (j, r) with quad Q = r / 4 loads the dword of V-scale row 4j + r%4
         // that holds block (r * D / 256), the block every lane of quad Q needs;
         // compute() broadcasts row i of the quad with a DPP quad_perm.
-        R.vs[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_vs, (int)(p.half + p.scales_off) + off * (D / 16), 0);
+        R.vs[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_vs + (int)p.half + so, 0, 0);
       } else {
-        R.ksc[h] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo_sc, (int)p.scales_off + off * 4, 0));
-        R.vsc[h] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo_sc, (int)(p.half + p.scales_off) + off * 4, 0));
+        R.ksc[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_sc + so, 0, 0);
+        R.vsc[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_sc + (int)p.half + so, 0, 0);
       }
       // V codes: rows off + 4j + i, the lane's D/32-byte segment r
 #pragma unroll
       for (int i = 0; i < 4; i++) {
+        const int vo = vo_v + (int)p.half + ko + i * (D / 2);
         if (VW == 2) {
-          const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo_v + i * (D / 2), (int)p.half + off * (D / 2), 0);
+          const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, 0, 0);
           R.vw[h][i][0] = w.x;
           R.vw[h][i][VW - 1] = w.y;
         } else {
-          R.vw[h][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_v + i * (D / 2), (int)p.half + off * (D / 2), 0);
+          R.vw[h][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo, 0, 0);
         }
       }
     }
@@ -169,12 +205,15 @@ struct Decoder {
 // low-order fp16 part of the probabilities, so P = hi + lo costs no extra
 // MFMA; otherwise the low part takes a second MFMA per tile.
 template <int D, int FMT, bool DUP>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(
+    const DecodeParams p) {
   using Dec = Decoder<D, FMT>;
   using Regs = typename Dec::Regs;
   constexpr int VEC = Dec::VEC, VW = Dec::VW, KCH = Dec::KCH, VT = Dec::VT;
+  extern __shared__ float smem[];  // [G][D] partial o, then [kWaves][G] (m, l)
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int L = p.seq_lens[b];
   const int G = p.group;
@@ -183,16 +222,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   float* ml = p.part_ml + part * G * 2;
   float* po = p.part_o + part * G * D;
 
+  // The workgroup's split [c0, c1) of 32-token chunks is dealt to its waves
+  // round-robin: wave w takes chunks c0 + w, c0 + w + kWaves, ...
   const int nchunks = (L + 31) / 32;
   const int c0 = split * p.chunks_per_split;
   const int c1 = min(nchunks, c0 + p.chunks_per_split);
   if (c0 >= c1) {
-    if (j == 0 && n < G) {
-      ml[2 * n] = -__builtin_inff();
-      ml[2 * n + 1] = 0.0f;
+    // empty split: (m, l) = (-inf, 0) and a zero o, so the merge can weight
+    // every partial without a branch
+    for (int i = threadIdx.x; i < G * D; i += 64 * kWaves) po[i] = 0.0f;
+    if (threadIdx.x < G) {
+      ml[2 * threadIdx.x] = -__builtin_inff();
+      ml[2 * threadIdx.x + 1] = 0.0f;
     }
     return;
   }
+  const int cw0 = c0 + wave;  // this wave's first chunk (may be >= c1)
 
   Dec dec(p, lane, b, g, L);
 
@@ -275,8 +320,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     float cmax = -__builtin_inff();
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-      const float ksc[4] = {R.ksc[h].x, R.ksc[h].y, R.ksc[h].z, R.ksc[h].w};
-      const float vsc[4] = {R.vsc[h].x, R.vsc[h].y, R.vsc[h].z, R.vsc[h].w};
+      float ksc[4] = {}, vsc[4] = {};
+      if (FMT == FMT_INT4) {
+        // scales of tokens 4j + q, held by lane q of every quad
+        ksc[0] = as_f32(quad_bcast<0>(R.ksc[h]));
+        ksc[1] = as_f32(quad_bcast<1>(R.ksc[h]));
+        ksc[2] = as_f32(quad_bcast<2>(R.ksc[h]));
+        ksc[3] = as_f32(quad_bcast<3>(R.ksc[h]));
+        vsc[0] = as_f32(quad_bcast<0>(R.vsc[h]));
+        vsc[1] = as_f32(quad_bcast<1>(R.vsc[h]));
+        vsc[2] = as_f32(quad_bcast<2>(R.vsc[h]));
+        vsc[3] = as_f32(quad_bcast<3>(R.vsc[h]));
+      }
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const bool valid = T + 16 * h + 4 * j + q < L;
@@ -327,25 +382,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       }
     }
     const half8_t pop = DUP ? (n < 8 ? pop_hi : pop_lo) : pop_hi;
-    // ---------------- V: nibble-interleave token pairs (2i, 2i+1)
-    uint32_t pw[2][2][VW][2];  // [half][pair][dword][lo/hi or W0/W1]
+    // ---------------- V scales of the token pairs (2pp, 2pp + 1) of each half
     half2_t vsc2[2][2];
+    if (FMT == FMT_NVFP4) {
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
+      for (int h = 0; h < 2; h++) {
 #pragma unroll
-      for (int pp = 0; pp < 2; pp++) {
-#pragma unroll
-        for (int d = 0; d < VW; d++) {
-          const uint32_t a = R.vw[h][2 * pp][d], bb = R.vw[h][2 * pp + 1][d];
-          if (FMT == FMT_NVFP4) {
-            pw[h][pp][d][0] = bitfield_insert(0x0F0F0F0Fu, a, bb << 4);
-            pw[h][pp][d][1] = bitfield_insert(0x0F0F0F0Fu, a >> 4, bb);
-          } else {
-            pw[h][pp][d][0] = byte_perm(bb, a, 0x05040100u) ^ 0x88888888u;
-            pw[h][pp][d][1] = byte_perm(bb, a, 0x07060302u) ^ 0x88888888u;
-          }
-        }
-        if (FMT == FMT_NVFP4) {
+        for (int pp = 0; pp < 2; pp++) {
           const bool va = T + 16 * h + 4 * j + 2 * pp < L, vb = T + 16 * h + 4 * j + 2 * pp + 1 < L;
           // dwords of scale rows 4j + 2pp and 4j + 2pp + 1 (quad lanes 2pp, 2pp+1)
           const uint32_t d0 = pp == 0 ? quad_bcast<0>(R.vs[h]) : quad_bcast<2>(R.vs[h]);
@@ -355,41 +398,61 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         }
       }
     }
-    // ---------------- PV
+    // ---------------- PV, in groups of 4 tiles that share one interleaved
+    // word per token pair: token pairs (2i, 2i+1) are nibble-interleaved so
+    // that one conversion yields (token a, token b) of a single channel.
 #pragma unroll
-    for (int t = 0; t < VT; t++) {
-      const int d = t / 8, cc = t % 8;
-      half2_t parts[4];
+    for (int d = 0; d < VW; d++) {
 #pragma unroll
-      for (int h = 0; h < 2; h++) {
+      for (int sel = 0; sel < 2; sel++) {
+        uint32_t pw[2][2];
 #pragma unroll
-        for (int pp = 0; pp < 2; pp++) {
-          half2_t x;
-          if (FMT == FMT_NVFP4) {
-            const uint32_t word = pw[h][pp][d][cc & 1];
-            switch (cc >> 1) {
-              case 0: x = e2m1x2_to_h2<0>(word); break;
-              case 1: x = e2m1x2_to_h2<1>(word); break;
-              case 2: x = e2m1x2_to_h2<2>(word); break;
-              default: x = e2m1x2_to_h2<3>(word); break;
-            }
-            x = x * vsc2[h][pp];
-          } else {
-            const uint32_t word = pw[h][pp][d][cc >> 2];
-            switch (cc & 3) {
-              case 0: x = int4x2_to_h2<0>(word); break;
-              case 1: x = int4x2_to_h2<1>(word); break;
-              case 2: x = int4x2_to_h2<2>(word); break;
-              default: x = int4x2_to_h2<3>(word); break;
+        for (int h = 0; h < 2; h++) {
+#pragma unroll
+          for (int pp = 0; pp < 2; pp++) {
+            const uint32_t a = R.vw[h][2 * pp][d], bb = R.vw[h][2 * pp + 1][d];
+            if (FMT == FMT_NVFP4)  // bytes hold (a, b) nibbles of even (sel 0) or odd (sel 1) channels
+              pw[h][pp] = sel == 0 ? bitfield_insert(0x0F0F0F0Fu, a, bb << 4) : bitfield_insert(0x0F0F0F0Fu, a >> 4, bb);
+            else  // nibble p of a and of b at positions p and p + 4 (channels 4 sel + p)
+              pw[h][pp] = byte_perm(bb, a, sel == 0 ? 0x05040100u : 0x07060302u) ^ 0x88888888u;
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const int cc = FMT == FMT_NVFP4 ? 2 * k + sel : 4 * sel + k;  // channel within the dword
+          const int t = 8 * d + cc;
+          half2_t parts[4];
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+#pragma unroll
+            for (int pp = 0; pp < 2; pp++) {
+              const uint32_t word = pw[h][pp];
+              half2_t x;
+              if (FMT == FMT_NVFP4) {
+                switch (k) {
+                  case 0: x = e2m1x2_to_h2<0>(word); break;
+                  case 1: x = e2m1x2_to_h2<1>(word); break;
+                  case 2: x = e2m1x2_to_h2<2>(word); break;
+                  default: x = e2m1x2_to_h2<3>(word); break;
+                }
+                x = x * vsc2[h][pp];
+              } else {
+                switch (k) {
+                  case 0: x = int4x2_to_h2<0>(word); break;
+                  case 1: x = int4x2_to_h2<1>(word); break;
+                  case 2: x = int4x2_to_h2<2>(word); break;
+                  default: x = int4x2_to_h2<3>(word); break;
+                }
+              }
+              parts[2 * h + pp] = x;
             }
           }
-          parts[2 * h + pp] = x;
+          const half8_t a = {parts[0][0], parts[0][1], parts[1][0], parts[1][1],
+                             parts[2][0], parts[2][1], parts[3][0], parts[3][1]};
+          oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop, oacc[t], 0, 0, 0);
+          if (!DUP) oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop_lo, oacc[t], 0, 0, 0);
         }
       }
-      const half8_t a = {parts[0][0], parts[0][1], parts[1][0], parts[1][1],
-                         parts[2][0], parts[2][1], parts[3][0], parts[3][1]};
-      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop, oacc[t], 0, 0, 0);
-      if (!DUP) oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop_lo, oacc[t], 0, 0, 0);
     }
   };
 
@@ -398,22 +461,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   // repeat the last chunk, an L2 hit) so the wait counts stay exact.
   // Each page-table fetch is issued before the chunk loads that precede its
   // use, so waiting for it never waits for chunk data (the counter is in order).
-  const int clast = c1 - 1;
-  Regs RA, RB;
-  const int2 pg0 = dec.fetch_pages(c0);
-  int2 pg1 = dec.fetch_pages(min(c0 + 1, clast));
-  dec.load(RA, c0, pg0);
-  for (int c = c0; c < c1; c += 2) {
-    const int2 pg2 = dec.fetch_pages(min(c + 2, clast));
-    dec.load(RB, min(c + 1, clast), pg1);
-    compute(RA, c);
-    if (c + 1 >= c1) break;
-    pg1 = dec.fetch_pages(min(c + 3, clast));
-    dec.load(RA, min(c + 2, clast), pg2);
-    compute(RB, c + 1);
+  constexpr int S1 = kWaves;
+  if (cw0 < c1) {
+    // last chunk of this wave's sequence c, c + S1, ...
+    const int clast = cw0 + (c1 - 1 - cw0) / S1 * S1;
+    Regs RA, RB;
+    const int dq = (32 * S1) / p.page_size, dr = (32 * S1) % p.page_size;
+    auto fc = dec.cursor_at(cw0);  // page-table fetch position, two chunks ahead
+    const auto ref0 = dec.fetch(fc);
+    dec.advance(fc, S1, clast, dq, dr);
+    auto ref1 = dec.fetch(fc);
+    dec.advance(fc, S1, clast, dq, dr);
+    dec.load(RA, ref0);
+    // scheduling barriers keep each chunk's loads ahead of the previous
+    // chunk's math and stop the two computes from interleaving (which would
+    // raise register pressure past two wavefronts per SIMD)
+    for (int c = cw0; c <= clast; c += 2 * S1) {
+      const auto ref2 = dec.fetch(fc);
+      dec.advance(fc, S1, clast, dq, dr);
+      dec.load(RB, ref1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(RA, c);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c + S1 > clast) break;
+      ref1 = dec.fetch(fc);
+      dec.advance(fc, S1, clast, dq, dr);
+      dec.load(RA, ref2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(RB, c + S1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
-  // ---- partial results
+  // ---- partial results: reduce the lanes, then the waves (in LDS)
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (DUP) {
@@ -424,43 +504,84 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       for (int rr = 0; rr < 4; rr++) oacc[t][rr] += __shfl_xor(oacc[t][rr], 8, 64);
     }
   }
+  float* sm_o = smem;              // [G][D]: the waves' o, accumulated in wave order
+  float* sm_ml = smem + G * D;     // [kWaves][G][2]
+  if (j == 0 && n < G) {
+    sm_ml[(wave * G + n) * 2] = m_run;
+    sm_ml[(wave * G + n) * 2 + 1] = l_run;
+  }
+  __syncthreads();
+  float scale_o = 0.0f;
   if (n < G) {
-    if (j == 0) {
-      ml[2 * n] = m_run;
-      ml[2 * n + 1] = l_run;
-    }
-    const float scale_o = FMT == FMT_NVFP4 ? p.gs[1] : 1.0f;
-    float* dst = po + (int64_t)n * D;
-    // O^T tile t, row 4j + rr <-> channel (4j + rr) * (D/16) + t
+    float M = -__builtin_inff();
 #pragma unroll
-    for (int rr = 0; rr < 4; rr++) {
-      float* row = dst + (4 * j + rr) * VT;
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, sm_ml[(w * G + n) * 2]);
+    scale_o = m_run == -__builtin_inff() ? 0.0f : exp2f(m_run - M) * (FMT == FMT_NVFP4 ? p.gs[1] : 1.0f);
+  }
 #pragma unroll
-      for (int t = 0; t < VT; t += 4)
-        *(float4*)(row + t) = make_float4(oacc[t][rr] * scale_o, oacc[t + 1][rr] * scale_o,
-                                          oacc[t + 2][rr] * scale_o, oacc[t + 3][rr] * scale_o);
+  for (int w = 0; w < kWaves; w++) {
+    if (wave == w && n < G) {
+      float* dst = sm_o + n * D;
+      // O^T tile t, row 4j + rr <-> channel (4j + rr) * (D/16) + t
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) {
+        float* row = dst + (4 * j + rr) * VT;
+#pragma unroll
+        for (int t = 0; t < VT; t += 4) {
+          float4 x = make_float4(oacc[t][rr] * scale_o, oacc[t + 1][rr] * scale_o, oacc[t + 2][rr] * scale_o,
+                                 oacc[t + 3][rr] * scale_o);
+          if (w > 0) {
+            const float4 y = *(float4*)(row + t);
+            x.x += y.x;
+            x.y += y.y;
+            x.z += y.z;
+            x.w += y.w;
+          }
+          *(float4*)(row + t) = x;
+        }
+      }
     }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < G * D; i += 64 * kWaves) po[i] = sm_o[i];
+  if (threadIdx.x < G) {
+    const int q = threadIdx.x;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, sm_ml[(w * G + q) * 2]);
+    float l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+      const float mw = sm_ml[(w * G + q) * 2];
+      if (mw != -__builtin_inff()) l += exp2f(mw - M) * sm_ml[(w * G + q) * 2 + 1];
+    }
+    ml[2 * q] = M;
+    ml[2 * q + 1] = l;
   }
 }
 
 // Merge the splits of one (sequence, query head): M = max m_s,
 // o = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s, lse = (M + log2 sum) ln 2.
-// One workgroup per (sequence, query head, 64-channel block): its 256 threads
-// scan the (m, l) pairs together, then 4 groups of 64 threads accumulate
-// interleaved splits for their channel and are summed in LDS.  Every sum runs
-// in a fixed order, so the result is reproducible.
+// One workgroup per (sequence, query head, 64-channel block).  Its 256 threads
+// scan the (m, l) pairs together and stage the split weights 2^(m_s - M) in
+// LDS (0 for an empty split, whose partial o is zero); then 4 groups of 64
+// threads accumulate interleaved splits for their channel, branch-free, and
+// are summed in LDS.  Every sum runs in a fixed order: reproducible.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
-  constexpr int CW = 64, SG = 4, NCB = D / CW;
+  constexpr int CW = 64, SG = 4, NCB = D / CW, WTILE = 4096;
   const int cb = blockIdx.x % NCB, h = blockIdx.x / NCB, b = blockIdx.y;
-  const int tid = threadIdx.x, sg = tid / CW, c = cb * CW + tid % CW;
+  const int tid = threadIdx.x, sg = tid / CW, cl = tid % CW, c = cb * CW + cl;
   const int G = p.group, g = h / G, n = h % G, S = p.num_splits;
   const int64_t part0 = ((int64_t)b * p.num_kv_heads + g) * S;
+  const float* mlp = p.part_ml + (part0 * G + n) * 2;  // split s at mlp[s * 2G]
+  const float* op = p.part_o + (part0 * G + n) * D + c;  // split s at op[s * G * D]
   __shared__ float red[256];
+  __shared__ float wts[WTILE];
   __shared__ float acc_s[SG][CW];
 
   float m = -__builtin_inff();
-  for (int s = tid; s < S; s += 256) m = fmaxf(m, p.part_ml[((part0 + s) * G + n) * 2]);
+  for (int s = tid; s < S; s += 256) m = fmaxf(m, mlp[(int64_t)s * 2 * G]);
   red[tid] = m;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
@@ -470,49 +591,49 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
   const float M = red[0];
   __syncthreads();
 
-  float den = 0.0f;
-  for (int s = tid; s < S; s += 256) {
-    const float ms = p.part_ml[((part0 + s) * G + n) * 2];
-    if (ms != -__builtin_inff()) den += exp2f(ms - M) * p.part_ml[((part0 + s) * G + n) * 2 + 1];
+  float den = 0.0f, o = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += WTILE) {
+    const int ns = min(WTILE, S - s0);
+    for (int s = tid; s < ns; s += 256) {
+      const float ms = mlp[(int64_t)(s0 + s) * 2 * G];
+      const float w = ms == -__builtin_inff() ? 0.0f : exp2f(ms - M);
+      wts[s] = w;
+      den += w * mlp[(int64_t)(s0 + s) * 2 * G + 1];
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int s = sg; s < ns; s += SG) o += wts[s] * op[(int64_t)(s0 + s) * G * D];
+    __syncthreads();
   }
   red[tid] = den;
+  acc_s[sg][cl] = o;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
     if (tid < w) red[tid] += red[tid + w];
     __syncthreads();
   }
   den = red[0];
-
-  float o = 0.0f;
-  if (M != -__builtin_inff()) {
-#pragma unroll 4
-    for (int s = sg; s < S; s += SG) {
-      const float ms = p.part_ml[((part0 + s) * G + n) * 2];
-      if (ms != -__builtin_inff()) o += exp2f(ms - M) * p.part_o[((part0 + s) * G + n) * D + c];
-    }
-  }
-  acc_s[sg][tid % CW] = o;
-  __syncthreads();
   if (sg != 0) return;
-  o = acc_s[0][tid] + acc_s[1][tid] + acc_s[2][tid] + acc_s[3][tid];
+  o = acc_s[0][cl] + acc_s[1][cl] + acc_s[2][cl] + acc_s[3][cl];
   o = den > 0.0f ? o / den : 0.0f;
   const int64_t oi = ((int64_t)b * p.num_q_heads + h) * D + c;
   if (p.out_bf16)
     ((uint16_t*)p.out)[oi] = f32_to_bf16_rne(o);
   else
     ((float*)p.out)[oi] = o;
-  if (p.lse != nullptr && cb == 0 && tid == 0)
+  if (p.lse != nullptr && cb == 0 && cl == 0)
     p.lse[(int64_t)b * p.num_q_heads + h] = den > 0.0f ? (M + log2f(den)) * kLn2 : -__builtin_inff();
 }
 
 hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream_t stream) {
-  const dim3 grid(p.num_splits, p.num_kv_heads, p.batch), block(64);
+  const dim3 grid(p.num_splits, p.num_kv_heads, p.batch), block(64 * kWaves);
+  const size_t lds = (size_t)p.group * (head_dim + 2 * kWaves) * sizeof(float);
   const dim3 mgrid(p.num_q_heads * (head_dim / 64), p.batch);
   const bool dup = p.group <= 8;
 #define KVQ_DECODE(D, F)                                                                        \
   do {                                                                                          \
-    if (dup) hipLaunchKernelGGL((decode_kernel<D, F, true>), grid, block, 0, stream, p);        \
-    else hipLaunchKernelGGL((decode_kernel<D, F, false>), grid, block, 0, stream, p);           \
+    if (dup) hipLaunchKernelGGL((decode_kernel<D, F, true>), grid, block, lds, stream, p);      \
+    else hipLaunchKernelGGL((decode_kernel<D, F, false>), grid, block, lds, stream, p);         \
   } while (0)
   if (head_dim == 256) {
     if (fmt == FMT_NVFP4) KVQ_DECODE(256, FMT_NVFP4);

@@ -6,6 +6,10 @@
 
 namespace kvq {
 
+// Wavefronts per decode workgroup: each takes every kDecodeWaves-th 32-token
+// chunk of the workgroup's split, and the workgroup merges them in LDS.
+constexpr int kDecodeWaves = 4;
+
 struct StoreParams {
   uint8_t* pool;
   const float* gs;  // {gs_K, gs_V} (NVFP4)

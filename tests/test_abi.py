@@ -106,14 +106,16 @@ def test_workspace_and_split_plan(lib):
     size = ctypes.c_size_t(0)
     assert lib.kvq_decode_num_splits(ctypes.byref(c), 32, 24, 32768, ctypes.byref(splits)) == OK
     S = splits.value
-    assert S >= 1 and 32 * 4 * S >= 1024                      # enough wavefronts for 256 CUs
+    assert S >= 1 and 32 * 4 * S * 4 >= 2048                  # 4-wave groups: >= 8 wavefronts per CU
     assert lib.kvq_decode_workspace_size(ctypes.byref(c), 32, 24, 32768, 0, ctypes.byref(size)) == OK
     assert size.value == 32 * 4 * S * 6 * (256 + 2) * 4
     assert lib.kvq_decode_workspace_size(ctypes.byref(c), 2, 8, 100, 3, ctypes.byref(size)) == OK
     assert size.value == 2 * 4 * 3 * 2 * (256 + 2) * 4
-    # short contexts never get more splits than 4-chunk (128-token) pieces
+    # each of a split's 4 wavefronts gets at least 4 chunks (128 tokens)
     assert lib.kvq_decode_num_splits(ctypes.byref(c), 1, 4, 200, ctypes.byref(splits)) == OK
-    assert splits.value == 2
+    assert splits.value == 1
+    assert lib.kvq_decode_num_splits(ctypes.byref(c), 1, 4, 4096, ctypes.byref(splits)) == OK
+    assert splits.value == 8
     assert lib.kvq_decode_num_splits(ctypes.byref(c), 1, 4, 0, ctypes.byref(splits)) == OK
     assert splits.value == 1
     assert lib.kvq_decode_num_splits(ctypes.byref(c), 1, 4, 10, None) == ERR_NULL

@@ -1,0 +1,179 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (automatic split plan), on sampled outputs the oracle computes
+one by one.
+
+Each test fills one layer's cache on the GPU through the C ABI, then checks:
+packed bytes of sampled rows against the oracle's quantization of the same
+input rows (bit-exact); decode attention of sampled (sequence, query head)
+pairs against the oracle run on that sequence's pages copied to the host
+(tolerance of gpu_cases); and, where the workload has them, the chunked-prefill
+store and prefix dequantization of sampled pages (bit-exact)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_quantized_kv_amd import inputs, kvq
+from gpu_cases import check_attention
+
+pytestmark = pytest.mark.gpu
+
+HKV, HQ, D = 4, 24, 256
+G = HQ // HKV
+
+
+def student_t4(g, shape):
+    z = torch.randn(shape, generator=g, device="cuda")
+    chi2 = torch.zeros(shape, device="cuda")
+    for _ in range(4):
+        chi2 += torch.randn(shape, generator=g, device="cuda") ** 2
+    return z / torch.sqrt(chi2 / 4.0) / math.sqrt(2.0)
+
+
+class FullLayer:
+    """One layer at full size: cache filled on the GPU, inputs regenerable."""
+
+    def __init__(self, wid, fmt, B, L, P, shuffled, kind, chunk=1 << 16):
+        self.wid, self.fmt, self.B, self.L, self.P, self.kind = wid, fmt, B, L, P, kind
+        self.pps = -(-L // P)
+        self.num_pages = B * self.pps
+        self.bt = inputs.page_tables(wid, B, self.pps, self.num_pages, shuffled=shuffled)
+        self.bt_dev = torch.from_numpy(self.bt).cuda()
+        self.cache = kvq.Cache(fmt, self.num_pages, P, HKV, D, device="cuda")
+        self.cache.pool.fill_(0xFF)  # poison: bytes past each sequence stay NaN scales
+        self.chunk = chunk
+        self.samples = []  # (b, t, k_row [HKV][D], v_row) fp32 values of sampled tokens
+        rng = np.random.default_rng(wid)
+        g = torch.Generator(device="cuda")
+        if kind == "lognormal":
+            g.manual_seed(inputs.seed_int(wid, 0, inputs.STREAM_KSCALE))
+            kscale = torch.exp(torch.randn((HKV, D), generator=g, device="cuda"))
+            g.manual_seed(inputs.seed_int(wid, 0, inputs.STREAM_VSCALE))
+            vscale = torch.exp(torch.randn((HKV, D), generator=g, device="cuda"))
+        g.manual_seed(inputs.seed_int(wid, 0, inputs.STREAM_K))
+        for b in range(B):
+            for t0 in range(0, L, chunk):
+                t1 = min(L, t0 + chunk)
+                n = t1 - t0
+                if kind == "lognormal":
+                    k = (torch.randn((n, HKV, D), generator=g, device="cuda") * kscale).to(torch.bfloat16)
+                    v = (torch.randn((n, HKV, D), generator=g, device="cuda") * vscale).to(torch.bfloat16)
+                else:
+                    k = student_t4(g, (n, HKV, D)).to(torch.bfloat16)
+                    v = student_t4(g, (n, HKV, D)).to(torch.bfloat16)
+                slots = torch.from_numpy(inputs.slots_for(self.bt, P, b, t0, t1)).cuda()
+                kvq.kvq_quantize_store(self.cache, k, v, slots)
+                for t in rng.choice(n, size=2, replace=False):
+                    self.samples.append((b, t0 + int(t), k[t].float().cpu().numpy(), v[t].float().cpu().numpy()))
+        torch.cuda.synchronize()
+        g.manual_seed(inputs.seed_int(wid, 0, inputs.STREAM_Q))
+        self.q = torch.randn((B, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
+        self.lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+
+    def slab_rows(self, pool_np, b, t):
+        """(K codes, K scales, V codes, V scales) bytes of token t of sequence b, head-major."""
+        page, row = int(self.bt[b, t // self.P]), t % self.P
+        out = []
+        sl = pool_np[page]
+        half = sl.shape[1] // 2
+        srow = D // 16 if self.fmt == 1 else 4
+        for base in (0, half):
+            out.append(sl[:, base + row * (D // 2): base + (row + 1) * (D // 2)])
+            s0 = base + self.P * (D // 2) + row * srow
+            out.append(sl[:, s0: s0 + srow])
+        return out
+
+    def check_packing(self):
+        pool = self.cache.pool.cpu().numpy()
+        for b, t, krow, vrow in self.samples:
+            kc, ks, vc, vs = self.slab_rows(pool, b, t)
+            for g in range(HKV):
+                for x, codes, scales in ((krow[g], kc[g], ks[g]), (vrow[g], vc[g], vs[g])):
+                    if self.fmt == 1:
+                        rc, rs = oracle.nvfp4_quantize_row(x, 1.0)
+                        assert np.array_equal(codes, rc) and np.array_equal(scales, rs), (b, t, g)
+                    else:
+                        rc, s = oracle.int4_quantize_row(x)
+                        assert np.array_equal(codes, rc) and scales.view(np.float32)[0] == s, (b, t, g)
+        return pool
+
+    def check_decode(self, pool, seqs, heads_per_group=1, seed=0):
+        out = torch.empty((self.B, HQ, D), dtype=torch.float32, device="cuda")
+        lse = torch.empty((self.B, HQ), dtype=torch.float32, device="cuda")
+        kvq.kvq_decode_attention(self.cache, self.q, self.bt_dev, self.lens, self.L, out=out, lse=lse)
+        torch.cuda.synchronize()
+        out, lse = out.cpu().numpy(), lse.cpu().numpy()
+        rng = np.random.default_rng(seed)
+        qh = self.q.float().cpu().numpy()
+        for b in seqs:
+            heads = [g * G + int(x) for g in range(HKV) for x in rng.choice(G, heads_per_group, replace=False)]
+            # the sequence's pages, renumbered, and one query per sampled head
+            sub = oracle.Pool(self.fmt, self.pps, self.P, HKV, D)
+            sub.data[:] = pool[self.bt[b]]
+            bt = np.arange(self.pps, dtype=np.int32)[None]
+            # oracle with Hq = len(heads) * ... : order heads by KV group so h -> h // (n/HKV)
+            qs = qh[b, heads][None]
+            ref, ref_lse = sub.decode_attention(qs, bt, np.array([self.L], np.int32))
+            got = out[b, heads][None]
+            check_attention(got, ref, np.array([self.L]), lse=lse[b, heads][None], ref_lse=ref_lse,
+                            label=f"seq {b} heads {heads}")
+
+
+def test_full_32k_nvfp4_batch32():
+    # Qwen3.8-27B-shaped layer: 4 KV heads x D 256, 24 q heads, batch 32, 32,768 tokens, 16-token pages
+    print("case: full 32K NVFP4 layer", flush=True)
+    lay = FullLayer(2, 1, 32, 32768, 16, False, "lognormal")
+    pool = lay.check_packing()
+    lay.check_decode(pool, seqs=[0, 31], heads_per_group=1)
+
+
+def test_full_160k_nvfp4_shuffled_with_chunk_store():
+    print("case: full 160K NVFP4 layer, shuffled pages", flush=True)
+    lay = FullLayer(3, 1, 4, 160000, 16, True, "lognormal")
+    # 64-token chunked-prefill store per sequence into the last 64 positions
+    g = torch.Generator(device="cuda")
+    g.manual_seed(inputs.seed_int(3, 0, 40))
+    kc = torch.randn((4 * 64, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((4 * 64, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    slots = np.concatenate([inputs.slots_for(lay.bt, 16, b, 160000 - 64, 160000) for b in range(4)])
+    kvq.kvq_quantize_store(lay.cache, kc, vc, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    kh, vh = kc.float().cpu().numpy(), vc.float().cpu().numpy()
+    lay.samples = [s for s in lay.samples if s[1] < 160000 - 64]
+    for i in (0, 63, 64, 200, 255):
+        lay.samples.append((i // 64, 160000 - 64 + i % 64, kh[i], vh[i]))
+    pool = lay.check_packing()
+    lay.check_decode(pool, seqs=[1, 3], heads_per_group=1)
+
+
+def test_full_1m_nvfp4_split_context_and_prefix_dequant():
+    print("case: full 1M NVFP4 layer", flush=True)
+    L = 1048576
+    lay = FullLayer(4, 1, 1, L, 16, False, "lognormal")
+    pool = lay.check_packing()
+    lay.check_decode(pool, seqs=[0], heads_per_group=1)
+    # prefix dequant of the whole prefix into a (L + 4096)-row workspace;
+    # sampled page-aligned windows compared bit for bit
+    rows = L + 4096
+    k_ws = torch.empty((rows, HKV * D), dtype=torch.bfloat16, device="cuda")
+    v_ws = torch.empty((rows, HKV * D), dtype=torch.bfloat16, device="cuda")
+    kvq.kvq_dequant_prefix(lay.cache, lay.bt_dev[0], L, k_ws, v_ws)
+    torch.cuda.synchronize()
+    sub = oracle.Pool(1, lay.pps, 16, HKV, D)
+    sub.data[:] = pool[lay.bt[0]]
+    for t0 in (0, 16 * 4096, L - 64):
+        pages = np.arange(t0 // 16, (t0 + 64) // 16, dtype=np.int32)
+        rk, rv = sub.dequant_prefix(pages, 64)
+        for got, ref in ((k_ws, rk), (v_ws, rv)):
+            g = got[t0:t0 + 64].view(torch.int16).cpu().numpy().view(np.uint16).reshape(64, HKV, D)
+            assert np.array_equal(g, ref), t0
+    del k_ws, v_ws
+
+
+def test_full_int4_220k_page1600():
+    print("case: full INT4 220K layer", flush=True)
+    lay = FullLayer(5, 2, 8, 220000, 1600, False, "student_t")
+    pool = lay.check_packing()
+    lay.check_decode(pool, seqs=[0, 7], heads_per_group=1)

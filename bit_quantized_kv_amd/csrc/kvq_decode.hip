@@ -35,6 +35,8 @@
 //   scales are folded into the score (K) and into the probability (V).
 //   q is scaled by a power of two so its largest magnitude sits in
 //   [2^14, 2^15), keeping fp16 exact for every finite bf16 input range.
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -69,17 +71,19 @@ struct Decoder {
   const int lane, j, r, b, g, L;
   const uint8_t* head_base;  // pool + g * slab
   const int32_t* pages;      // block_table row of sequence b
-  int vo_k, vo_ks, vo_vs, vo_sc, vo_v;  // per-lane byte offsets inside a slab
+  int vo_k, vo_ks, vo_vs_h, vo_sc, vo_sc_h, vo_v_h;  // per-lane byte offsets inside a slab
 
   __device__ Decoder(const DecodeParams& p_, int lane_, int b_, int g_, int L_)
       : p(p_), lane(lane_), j(lane_ >> 4), r(lane_ & 15), b(b_), g(g_), L(L_) {
     head_base = p.pool + (int64_t)g * p.slab;
     pages = p.block_table + (int64_t)b * p.max_pages;
-    vo_k = r * (D / 2) + 16 * j;                           // K code row r
-    vo_ks = r * (D / 16) + 4 * (j >> 1);                   // K scale row r
-    vo_vs = (4 * j + (r & 3)) * (D / 16) + 4 * (((r >> 2) * D) / 256);
-    vo_sc = (4 * j + (r & 3)) * 4;                         // INT4 scale of row 4j + r%4
-    vo_v = 4 * j * (D / 2) + r * (D / 32);                 // V code rows 4j + i
+    // (the _h offsets include the K half, i.e. they address the V half)
+    vo_k = r * (D / 2) + 16 * j;                                            // K code row r
+    vo_ks = r * (D / 16) + 4 * (j >> 1);                                    // K scale row r
+    vo_vs_h = (int)p.half + (4 * j + (r & 3)) * (D / 16) + 4 * (((r >> 2) * D) / 256);
+    vo_sc = (4 * j + (r & 3)) * 4;                                          // INT4 scale of row 4j + r%4
+    vo_sc_h = (int)p.half + vo_sc;
+    vo_v_h = (int)p.half + 4 * j * (D / 2) + r * (D / 32);                  // V code rows 4j + i
   }
 
   // Position of a chunk in the page table, advanced without division: the
@@ -135,40 +139,41 @@ struct Decoder {
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)p.slab, 0x00020000);
   }
 
+  // Loads of one chunk: the descriptor and the chunk's row offsets are
+  // uniform (SGPR descriptor and soffset), the lane's position inside a row is
+  // a loop-invariant VGPR offset, and constant parts fold into the
+  // instruction's immediate offset, so issuing a load costs no VALU work.
   __device__ inline void load(Regs& R, const ChunkRef& ref) const {
     const int2 pg = ref.pg;
-    const int off0 = ref.row0, off1 = ref.row1;
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-      // the descriptor is uniform (page id read from lane 0); all per-chunk
-      // offsets go through the VGPR offset so no operand needs to be uniform
       const __amdgpu_buffer_rsrc_t rs = slab_rsrc(__builtin_amdgcn_readfirstlane(h == 0 ? pg.x : pg.y));
-      const int off = h == 0 ? off0 : off1;
-      const int ko = off * (D / 2), so = (int)p.scales_off + off * (FMT == FMT_NVFP4 ? D / 16 : 4);
+      const int off = __builtin_amdgcn_readfirstlane(h == 0 ? ref.row0 : ref.row1);
+      const int ko = off * (D / 2);
+      const int so = (int)p.scales_off + off * (FMT == FMT_NVFP4 ? D / 16 : 4);
       // K codes: row off + r, bytes 64v + 16j
 #pragma unroll
-      for (int v = 0; v < VEC; v++) R.kw[h][v] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo_k + ko + 64 * v, 0, 0);
+      for (int v = 0; v < VEC; v++) R.kw[h][v] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo_k + 64 * v, ko, 0);
       if (FMT == FMT_NVFP4) {
 #pragma unroll
-        for (int v = 0; v < VEC; v++) R.ks[h][v] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_ks + so + 8 * v, 0, 0);
+        for (int v = 0; v < VEC; v++) R.ks[h][v] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_ks + 8 * v, so, 0);
         // Lane (j, r) with quad Q = r / 4 loads the dword of V-scale row 4j + r%4
         // that holds block (r * D / 256), the block every lane of quad Q needs;
         // compute() broadcasts row i of the quad with a DPP quad_perm.
-        R.vs[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_vs + (int)p.half + so, 0, 0);
+        R.vs[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_vs_h, so, 0);
       } else {
-        R.ksc[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_sc + so, 0, 0);
-        R.vsc[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_sc + (int)p.half + so, 0, 0);
+        R.ksc[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_sc, so, 0);
+        R.vsc[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_sc_h, so, 0);
       }
       // V codes: rows off + 4j + i, the lane's D/32-byte segment r
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const int vo = vo_v + (int)p.half + ko + i * (D / 2);
         if (VW == 2) {
-          const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, 0, 0);
+          const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo_v_h + i * (D / 2), ko, 0);
           R.vw[h][i][0] = w.x;
           R.vw[h][i][VW - 1] = w.y;
         } else {
-          R.vw[h][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo, 0, 0);
+          R.vw[h][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_v_h + i * (D / 2), ko, 0);
         }
       }
     }
@@ -179,10 +184,11 @@ struct Decoder {
     const uint32_t word = w == 0 ? R.kw[h][v].x : w == 1 ? R.kw[h][v].y : w == 2 ? R.kw[h][v].z : R.kw[h][v].w;
     half2_t a0, a1, a2, a3;
     if (FMT == FMT_NVFP4) {
-      a0 = e2m1x2_to_h2<0>(word) * s2;
-      a1 = e2m1x2_to_h2<1>(word) * s2;
-      a2 = e2m1x2_to_h2<2>(word) * s2;
-      a3 = e2m1x2_to_h2<3>(word) * s2;
+      // (e2m1 * 2^8) * (scale * 2^-8): pairs of channels (2k, 2k + 1)
+      a0 = e2m1x2_to_h2_x256<0>(word) * s2;
+      a1 = e2m1x2_to_h2_x256<1>(word) * s2;
+      a2 = e2m1x2_to_h2_x256<2>(word) * s2;
+      a3 = e2m1x2_to_h2_x256<3>(word) * s2;
     } else {
       const uint32_t wb = word ^ 0x88888888u;
       a0 = int4x2_to_h2<0>(wb);
@@ -283,6 +289,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   }
   const float sm = p.sm_scale * kLog2e * ldexpf(1.0f, -kq) * (FMT == FMT_NVFP4 ? p.gs[0] : 1.0f);
 
+  const float lo_sel = n < 8 ? 0.0f : 1.0f;  // DUP: lanes n >= 8 carry the low fp16 part of p
   // byte of block (n * D / 256) within its scale dword, from two dwords -> bytes 0, 1
   const uint32_t vb_byte = ((n * D) / 256) & 3;
   const uint32_t vsel = vb_byte | ((4 + vb_byte) << 8) | 0x0C0C0000u;
@@ -293,7 +300,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
 
-  auto compute = [&](const Regs& R, int c) {
+  // FULL: all 32 tokens of the chunk are inside the sequence (no masking)
+  auto compute = [&](const Regs& R, int c, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int T = c * 32;
     // ---------------- QK
     float4_t sacc[2];
@@ -304,9 +313,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       for (int v = 0; v < VEC; v++) {
         half2_t s_lo = {}, s_hi = {};
         if (FMT == FMT_NVFP4) {
-          const float2_t s01 = __builtin_amdgcn_cvt_pk_f32_fp8(R.ks[h][v] >> (16 * (j & 1)), false);
-          s_lo = (half2_t){(_Float16)s01[0], (_Float16)s01[0]};
-          s_hi = (half2_t){(_Float16)s01[1], (_Float16)s01[1]};
+          // the lane's two block scales (bytes 0, 1), each as scale * 2^-8 in both halves
+          const uint32_t sb = R.ks[h][v] >> (16 * (j & 1));
+          s_lo = u32_as_h2(e4m3_to_h_x2m8(sb) * 0x00010001u);
+          s_hi = u32_as_h2(e4m3_to_h_x2m8(sb >> 8) * 0x00010001u);
         }
 #pragma unroll
         for (int w = 0; w < 4; w++) {
@@ -334,7 +344,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       }
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        const bool valid = T + 16 * h + 4 * j + q < L;
+        const bool valid = FULL || T + 16 * h + 4 * j + q < L;
         float x = sacc[h][q] * sm;
         if (FMT == FMT_INT4) x *= ksc[q];
         s[h][q] = valid ? x : -__builtin_inff();
@@ -348,8 +358,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         cmax = fmaxf(cmax, cand[h][q]);
       }
     }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    cmax = max_xor16_xor32(cmax);
     if (__builtin_amdgcn_ballot_w64(cmax > m_run + kRescaleSlack) != 0) {
       const float m_new = cmax > m_run + kRescaleSlack ? cmax : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -369,19 +378,23 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         pr[h][q] = FMT == FMT_INT4 ? e * sv[h][q] : e;
       }
     }
-    // p = hi + lo, both fp16: the PV product keeps ~22 bits of each p
-    half8_t pop_hi, pop_lo;
+    // p = hi + lo, both fp16: the PV product keeps ~22 bits of each p.  With
+    // DUP, lanes n < 8 feed hi and lanes n >= 8 (the repeated queries) feed lo:
+    // each lane converts p - sub with sub = 0 or its own hi.
+    half8_t pop, pop_lo;
 #pragma unroll
     for (int h = 0; h < 2; h++) {
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const _Float16 hi = (_Float16)pr[h][q];
-        const _Float16 lo = (_Float16)(pr[h][q] - (float)hi);
-        pop_hi[4 * h + q] = hi;
-        pop_lo[4 * h + q] = lo;
+        if (DUP) {
+          pop[4 * h + q] = (_Float16)(pr[h][q] - lo_sel * (float)hi);
+        } else {
+          pop[4 * h + q] = hi;
+          pop_lo[4 * h + q] = (_Float16)(pr[h][q] - (float)hi);
+        }
       }
     }
-    const half8_t pop = DUP ? (n < 8 ? pop_hi : pop_lo) : pop_hi;
     // ---------------- V scales of the token pairs (2pp, 2pp + 1) of each half
     half2_t vsc2[2][2];
     if (FMT == FMT_NVFP4) {
@@ -389,68 +402,102 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       for (int h = 0; h < 2; h++) {
 #pragma unroll
         for (int pp = 0; pp < 2; pp++) {
-          const bool va = T + 16 * h + 4 * j + 2 * pp < L, vb = T + 16 * h + 4 * j + 2 * pp + 1 < L;
-          // dwords of scale rows 4j + 2pp and 4j + 2pp + 1 (quad lanes 2pp, 2pp+1)
+          // dwords of scale rows 4j + 2pp and 4j + 2pp + 1 (quad lanes 2pp, 2pp+1);
+          // (s_a, s_b) * 2^-8 as an fp16 pair.  Past the end of the sequence the
+          // bytes are arbitrary but decode finite, and p is exactly 0 there.
           const uint32_t d0 = pp == 0 ? quad_bcast<0>(R.vs[h]) : quad_bcast<2>(R.vs[h]);
           const uint32_t d1 = pp == 0 ? quad_bcast<1>(R.vs[h]) : quad_bcast<3>(R.vs[h]);
-          const float2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(byte_perm(d1, d0, vsel), false);
-          vsc2[h][pp] = (half2_t){(_Float16)(va ? f[0] : 0.0f), (_Float16)(vb ? f[1] : 0.0f)};
+          const uint32_t ab = byte_perm(d1, d0, vsel);  // bytes [s_a, s_b, 0, 0]
+          vsc2[h][pp] = u32_as_h2(e4m3_to_h_x2m8(ab) | (e4m3_to_h_x2m8(ab >> 8) << 16));
         }
       }
     }
-    // ---------------- PV, in groups of 4 tiles that share one interleaved
-    // word per token pair: token pairs (2i, 2i+1) are nibble-interleaved so
-    // that one conversion yields (token a, token b) of a single channel.
+    // ---------------- PV.  The A operand of tile t holds channel t of the
+    // lane's 16-channel segment for the 8 tokens 4j..4j+3 of each half, as
+    // fp16 pairs (token 2i, token 2i + 1).
+    if (FMT == FMT_NVFP4) {
+      // token pairs (2i, 2i+1) nibble-interleaved so one conversion yields
+      // (token a, token b) of a single channel; groups of 4 tiles share the
+      // interleaved word of each pair (sel 0: even channels, 1: odd)
 #pragma unroll
-    for (int d = 0; d < VW; d++) {
+      for (int d = 0; d < VW; d++) {
 #pragma unroll
-      for (int sel = 0; sel < 2; sel++) {
-        uint32_t pw[2][2];
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-#pragma unroll
-          for (int pp = 0; pp < 2; pp++) {
-            const uint32_t a = R.vw[h][2 * pp][d], bb = R.vw[h][2 * pp + 1][d];
-            if (FMT == FMT_NVFP4)  // bytes hold (a, b) nibbles of even (sel 0) or odd (sel 1) channels
-              pw[h][pp] = sel == 0 ? bitfield_insert(0x0F0F0F0Fu, a, bb << 4) : bitfield_insert(0x0F0F0F0Fu, a >> 4, bb);
-            else  // nibble p of a and of b at positions p and p + 4 (channels 4 sel + p)
-              pw[h][pp] = byte_perm(bb, a, sel == 0 ? 0x05040100u : 0x07060302u) ^ 0x88888888u;
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-          const int cc = FMT == FMT_NVFP4 ? 2 * k + sel : 4 * sel + k;  // channel within the dword
-          const int t = 8 * d + cc;
-          half2_t parts[4];
+        for (int sel = 0; sel < 2; sel++) {
+          uint32_t pw[2][2];
 #pragma unroll
           for (int h = 0; h < 2; h++) {
 #pragma unroll
             for (int pp = 0; pp < 2; pp++) {
-              const uint32_t word = pw[h][pp];
-              half2_t x;
-              if (FMT == FMT_NVFP4) {
+              const uint32_t a = R.vw[h][2 * pp][d], bb = R.vw[h][2 * pp + 1][d];
+              pw[h][pp] = sel == 0 ? bitfield_insert(0x0F0F0F0Fu, a, bb << 4) : bitfield_insert(0x0F0F0F0Fu, a >> 4, bb);
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            const int t = 8 * d + 2 * k + sel;
+            half2_t parts[4];
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+#pragma unroll
+              for (int pp = 0; pp < 2; pp++) {
+                const uint32_t word = pw[h][pp];
+                half2_t x;
                 switch (k) {
-                  case 0: x = e2m1x2_to_h2<0>(word); break;
-                  case 1: x = e2m1x2_to_h2<1>(word); break;
-                  case 2: x = e2m1x2_to_h2<2>(word); break;
-                  default: x = e2m1x2_to_h2<3>(word); break;
+                  case 0: x = e2m1x2_to_h2_x256<0>(word); break;
+                  case 1: x = e2m1x2_to_h2_x256<1>(word); break;
+                  case 2: x = e2m1x2_to_h2_x256<2>(word); break;
+                  default: x = e2m1x2_to_h2_x256<3>(word); break;
                 }
-                x = x * vsc2[h][pp];
-              } else {
+                parts[2 * h + pp] = x * vsc2[h][pp];
+              }
+            }
+            const half8_t a = {parts[0][0], parts[0][1], parts[1][0], parts[1][1],
+                               parts[2][0], parts[2][1], parts[3][0], parts[3][1]};
+            oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop, oacc[t], 0, 0, 0);
+            if (!DUP) oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop_lo, oacc[t], 0, 0, 0);
+          }
+        }
+      }
+    } else {
+      // INT4: nibbles of tokens a, b interleaved 16 bits apart, so the 1024
+      // offset trick yields (a, b) of one channel per conversion
+#pragma unroll
+      for (int d = 0; d < VW; d++) {
+#pragma unroll
+        for (int sel = 0; sel < 2; sel++) {
+          uint32_t pw[2][2];
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+#pragma unroll
+            for (int pp = 0; pp < 2; pp++) {
+              const uint32_t a = R.vw[h][2 * pp][d], bb = R.vw[h][2 * pp + 1][d];
+              pw[h][pp] = byte_perm(bb, a, sel == 0 ? 0x05040100u : 0x07060302u) ^ 0x88888888u;
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            const int t = 8 * d + 4 * sel + k;
+            half2_t parts[4];
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+#pragma unroll
+              for (int pp = 0; pp < 2; pp++) {
+                const uint32_t word = pw[h][pp];
+                half2_t x;
                 switch (k) {
                   case 0: x = int4x2_to_h2<0>(word); break;
                   case 1: x = int4x2_to_h2<1>(word); break;
                   case 2: x = int4x2_to_h2<2>(word); break;
                   default: x = int4x2_to_h2<3>(word); break;
                 }
+                parts[2 * h + pp] = x;
               }
-              parts[2 * h + pp] = x;
             }
+            const half8_t a = {parts[0][0], parts[0][1], parts[1][0], parts[1][1],
+                               parts[2][0], parts[2][1], parts[3][0], parts[3][1]};
+            oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop, oacc[t], 0, 0, 0);
+            if (!DUP) oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop_lo, oacc[t], 0, 0, 0);
           }
-          const half8_t a = {parts[0][0], parts[0][1], parts[1][0], parts[1][1],
-                             parts[2][0], parts[2][1], parts[3][0], parts[3][1]};
-          oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop, oacc[t], 0, 0, 0);
-          if (!DUP) oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop_lo, oacc[t], 0, 0, 0);
         }
       }
     }
@@ -465,31 +512,34 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   if (cw0 < c1) {
     // last chunk of this wave's sequence c, c + S1, ...
     const int clast = cw0 + (c1 - 1 - cw0) / S1 * S1;
-    Regs RA, RB;
     const int dq = (32 * S1) / p.page_size, dr = (32 * S1) % p.page_size;
-    auto fc = dec.cursor_at(cw0);  // page-table fetch position, two chunks ahead
-    const auto ref0 = dec.fetch(fc);
-    dec.advance(fc, S1, clast, dq, dr);
-    auto ref1 = dec.fetch(fc);
-    dec.advance(fc, S1, clast, dq, dr);
-    dec.load(RA, ref0);
-    // scheduling barriers keep each chunk's loads ahead of the previous
-    // chunk's math and stop the two computes from interleaving (which would
-    // raise register pressure past two wavefronts per SIMD)
-    for (int c = cw0; c <= clast; c += 2 * S1) {
-      const auto ref2 = dec.fetch(fc);
+    {
+      const std::false_type full_tag{};  // masked chunk math (a second, mask-free copy spills registers)
+      Regs RA, RB;
+      auto fc = dec.cursor_at(cw0);  // page-table fetch position, two chunks ahead
+      const auto ref0 = dec.fetch(fc);
       dec.advance(fc, S1, clast, dq, dr);
-      dec.load(RB, ref1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(RA, c);
-      __builtin_amdgcn_sched_barrier(0);
-      if (c + S1 > clast) break;
-      ref1 = dec.fetch(fc);
+      auto ref1 = dec.fetch(fc);
       dec.advance(fc, S1, clast, dq, dr);
-      dec.load(RA, ref2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(RB, c + S1);
-      __builtin_amdgcn_sched_barrier(0);
+      dec.load(RA, ref0);
+      // scheduling barriers keep each chunk's loads ahead of the previous
+      // chunk's math and stop the two computes from interleaving (which would
+      // raise register pressure past two wavefronts per SIMD)
+      for (int c = cw0; c <= clast; c += 2 * S1) {
+        const auto ref2 = dec.fetch(fc);
+        dec.advance(fc, S1, clast, dq, dr);
+        dec.load(RB, ref1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(RA, c, full_tag);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + S1 > clast) break;
+        ref1 = dec.fetch(fc);
+        dec.advance(fc, S1, clast, dq, dr);
+        dec.load(RA, ref2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(RB, c + S1, full_tag);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 

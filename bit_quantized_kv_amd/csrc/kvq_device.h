@@ -72,6 +72,15 @@ __device__ inline uint32_t quad_bcast(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, I * 0x55, 0xF, 0xF, false);
 }
 
+// max over lanes {l, l^16, l^32, l^48} with the gfx950 lane-swap instructions
+// (VALU only, no LDS round trip).
+__device__ inline float max_xor16_xor32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+  x = fmaxf(as_f32(a[0]), as_f32(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  return fmaxf(as_f32(b[0]), as_f32(b[1]));
+}
+
 // ---------------------------------------------------------------- encoders
 
 // fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
@@ -126,12 +135,20 @@ __device__ inline float e2m1_magnitude(uint32_t c3) {
 
 // ---------------------------------------------------------------- decoders for the attention kernels
 
+// E4M3 code byte(s) -> fp16 value * 2^-8: the 7 exponent/mantissa bits moved
+// up by 7 land on fp16's exponent/mantissa with an exponent offset of 8
+// (subnormals included), exact.  The sign bit (always 0 for a stored scale)
+// is dropped so even corrupt bytes give finite values.
+__device__ inline uint32_t e4m3_to_h_x2m8(uint32_t b) { return (b & 0x7Fu) << 7; }
+
 // Two E2M1 nibbles (byte `sel` of w: low nibble -> element 0, high -> element
-// 1) as exact fp16 (v_cvt_scalef32_pk_f16_fp4 with a unit scale; that
-// instruction applies only the exponent of its scale operand).
+// 1) as exact fp16 values times 2^8 (v_cvt_scalef32_pk_f16_fp4; that
+// instruction applies only the exponent of its scale operand, so the 2^8 is
+// free and exact).  Paired with scales from e4m3_to_h_x2m8 the product is the
+// exact e2m1 * e4m3.
 template <int SEL>
-__device__ inline half2_t e2m1x2_to_h2(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+__device__ inline half2_t e2m1x2_to_h2_x256(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, SEL);
 }
 
 // Two-nibble INT4 pairs: given w' = w ^ 0x88888888 (offset-8 nibbles), the

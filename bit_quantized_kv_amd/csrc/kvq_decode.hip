@@ -668,7 +668,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
   o = den > 0.0f ? o / den : 0.0f;
   const int64_t oi = ((int64_t)b * p.num_q_heads + h) * D + c;
   if (p.out_bf16)
-    ((uint16_t*)p.out)[oi] = f32_to_bf16_rne(o);
+    ((uint16_t*)p.out)[oi] = (uint16_t)bf16x2_rne((float2_t){o, 0.0f});
   else
     ((float*)p.out)[oi] = o;
   if (p.lse != nullptr && cb == 0 && cl == 0)

@@ -17,6 +17,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 enum { FMT_NVFP4 = 1, FMT_INT4 = 2 };
 
@@ -83,11 +84,10 @@ __device__ inline float max_xor16_xor32(float x) {
 
 // ---------------------------------------------------------------- encoders
 
-// fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
-__device__ inline uint16_t f32_to_bf16_rne(float x) {
-  uint32_t u = as_u32(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two fp32 -> two bf16 (element 0 in the low half), round to nearest even,
+// denormals kept: one v_cvt_pk_bf16_f32.
+__device__ inline uint32_t bf16x2_rne(float2_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Non-negative fp32 -> E4M3 (OCP) code: round to nearest, ties to even,
@@ -113,24 +113,6 @@ __device__ inline uint32_t e4m3_encode(float s) {
 // E4M3 code -> fp32 (exact).  Hardware OCP E4M3 conversion (v_cvt_pk_f32_fp8).
 __device__ inline float e4m3_decode(uint32_t code) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(code, false)[0];
-}
-
-// fp32 ratio r = x / S -> E2M1 code: nearest grid value {0,.5,1,1.5,2,3,4,6},
-// a midpoint going to the code with an even mantissa bit, |r| >= 6 -> 6, the
-// sign bit of r kept.
-__device__ inline uint32_t e2m1_encode(float r) {
-  float a = __builtin_fabsf(r);
-  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
-               (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-  return c | ((as_u32(r) >> 28) & 8u);
-}
-
-// E2M1 magnitude (3-bit code) -> fp32.
-__device__ inline float e2m1_magnitude(uint32_t c3) {
-  // values 0, 0.5, 1, 1.5, 2, 3, 4, 6: exponent field e = c3 >> 1, mantissa m = c3 & 1
-  uint32_t e = c3 >> 1, m = c3 & 1u;
-  float v = e == 0 ? 0.5f * (float)m : (1.0f + 0.5f * (float)m) * (float)(1u << (e - 1));
-  return v;
 }
 
 // ---------------------------------------------------------------- decoders for the attention kernels

@@ -7,12 +7,12 @@
 // same four RTX 5090s" ("What we changed").  Prefix dequantization is the
 // extend path of the same Figure 2 caption, with a bf16 workspace.
 //
-// Both kernels stream: one thread per 16-element block of a (token, head,
-// K|V) row, 16/32-byte vector loads and stores, consecutive threads on
-// consecutive blocks so every wavefront touches contiguous memory.  Every
-// rounding decision is made in IEEE fp32 (correctly rounded division, no FMA
-// contraction), so the packed bytes are bit-exact against a scalar
-// implementation of the same rules.
+// Both kernels stream, one workgroup per run of consecutive tokens of one
+// (K|V, head) pair, with 16/32-byte vector accesses on consecutive lanes.
+// Every rounding decision is an IEEE fp32 operation (correctly rounded
+// quotients, no FMA contraction) or a gfx950 conversion instruction with the
+// same rounding, so the packed bytes and the dequantized bf16 are bit-exact
+// against a scalar implementation of the same rules.
 #pragma clang fp contract(off)
 
 #include "kvq_device.h"
@@ -55,45 +55,85 @@ struct Row16<uint16_t> {  // bf16 bit patterns, widened exactly
   }
 };
 
-// Thread t handles block b = t % (D/16) of row (token i, K|V, head g), rows
-// ordered token-major so a wavefront reads a contiguous span of each token.
+// A workgroup takes kStoreTokens(D) = 256 / (D/16) consecutive input tokens of
+// one (K|V, head) pair, blockIdx.y = kv * num_kv_heads + head; thread (i, b)
+// quantizes block b (16 head-dim elements) of token t0 + i.  No 64-bit
+// division: the token comes from blockIdx.x, the pair from blockIdx.y.
+template <int D>
+__device__ inline int64_t store_token(int tid) {
+  return (int64_t)blockIdx.x * (256 / (D / 16)) + tid / (D / 16);
+}
+
+// True when the FMA-corrected quotient below is the correctly rounded x / S
+// for every x: S = e4m3 * gs has at most 4 significant bits when gs is a
+// power of two (an exhaustive check over every fp32 significand against each
+// of the 8 E4M3 significands finds no difference), and the bounded exponent
+// range keeps the residual exact.
+__device__ inline bool fma_quotient_exact(float gs) {
+  const uint32_t u = as_u32(gs);
+  return (u & 0x807FFFFFu) == 0u && (u >> 23) - 103u <= 48u;  // gs = 2^k, -24 <= k <= 24
+}
+
+// y = RN(x / S) from r = RN(1 / S): q = RN(x r) is within an ulp of x / S,
+// the residual x - q S is exact in an FMA, and one correction step rounds
+// correctly (Markstein's division step).  Written as q - (q S - x) r so that
+// x = -0 keeps its sign.
+__device__ inline float fma_quotient(float x, float S, float r) {
+  const float q = x * r;
+  const float e = __builtin_fmaf(q, S, -x);
+  return __builtin_fmaf(-e, r, q);
+}
+
+// Eight ratios -> one dword of E2M1 codes (element 0 in the low nibble) with
+// the gfx950 conversion v_cvt_scalef32_pk_fp4_f32 at scale 1: round to
+// nearest, ties to the even code, saturation at 6, the sign kept (also for
+// zeros and denormals).  Checked exhaustively against a scalar encoder of
+// that rule over every non-NaN fp32 input.
+__device__ inline uint32_t e2m1_pack8(const float* y) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+}
+
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void nvfp4_store_kernel(StoreParams p) {
   constexpr int NB = D / 16;
-  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)p.num_tokens * 2 * p.num_kv_heads * NB;
-  if (tid >= total) return;
-  const int b = (int)(tid % NB);
-  const int64_t row = tid / NB;
-  const int g = (int)(row % p.num_kv_heads);
-  const int kv = (int)((row / p.num_kv_heads) & 1);
-  const int64_t i = row / (2 * p.num_kv_heads);
-  const int32_t slot = p.slots[i];
-  if (slot < 0) return;
-
+  const int kv = (int)blockIdx.y >= p.num_kv_heads ? 1 : 0;
+  const int g = (int)blockIdx.y - kv * p.num_kv_heads;
+  const int b = threadIdx.x % NB;
+  const int64_t i = store_token<D>(threadIdx.x);
+  if (i >= p.num_tokens) return;
+  // the input row and the slot are loaded together; a skipped token (slot < 0)
+  // is quantized and dropped
   float x[16];
   const TIn* src = (const TIn*)(kv ? p.v : p.k) + i * p.in_stride + (int64_t)g * D + 16 * b;
   Row16<TIn>::load(src, x);
+  const int32_t slot = p.slots[i];
 
   float amax = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 16; e++) {
-    float a = __builtin_fabsf(x[e]);
-    amax = a > amax ? a : amax;
-  }
+  for (int e = 0; e < 16; e++) amax = fmaxf(amax, __builtin_fabsf(x[e]));
   const float gs = p.gs[kv];
   const float den = 6.0f * gs;
   const float s_raw = amax / den;
   const uint32_t cs = e4m3_encode(s_raw);
   const float S = e4m3_decode(cs) * gs;
 
-  uint32_t w0 = 0, w1 = 0;
-  if (S != 0.0f) {
+  float y[16];
+  if (S != 0.0f && s_raw <= 448.0f && fma_quotient_exact(gs)) {
+    const float r = 1.0f / S;
 #pragma unroll
-    for (int e = 0; e < 8; e++) w0 |= e2m1_encode(x[e] / S) << (4 * e);
+    for (int e = 0; e < 16; e++) y[e] = fma_quotient(x[e], S, r);
+  } else {
+    // general global scale, a saturated block scale, or S = 0 (codes 0 below)
 #pragma unroll
-    for (int e = 0; e < 8; e++) w1 |= e2m1_encode(x[8 + e] / S) << (4 * e);
+    for (int e = 0; e < 16; e++) y[e] = x[e] / S;
   }
+  uint32_t w0 = e2m1_pack8(y), w1 = e2m1_pack8(y + 8);
+  if (S == 0.0f) w0 = w1 = 0u;
+  if (slot < 0) return;
+
   const int64_t page = slot / p.page_size;
   const int64_t off = slot % p.page_size;
   uint8_t* half = p.pool + (page * p.num_kv_heads + g) * p.slab + kv * p.half;
@@ -102,48 +142,57 @@ __global__ __launch_bounds__(256) void nvfp4_store_kernel(StoreParams p) {
 }
 
 // INT4: the D/16 threads of one row reduce the row amax with lane shuffles.
+// q = rint(RN(x / s)) with RN(x / s) from the FMA-corrected quotient; where
+// that quotient lies within two ulps of a rounding boundary (a half-integer)
+// the lane recomputes the row with IEEE division, so the codes never depend
+// on the quotient's last bit.
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void int4_store_kernel(StoreParams p) {
   constexpr int NB = D / 16;
-  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)p.num_tokens * 2 * p.num_kv_heads * NB;
-  if (tid >= total) return;  // whole rows only: total is a multiple of NB
-  const int b = (int)(tid % NB);
-  const int64_t row = tid / NB;
-  const int g = (int)(row % p.num_kv_heads);
-  const int kv = (int)((row / p.num_kv_heads) & 1);
-  const int64_t i = row / (2 * p.num_kv_heads);
-  const int32_t slot = p.slots[i];
-  if (slot < 0) return;  // uniform over the row's lanes
-
+  const int kv = (int)blockIdx.y >= p.num_kv_heads ? 1 : 0;
+  const int g = (int)blockIdx.y - kv * p.num_kv_heads;
+  const int b = threadIdx.x % NB;
+  const int64_t i = store_token<D>(threadIdx.x);
+  if (i >= p.num_tokens) return;  // whole rows only: a row's NB lanes share i
   float x[16];
   const TIn* src = (const TIn*)(kv ? p.v : p.k) + i * p.in_stride + (int64_t)g * D + 16 * b;
   Row16<TIn>::load(src, x);
+  const int32_t slot = p.slots[i];
   float amax = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 16; e++) {
-    float a = __builtin_fabsf(x[e]);
-    amax = a > amax ? a : amax;
-  }
+  for (int e = 0; e < 16; e++) amax = fmaxf(amax, __builtin_fabsf(x[e]));
 #pragma unroll
-  for (int m = 1; m < NB; m <<= 1) {
-    float o = __shfl_xor(amax, m, NB);
-    amax = o > amax ? o : amax;
-  }
+  for (int m = 1; m < NB; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, NB));
   const float s = amax / 7.0f;
   uint32_t w0 = 0, w1 = 0;
   if (s != 0.0f) {
+    float n[16];
+    // below 2^-100 the residual could round; such rows take the division
+    bool exact = !(s >= 0x1p-100f);
+    if (!exact) {
+      const float r = 1.0f / s;
+#pragma unroll
+      for (int e = 0; e < 16; e++) {
+        const float y = fma_quotient(x[e], s, r);
+        n[e] = __builtin_rintf(y);
+        exact |= __builtin_fabsf(y - n[e]) >= 0.5f - 0x1p-20f;
+      }
+    }
+    if (exact) {
+#pragma unroll
+      for (int e = 0; e < 16; e++) n[e] = __builtin_rintf(x[e] / s);
+    }
 #pragma unroll
     for (int e = 0; e < 16; e++) {
-      float r = __builtin_rintf(x[e] / s);
-      r = r > 7.0f ? 7.0f : (r < -7.0f ? -7.0f : r);
-      uint32_t nib = (uint32_t)(int)r & 0xFu;
+      const float c = __builtin_amdgcn_fmed3f(n[e], -7.0f, 7.0f);
+      const uint32_t nib = (uint32_t)(int)c & 0xFu;
       if (e < 8)
         w0 |= nib << (4 * e);
       else
         w1 |= nib << (4 * (e - 8));
     }
   }
+  if (slot < 0) return;
   const int64_t page = slot / p.page_size;
   const int64_t off = slot % p.page_size;
   uint8_t* half = p.pool + (page * p.num_kv_heads + g) * p.slab + kv * p.half;
@@ -151,58 +200,113 @@ __global__ __launch_bounds__(256) void int4_store_kernel(StoreParams p) {
   if (b == 0) *(float*)(half + p.scales_off + off * 4) = s;
 }
 
-// Prefix dequantization: thread per 16-element block, writing 32 bytes of
-// bf16.  NVFP4 value fp32(e2m1 * e4m3) is exact; one fp32 multiply by gs; bf16
-// round-to-nearest-even.  INT4 value fp32(q * s).
-template <int D, int FMT>
-__global__ __launch_bounds__(256) void dequant_prefix_kernel(DequantParams p) {
+// Prefix dequantization.  A workgroup expands kDequantTokens = 64 consecutive
+// tokens (four 16-token groups, each inside one page since the page size is a
+// multiple of 16) of one (K|V, head) pair, blockIdx.y = kv * num_kv_heads +
+// head.  Thread (row r, column c) expands code dword c (elements 8c..8c+7)
+// of rows r, r + RPP, ... and writes 16 bytes of bf16 per row, so a row of
+// D elements is one contiguous 2D-byte store across D/8 lanes.
+//   NVFP4: bf16_rne(fp32(fp32(e2m1 * e4m3) * gs)): the E2M1 values come from
+//   v_cvt_scalef32_pk_f32_fp4 (exact), the product with the E4M3 scale is
+//   exact, the gs product rounds once, v_cvt_pk_bf16_f32 rounds to nearest
+//   even.  INT4: bf16_rne(fp32(q * s)).
+constexpr int kDequantTokens = 64;
+
+template <int D, int FMT, bool TAIL>
+__device__ inline void dequant_rows(const DequantParams& p, int kv, int g, int t0) {
+  constexpr int CPR = D / 8;               // code dwords per row
+  constexpr int RPP = 256 / CPR;           // rows per pass: 8 (D 256) or 16 (D 128)
+  constexpr int NI = kDequantTokens / RPP; // rows per thread
   constexpr int NB = D / 16;
-  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)p.prefix_len * 2 * p.num_kv_heads * NB;
-  if (tid >= total) return;
-  const int b = (int)(tid % NB);
-  const int64_t row = tid / NB;
-  const int g = (int)(row % p.num_kv_heads);
-  const int kv = (int)((row / p.num_kv_heads) & 1);
-  const int64_t t = row / (2 * p.num_kv_heads);
-  const int64_t page = p.pages[t / p.page_size];
-  const int64_t off = t % p.page_size;
-  const uint8_t* half = p.pool + (page * p.num_kv_heads + g) * p.slab + kv * p.half;
-  const uint2 w = *(const uint2*)(half + off * (D / 2) + 8 * b);
-  uint32_t outw[8];
-  if (FMT == FMT_NVFP4) {
-    const float sc = e4m3_decode(half[p.scales_off + off * NB + b]);
-    const float gs = p.gs[kv];
+  const int c = threadIdx.x % CPR, r = threadIdx.x / CPR;
+  const uint8_t* pool = p.pool + (int64_t)g * p.slab + kv * p.half;
+  const int64_t page_bytes = (int64_t)p.num_kv_heads * p.slab;
+  uint32_t w[NI];
+  uint32_t sc[NI];  // NVFP4: E4M3 byte; INT4: fp32 scale bits
+  // position of the workgroup's first 16-token group in the page table
+  int pidx = t0 / p.page_size, poff = t0 - pidx * p.page_size;
 #pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      uint32_t word = e < 8 ? w.x : w.y;
-      int sh = 4 * (e & 7);
-      uint32_t c0 = (word >> sh) & 15u, c1 = (word >> (sh + 4)) & 15u;
-      float v0 = e2m1_magnitude(c0 & 7u) * sc, v1 = e2m1_magnitude(c1 & 7u) * sc;
-      v0 = (c0 & 8u) ? -v0 : v0;
-      v1 = (c1 & 8u) ? -v1 : v1;
-      outw[e / 2] = (uint32_t)f32_to_bf16_rne(v0 * gs) | ((uint32_t)f32_to_bf16_rne(v1 * gs) << 16);
+  for (int k = 0; k < NI; k++) {
+    // row r + RPP k lies in 16-token group (RPP k) / 16 (r < RPP)
+    constexpr int kGrpStep = RPP >= 16 ? 1 : 16 / RPP;  // rows k sharing a group
+    if (k > 0 && k % kGrpStep == 0) {
+      poff += 16;
+      if (poff >= p.page_size) {
+        poff -= p.page_size;
+        pidx += 1;
+      }
     }
-  } else {
-    const float s = *(const float*)(half + p.scales_off + off * 4);
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      uint32_t word = e < 8 ? w.x : w.y;
-      int sh = 4 * (e & 7);
-      int q0 = (int)(((word >> sh) & 15u) ^ 8u) - 8, q1 = (int)(((word >> (sh + 4)) & 15u) ^ 8u) - 8;
-      outw[e / 2] = (uint32_t)f32_to_bf16_rne((float)q0 * s) | ((uint32_t)f32_to_bf16_rne((float)q1 * s) << 16);
+    const int rr = r + RPP * k - 16 * (k / kGrpStep);  // row inside the group
+    const uint8_t* half;
+    int off;
+    if (TAIL) {
+      const int t = t0 + r + RPP * k;
+      if (t >= p.prefix_len) continue;
+      half = pool + (int64_t)p.pages[t / p.page_size] * page_bytes;
+      off = t % p.page_size;
+    } else {
+      half = pool + (int64_t)p.pages[pidx] * page_bytes;
+      off = poff + rr;
     }
+    w[k] = ld_global<uint32_t>(half + (uint32_t)(off * (D / 2) + 4 * c));
+    if (FMT == FMT_NVFP4)
+      sc[k] = ld_global<uint8_t>(half + (uint32_t)(p.scales_off + off * NB + (c >> 1)));
+    else
+      sc[k] = ld_global<uint32_t>(half + (uint32_t)(p.scales_off + off * 4));
   }
-  uint16_t* dst = (kv ? p.v_out : p.k_out) + t * p.out_stride + (int64_t)g * D + 16 * b;
-  ((uint4*)dst)[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-  ((uint4*)dst)[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
+  const float gs = FMT == FMT_NVFP4 ? p.gs[kv] : 1.0f;
+  uint16_t* out = (kv ? p.v_out : p.k_out) + (int64_t)g * D + 8 * c;
+#pragma unroll
+  for (int k = 0; k < NI; k++) {
+    const int t = t0 + r + RPP * k;
+    if (TAIL && t >= p.prefix_len) continue;
+    uint32_t o[4];
+    if (FMT == FMT_NVFP4) {
+      const float s = e4m3_decode(sc[k]);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        float2_t v;
+        switch (e) {
+          case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 0); break;
+          case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 1); break;
+          case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 2); break;
+          default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 3); break;
+        }
+        v[0] = (v[0] * s) * gs;
+        v[1] = (v[1] * s) * gs;
+        o[e] = bf16x2_rne(v);
+      }
+    } else {
+      const float s = as_f32(sc[k]);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        float2_t v;
+        // sign-extended nibbles 2e, 2e + 1 (v_bfe_i32)
+        v[0] = (float)((int)(w[k] << (28 - 8 * e)) >> 28) * s;
+        v[1] = (float)((int)(w[k] << (24 - 8 * e)) >> 28) * s;
+        o[e] = bf16x2_rne(v);
+      }
+    }
+    // uniform row base plus a 32-bit lane offset
+    uint16_t* row = out + (int64_t)(t0 + RPP * k) * p.out_stride;
+    *(u32x4_t*)(row + (uint32_t)(r * p.out_stride)) = (u32x4_t){o[0], o[1], o[2], o[3]};
+  }
 }
 
-static inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
+template <int D, int FMT>
+__global__ __launch_bounds__(256) void dequant_prefix_kernel(DequantParams p) {
+  const int kv = (int)blockIdx.y >= p.num_kv_heads ? 1 : 0;
+  const int g = (int)blockIdx.y - kv * p.num_kv_heads;
+  const int t0 = (int)blockIdx.x * kDequantTokens;
+  if (t0 + kDequantTokens <= p.prefix_len)
+    dequant_rows<D, FMT, false>(p, kv, g, t0);
+  else
+    dequant_rows<D, FMT, true>(p, kv, g, t0);
+}
 
 hipError_t launch_quantize_store(const StoreParams& p, int fmt, int head_dim, int in_bf16, hipStream_t stream) {
-  const int64_t threads = (int64_t)p.num_tokens * 2 * p.num_kv_heads * (head_dim / 16);
-  const dim3 grid(grid_for(threads)), block(256);
+  const int tpw = 256 / (head_dim / 16);
+  const dim3 grid((unsigned)((p.num_tokens + tpw - 1) / tpw), (unsigned)(2 * p.num_kv_heads)), block(256);
 #define KVQ_STORE(D, T)                                                            \
   do {                                                                             \
     if (fmt == FMT_NVFP4)                                                          \
@@ -220,8 +324,8 @@ hipError_t launch_quantize_store(const StoreParams& p, int fmt, int head_dim, in
 }
 
 hipError_t launch_dequant_prefix(const DequantParams& p, int fmt, int head_dim, hipStream_t stream) {
-  const int64_t threads = (int64_t)p.prefix_len * 2 * p.num_kv_heads * (head_dim / 16);
-  const dim3 grid(grid_for(threads)), block(256);
+  const dim3 grid((unsigned)((p.prefix_len + kDequantTokens - 1) / kDequantTokens), (unsigned)(2 * p.num_kv_heads));
+  const dim3 block(256);
   if (head_dim == 256) {
     if (fmt == FMT_NVFP4) hipLaunchKernelGGL((dequant_prefix_kernel<256, FMT_NVFP4>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((dequant_prefix_kernel<256, FMT_INT4>), grid, block, 0, stream, p);

@@ -110,3 +110,71 @@ def test_quality_vs_unquantized_is_a_format_property():
             cg = cosine(out[0, h], full[h].numpy())
             co = cosine(ref[0, h], full[h].numpy())
             assert abs(cg - co) <= 1e-5, (fmt, h, cg, co)
+
+
+def _special_rows(fmt, D, rng):
+    """Rows that reach every branch of the quantizers: signed zeros, fp32
+    denormals, exact rounding ties, all-zero blocks, block scales that
+    underflow E4M3 or saturate at 448, and INT4 rows with denormal scales."""
+    rows = []
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for _ in range(6):
+        x = rng.standard_normal(D).astype(np.float32)
+        x[::7] = 0.0
+        x[1::7] = -0.0
+        x[2::11] = np.float32(1e-40) * rng.choice([-1, 1], size=x[2::11].shape)
+        rows.append(x)
+    if fmt == 1:
+        for S in (0.171875, 0.001953125, 1.0, 26.0):
+            x = np.zeros(D, np.float32)
+            for b in range(D // 16):
+                blk = np.concatenate([[6.0], ties, -ties[:4], grid[1:5]])[:16] * S
+                rng.shuffle(blk)
+                x[16 * b:16 * b + 16] = blk
+            rows.append(x.astype(np.float32))
+        x = rng.standard_normal(D).astype(np.float32)
+        x[:16] = 0.0                                # all-zero block
+        x[16:32] *= np.float32(1e-5)                # scale below E4M3's smallest subnormal
+        x[32:48] *= np.float32(1e4)                 # block scale saturated at 448
+        x[48:64] = -x[48:64] * np.float32(1e-38)    # tiny but nonzero
+        rows.append(x)
+    else:
+        x = np.array([(k % 15 - 7) + 0.5 * (k % 2) for k in range(D)], np.float32)
+        x[0] = 7.0                                  # s = 1: exact ties at half-integers
+        rows.append(x)
+        rows.append((rng.standard_normal(D) * 1e-39).astype(np.float32))   # denormal row scale
+        rows.append((rng.standard_normal(D) * 1e-30).astype(np.float32))   # scale near 2^-100
+        rows.append(np.zeros(D, np.float32))
+        y = rng.standard_normal(D).astype(np.float32)
+        y[::5] = -0.0
+        rows.append(y)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("fmt,gs", [(1, (1.0, 1.0)), (1, (0.125, 4.0)), (1, (0.37, 2.5)), (2, (1.0, 1.0))])
+def test_store_special_values(fmt, gs):
+    import oracle
+    from bit_quantized_kv_amd import kvq
+    print(f"case: special values fmt {fmt} gs {gs}", flush=True)
+    D, Hkv, P = 256, 2, 16
+    rng = np.random.default_rng(7 + fmt)
+    rows = _special_rows(fmt, D, rng)
+    n = rows.shape[0] * 2
+    k = np.stack([rows, rows[::-1]], axis=1)        # [n/2][2][D]
+    k = np.concatenate([k, -k])                      # [n][2][D]
+    v = np.ascontiguousarray(k[:, ::-1] * np.float32(0.5))
+    k = np.ascontiguousarray(k)
+    num_pages = -(-n // P) + 1
+    slots = np.arange(n, dtype=np.int32)
+    cache = kvq.Cache(fmt, num_pages, P, Hkv, D, device=torch.device("cuda"), global_scale=gs)
+    cache.pool.fill_(0xFF)
+    kvq.kvq_quantize_store(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                           torch.from_numpy(slots).cuda())
+    ref = oracle.Pool(fmt, num_pages, P, Hkv, D, global_scale=gs, fill=0xFF)
+    ref.quantize_store(k, v, slots)
+    torch.cuda.synchronize()
+    got = cache.pool.cpu().numpy()
+    if not np.array_equal(got, ref.data):
+        diff = np.argwhere(got != ref.data)
+        raise AssertionError(f"{len(diff)} bytes differ, first {diff[:5].tolist()}")

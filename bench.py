@@ -57,6 +57,133 @@ def token_head_bytes(fmt: int) -> int:
     return 2 * (D // 2 + (D // 16 if fmt == 1 else 4))
 
 
+# ------------------------------------------------------------------ profiler summaries
+# The decode call's HBM traffic comes from two rocprofv3 counter passes over a
+# short run of the headline workload (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch), each scaled by what the same counter reads for a plain 1 GiB
+# device copy in the same run.  The summary records a digest of the decode
+# kernel's sources; once they change, the recorded traffic no longer applies
+# and the bench reports null.
+REPO = os.path.dirname(os.path.abspath(__file__))
+DECODE_SOURCES = ["bit_quantized_kv_amd/csrc/kvq_decode.hip", "bit_quantized_kv_amd/csrc/kvq_device.h",
+                  "bit_quantized_kv_amd/csrc/kvq_launch.h"]
+PMC_RUN = ('cd /tmp && export TMPDIR=/tmp && cd "$GRAFT_REPO_ROOT" && timeout -s KILL 150 rocprofv3 --pmc {counter} '
+           '--output-format csv -d gpurun_out/pmc_{tag} -o run -- python -u bench.py --workload {workload} '
+           '--secondary "" --no-cpu-baseline --steps 5 --warmup 1 --layers 2 --copy-calibration-gib 1')
+CALIB_BYTES = 1 << 30
+
+
+def decode_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(REPO, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_path(workload: str) -> str:
+    fmt = "nvfp4" if WORKLOADS[workload]["fmt"] == 1 else "int4"
+    return os.path.join(REPO, "profiles", f"decode_{fmt}_{workload}_counters.md")
+
+
+def load_counter_summary(workload: str):
+    """The recorded traffic of the decode call, if its kernel sources are unchanged."""
+    path = counters_path(workload)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    text = open(path).read()
+    start = text.find("```json")
+    if start < 0:
+        return None, "counter summary without a json block"
+    rec = json.loads(text[start + 7:text.index("```", start + 7)])
+    if rec.get("decode_source_digest") != decode_source_digest():
+        return None, "decode kernel changed since the counters were taken"
+    return rec, os.path.relpath(path, REPO)
+
+
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    with open(files[0], newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> str:
+    """Markdown summary of the FETCH_SIZE / WRITE_SIZE passes (see PMC_RUN)."""
+    per = {}
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _csv_rows(directory, "counter_collection.csv") if r["Counter_Name"] == counter]
+        def avg(pred):
+            v = [float(r["Counter_Value"]) for r in rows if pred(r)]
+            return (sum(v) / len(v), len(v)) if v else (None, 0)
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        big = max(int(r["Grid_Size"]) for r in copies)
+        per[counter] = {
+            "decode_kernel": avg(lambda r: "decode_kernel" in r["Kernel_Name"]),
+            "merge_kernel": avg(lambda r: "merge_kernel" in r["Kernel_Name"]),
+            "copy_1gib": avg(lambda r: "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) == big),
+        }
+    f_fac = CALIB_BYTES / 1024 / per["FETCH_SIZE"]["copy_1gib"][0]
+    w_fac = CALIB_BYTES / 1024 / per["WRITE_SIZE"]["copy_1gib"][0]
+    fetch_kib = per["FETCH_SIZE"]["decode_kernel"][0] + per["FETCH_SIZE"]["merge_kernel"][0]
+    write_kib = per["WRITE_SIZE"]["decode_kernel"][0] + per["WRITE_SIZE"]["merge_kernel"][0]
+    traffic = 1024 * (f_fac * fetch_kib + w_fac * write_kib)
+    w = WORKLOADS[workload]
+    algo = w["batch"] * w["ctx"] * HKV * token_head_bytes(w["fmt"])
+    rec = {"workload": workload, "decode_source_digest": decode_source_digest(),
+           "fetch_factor": f_fac, "write_factor": w_fac,
+           "fetch_kib_per_call": fetch_kib, "write_kib_per_call": write_kib,
+           "traffic_bytes_per_call": traffic, "algorithmic_bytes_per_call": algo}
+    lines = [f"# HBM traffic of the decode call: {workload}", "",
+             "Two counter passes (run from the repository root on one MI355X):", "", "```",
+             PMC_RUN.format(counter="FETCH_SIZE", tag="fetch", workload=workload),
+             PMC_RUN.format(counter="WRITE_SIZE", tag="write", workload=workload),
+             f"python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write --workload {workload}",
+             "```", "",
+             "Per-dispatch averages (KiB as the counters report them):", "",
+             "| kernel | FETCH_SIZE | dispatches | WRITE_SIZE | dispatches |", "|---|---|---|---|---|"]
+    for k in ("decode_kernel", "merge_kernel", "copy_1gib"):
+        fv, fn = per["FETCH_SIZE"][k]
+        wv, wn = per["WRITE_SIZE"][k]
+        lines.append(f"| {k} | {fv:,.1f} | {fn} | {wv:,.1f} | {wn} |")
+    lines += ["",
+              f"Calibration: a 1 GiB device copy (1,048,576 KiB read and written) reads "
+              f"{per['FETCH_SIZE']['copy_1gib'][0]:,.1f} KiB of FETCH_SIZE and "
+              f"{per['WRITE_SIZE']['copy_1gib'][0]:,.1f} KiB of WRITE_SIZE, so the factors are "
+              f"{f_fac:.4f} (fetch) and {w_fac:.4f} (write).", "",
+              f"Traffic per decode call (decode + merge kernels): {traffic:,.0f} B = "
+              f"{traffic / algo:.4f} x the algorithmic {algo:,} B of packed KV.", "",
+              "```json", json.dumps(rec, indent=1), "```", ""]
+    return "\n".join(lines)
+
+
+def summarize_trace(trace_dir: str, bench_json: str | None) -> str:
+    """Markdown table of kernel durations (rocprofv3 --kernel-trace, csv output) per
+    kernel and launch grid, plus the bench's own live figures for comparison."""
+    rows = _csv_rows(trace_dir, "kernel_trace.csv")
+    groups = {}
+    for r in rows:
+        grid = tuple(int(r.get(f"Grid_Size_{a}", 0) or 0) for a in "XYZ")
+        key = (r["Kernel_Name"], grid)
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["| kernel | grid (x, y, z) | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        if sum(v) < 100.0:  # hide torch's small setup kernels
+            continue
+        lines.append(f"| `{name[:90]}` | {grid} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    if bench_json:
+        with open(bench_json) as f:
+            line = json.loads([l for l in f if l.startswith("{")][-1])
+        rf = line["roofline"]
+        lines += ["", f"The same run's JSON line: decode call {rf['avg_launch_us']:.2f} us live (HIP events on the "
+                  f"launch stream), {rf['achieved']:.0f} GB/s = {100 * rf['frac']:.1f} % of {rf['peak']:.0f} GB/s."]
+    return "\n".join(lines) + "\n"
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,6 +199,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the CPU-oracle sample")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (profiler counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the counter summary of two rocprofv3 --pmc runs (no GPU use)")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print a kernel-duration table of a rocprofv3 --kernel-trace csv run (no GPU use)")
+    ap.add_argument("--bench-json", help="with --summarize-trace: the JSON line printed by the traced run")
     return ap.parse_args()
 
 
@@ -296,6 +428,12 @@ def cpu_baseline(torch, lay, w, target_s):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        sys.stdout.write(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload))
+        return
+    if args.summarize_trace:
+        sys.stdout.write(summarize_trace(args.summarize_trace, args.bench_json))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the split-context path is "
               f"single-GPU by design", file=sys.stderr)
@@ -332,6 +470,7 @@ def main():
         print(f"[bench] cpu oracle: {cpu['value']:.4f} GB/s on {cpu['cores']} threads", file=sys.stderr, flush=True)
     w = WORKLOADS[args.workload]
     r = main_res
+    counters, counters_note = load_counter_summary(args.workload)
     line = {
         "metric": METRIC,
         "value": r["effective_kv_gbs"],
@@ -352,7 +491,9 @@ def main():
         "tokens_per_s": r["tokens_per_s"],
         "pct_hbm_roofline_step": 100.0 * r["effective_kv_gbs"] / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": r["decode_call_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": r["decode_call_frac_hbm"], "traffic": None,
+                     "frac": r["decode_call_frac_hbm"],
+                     "traffic": counters["traffic_bytes_per_call"] if counters else None,
+                     "traffic_source": counters_note,
                      "kernel": "kvq_decode_attention call (decode_kernel + merge_kernel)",
                      "algorithmic_bytes_per_launch": r["kv_bytes_per_layer"],
                      "avg_launch_us": r["decode_call_us"]},

@@ -612,13 +612,63 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 
 // Merge the splits of one (sequence, query head): M = max m_s,
 // o = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s, lse = (M + log2 sum) ln 2.
-// One workgroup per (sequence, query head, 64-channel block).  Its 256 threads
+//
+// Up to kMergePre splits: one wavefront per (sequence, query head, 64-channel
+// block), lane = channel.  The partial o of every split are loaded together
+// with the (m, l) pairs, so the merge costs one memory round trip; lane s
+// holds the weight of split s (0 for an empty split, whose partial o is
+// zero) and v_readlane broadcasts it.  Sums run over s = 0, 1, ... and over a
+// fixed butterfly: the result is reproducible for a given split plan.
+constexpr int kMergePre = 16;
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
+  constexpr int NCB = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= (int64_t)p.batch * p.num_q_heads * NCB) return;  // whole wavefronts
+  const int cb = (int)(unit % NCB);
+  const int64_t bh = unit / NCB;
+  const int h = (int)(bh % p.num_q_heads), b = (int)(bh / p.num_q_heads);
+  const int G = p.group, g = h / G, n = h - g * G, S = p.num_splits;  // S <= kMergePre
+  const int64_t part0 = ((int64_t)b * p.num_kv_heads + g) * S;
+  const float* mlp = p.part_ml + (part0 * G + n) * 2;                // split s at mlp[s * 2G]
+  const float* op = p.part_o + (part0 * G + n) * D + cb * 64 + lane;  // split s at op[s * G * D]
+  const int64_t os = (int64_t)G * D, ms = 2 * G;
+
+  float ov[kMergePre];
+#pragma unroll
+  for (int i = 0; i < kMergePre; i++) ov[i] = i < S ? op[i * os] : 0.0f;
+  const float m0 = lane < S ? mlp[lane * ms] : -__builtin_inff();
+  const float l0 = lane < S ? mlp[lane * ms + 1] : 0.0f;
+  float M = m0;
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, 64));
+  const float w = m0 == -__builtin_inff() ? 0.0f : exp2f(m0 - M);
+  float den = w * l0, o = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMergePre; i++)
+    if (i < S) o += as_f32(__builtin_amdgcn_readlane(as_u32(w), i)) * ov[i];
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) den += __shfl_xor(den, k, 64);
+  o = den > 0.0f ? o / den : 0.0f;
+  const int64_t oi = ((int64_t)b * p.num_q_heads + h) * D + cb * 64 + lane;
+  if (p.out_bf16)
+    ((uint16_t*)p.out)[oi] = (uint16_t)bf16x2_rne((float2_t){o, 0.0f});
+  else
+    ((float*)p.out)[oi] = o;
+  if (p.lse != nullptr && cb == 0 && lane == 0)
+    p.lse[(int64_t)b * p.num_q_heads + h] = den > 0.0f ? (M + log2f(den)) * kLn2 : -__builtin_inff();
+}
+
+// Merge for more than kMergePre splits: one workgroup per (sequence, query
+// head, 64-channel block).  Its 256 threads
 // scan the (m, l) pairs together and stage the split weights 2^(m_s - M) in
 // LDS (0 for an empty split, whose partial o is zero); then 4 groups of 64
 // threads accumulate interleaved splits for their channel, branch-free, and
 // are summed in LDS.  Every sum runs in a fixed order: reproducible.
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(256) void merge_wide_kernel(const DecodeParams p) {
   constexpr int CW = 64, SG = 4, NCB = D / CW, WTILE = 4096;
   const int cb = blockIdx.x % NCB, h = blockIdx.x / NCB, b = blockIdx.y;
   const int tid = threadIdx.x, sg = tid / CW, cl = tid % CW, c = cb * CW + cl;
@@ -678,7 +728,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
 hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream_t stream) {
   const dim3 grid(p.num_splits, p.num_kv_heads, p.batch), block(64 * kWaves);
   const size_t lds = (size_t)p.group * (head_dim + 2 * kWaves) * sizeof(float);
-  const dim3 mgrid(p.num_q_heads * (head_dim / 64), p.batch);
+  const int64_t munits = (int64_t)p.batch * p.num_q_heads * (head_dim / 64);
+  const bool narrow = p.num_splits <= kMergePre;
+  const dim3 mgrid = narrow ? dim3((unsigned)((munits + 3) / 4)) : dim3(p.num_q_heads * (head_dim / 64), p.batch);
   const bool dup = p.group <= 8;
 #define KVQ_DECODE(D, F)                                                                        \
   do {                                                                                          \
@@ -688,11 +740,13 @@ hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream
   if (head_dim == 256) {
     if (fmt == FMT_NVFP4) KVQ_DECODE(256, FMT_NVFP4);
     else KVQ_DECODE(256, FMT_INT4);
-    hipLaunchKernelGGL((merge_kernel<256>), mgrid, dim3(256), 0, stream, p);
+    if (narrow) hipLaunchKernelGGL((merge_kernel<256>), mgrid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((merge_wide_kernel<256>), mgrid, dim3(256), 0, stream, p);
   } else {
     if (fmt == FMT_NVFP4) KVQ_DECODE(128, FMT_NVFP4);
     else KVQ_DECODE(128, FMT_INT4);
-    hipLaunchKernelGGL((merge_kernel<128>), mgrid, dim3(256), 0, stream, p);
+    if (narrow) hipLaunchKernelGGL((merge_kernel<128>), mgrid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((merge_wide_kernel<128>), mgrid, dim3(256), 0, stream, p);
   }
 #undef KVQ_DECODE
   return hipGetLastError();

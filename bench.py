@@ -43,6 +43,7 @@ WORKLOADS = {
                     desc="NVFP4, batch 4, context 160,000, shuffled page tables, plus a 64-token "
                          "chunked-prefill quantize-store per sequence"),
     "ctx1m": dict(fmt=1, batch=1, ctx=1048576, page=16, shuffled=False, kind="lognormal", prefix=True,
+                  split_sweep=(32, 64, 128, 256, 512),
                   desc="NVFP4, batch 1, context 1,048,576, split-context decode; plus kvq_dequant_prefix of "
                        "the full prefix into a bf16 workspace of 1,048,576 + 4,096 rows"),
     "int4_220k": dict(fmt=2, batch=8, ctx=220000, page=1600, shuffled=False, kind="student_t",
@@ -372,6 +373,26 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
         torch.cuda.synchronize()
         res["chunk_store_us"] = a.elapsed_time(b_) / steps * 1e3
         res["chunk_store_tokens"] = int(slots.numel())
+    if w.get("split_sweep"):
+        # decode call time against the split count (fixed plan per entry), layers rotated
+        sweep = {}
+        for ns in w["split_sweep"]:
+            wsz = torch.empty(kvq.kvq_decode_workspace_size(layers[0].cache, B, HQ, L, ns), dtype=torch.uint8,
+                              device="cuda")
+            times = []
+            for i in range(steps + 2):
+                lay = layers[i % n_layers]
+                a, b_ = ev(), ev()
+                a.record(stream)
+                kvq.kvq_decode_attention(lay.cache, lay.q, lay.bt, lay.lens, L, out=lay.out, workspace=wsz,
+                                         num_splits=ns)
+                b_.record(stream)
+                times.append((a, b_))
+            torch.cuda.synchronize()
+            us = sum(a.elapsed_time(b) for a, b in times[2:]) / steps * 1e3
+            sweep[str(ns)] = {"decode_call_us": us, "gbs": kv_bytes_layer / (us * 1e-6) / 1e9}
+            del wsz
+        res["split_sweep"] = sweep
     if w.get("prefix"):
         rows = L + 4096
         k_ws = torch.empty((rows, HKV * D), dtype=torch.bfloat16, device="cuda")
@@ -398,6 +419,28 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
     return res, keep
 
 
+def read_ceiling(torch, kvq, steps):
+    """Practical HBM read ceiling: the library's plain streaming-read kernel over
+    4 GiB (16x the Infinity Cache), timed like the decode call."""
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        kvq.kvq_stream_read(buf, sink)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        kvq.kvq_stream_read(buf, sink)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1e3
+    del buf
+    return {"gbs": nbytes / (us * 1e-6) / 1e9, "us": us, "bytes": nbytes,
+            "kernel": "kvq_stream_read: grid-stride 16-byte loads, 2048 workgroups"}
+
+
 def cpu_baseline(torch, lay, w, target_s):
     """The CPU oracle on a sample of the same cache: whole sequences of layer 0
     (their packed pages copied to the host), all 24 query heads."""
@@ -420,10 +463,19 @@ def cpu_baseline(torch, lay, w, target_s):
     n = int(max(1, min(w["batch"], round(target_s / max(t1, 1e-3)))))
     t = run(n) if n > 1 else t1
     nbytes = n * L * HKV * token_head_bytes(w["fmt"])
-    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+    threads = oracle.num_threads()
+    # the same oracle on one thread, one sequence
+    oracle.set_num_threads(1)
+    try:
+        t_one = run(1)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"1 layer, {n} of {w['batch']} sequences x {L} tokens, all {HQ} query heads, fp64 attention "
                       f"over the same packed pages ({t:.1f} s)",
-            "seconds": t, "tokens_per_s_16_layers_extrapolated": n / (t * LAYERS)}
+            "seconds": t, "tokens_per_s_16_layers_extrapolated": n / (t * LAYERS),
+            "one_thread": {"value": L * HKV * token_head_bytes(w["fmt"]) / t_one / 1e9, "unit": "GB/s",
+                           "sample": f"1 sequence, 1 thread ({t_one:.1f} s)"}}
 
 
 def main():
@@ -456,6 +508,8 @@ def main():
         secondary[name] = r
         print(f"[bench] {name}: step {r['step_ms']:.3f} ms, decode call {r['decode_call_us']:.1f} us "
               f"({r['decode_call_gbs']:.0f} GB/s), {time.time() - t1:.1f} s", file=sys.stderr, flush=True)
+    ceiling = read_ceiling(torch, kvq, args.steps)
+    print(f"[bench] plain streaming read: {ceiling['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     if args.copy_calibration_gib > 0:
         n = int(args.copy_calibration_gib * (1 << 30))
         src = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -496,7 +550,9 @@ def main():
                      "traffic_source": counters_note,
                      "kernel": "kvq_decode_attention call (decode_kernel + merge_kernel)",
                      "algorithmic_bytes_per_launch": r["kv_bytes_per_layer"],
-                     "avg_launch_us": r["decode_call_us"]},
+                     "avg_launch_us": r["decode_call_us"],
+                     "frac_of_measured_read_ceiling": r["decode_call_gbs"] / ceiling["gbs"]},
+        "hbm_read_ceiling": ceiling,
         "cpu_baseline": cpu,
         "store_call_us": r["store_call_us"],
         "populate": r["populate"],

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/kvq.h"
 #include "kvq_device.h"
 #include "kvq_launch.h"
@@ -12,8 +14,10 @@ namespace {
 
 thread_local int32_t g_last_hip_error = 0;
 
-constexpr int kTargetWaves = 2048;  // wavefronts per decode launch: 8 per CU on 256 CUs
+constexpr int kDefaultCUs = 256;   // MI355X
+constexpr int kMaxDevices = 64;
 constexpr int kMinChunksPerWave = 4;  // 128 tokens per wavefront at least
+constexpr int kStreamWorkgroups = 2048;  // 8 per CU: the best plain streaming read measured on MI355X
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -34,11 +38,36 @@ kvq_status hip_status(hipError_t e) {
   return KVQ_ERR_HIP;
 }
 
-int32_t auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
+// Compute units of the current device (queried once per device; 256, an
+// MI355X, when no device is visible, e.g. for a host-only planning call).
+int device_cus() {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = kDefaultCUs;
+  }
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Splits per (sequence, KV head): the grid of batch x num_kv_heads x splits
+// four-wavefront workgroups is sized to one workgroup per CU for NVFP4 and
+// two for INT4 (whose heavier dequantization gains from a second wavefront
+// per SIMD); measured best on MI355X at the 32K, 160K, 1M and INT4 220K
+// shapes.  Each wavefront keeps at least kMinChunksPerWave chunks.
+int32_t auto_splits(int32_t fmt, int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
   const int64_t chunks = ((int64_t)max_seq_len + 31) / 32;
   if (chunks <= 0) return 1;
-  const int64_t units = (int64_t)batch * num_kv_heads * kvq::kDecodeWaves;
-  int64_t s = (kTargetWaves + units - 1) / units;
+  const int64_t units = (int64_t)batch * num_kv_heads;
+  const int64_t target = (int64_t)device_cus() * (fmt == KVQ_FMT_INT4_TOKHEAD ? 2 : 1);
+  int64_t s = (target + units / 2) / units;
   const int64_t per_split = (int64_t)kMinChunksPerWave * kvq::kDecodeWaves;
   const int64_t cap = (chunks + per_split - 1) / per_split;
   if (s > cap) s = cap;
@@ -106,7 +135,7 @@ kvq_status kvq_decode_num_splits(const kvq_cache* cache, int32_t batch, int32_t 
   if (num_splits == nullptr) return KVQ_ERR_NULL;
   kvq_status st = decode_shape(cache, batch, num_q_heads, max_seq_len);
   if (st != KVQ_OK) return st;
-  *num_splits = auto_splits(batch, cache->num_kv_heads, max_seq_len);
+  *num_splits = auto_splits(cache->fmt, batch, cache->num_kv_heads, max_seq_len);
   return KVQ_OK;
 }
 
@@ -115,7 +144,7 @@ kvq_status kvq_decode_workspace_size(const kvq_cache* cache, int32_t batch, int3
   if (bytes == nullptr) return KVQ_ERR_NULL;
   kvq_status st = decode_shape(cache, batch, num_q_heads, max_seq_len);
   if (st != KVQ_OK) return st;
-  const int32_t s = num_splits > 0 ? num_splits : auto_splits(batch, cache->num_kv_heads, max_seq_len);
+  const int32_t s = num_splits > 0 ? num_splits : auto_splits(cache->fmt, batch, cache->num_kv_heads, max_seq_len);
   *bytes = workspace_bytes(cache, batch, num_q_heads, s);
   return KVQ_OK;
 }
@@ -133,7 +162,7 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
   if (max_pages <= 0 || (int64_t)max_pages * cache->page_size < max_seq_len) return KVQ_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) || (lse_out && ((uintptr_t)lse_out & 3u)))
     return KVQ_ERR_ALIGN;
-  const int32_t splits = num_splits > 0 ? num_splits : auto_splits(batch, cache->num_kv_heads, max_seq_len);
+  const int32_t splits = num_splits > 0 ? num_splits : auto_splits(cache->fmt, batch, cache->num_kv_heads, max_seq_len);
   if (splits > 65535) return KVQ_ERR_UNSUPPORTED;
   if (workspace_bytes_ < workspace_bytes(cache, batch, num_q_heads, splits)) return KVQ_ERR_WORKSPACE;
   if (batch > 65535) return KVQ_ERR_UNSUPPORTED;
@@ -193,6 +222,15 @@ kvq_status kvq_dequant_prefix(const kvq_cache* cache, const int32_t* block_table
   p.page_size = cache->page_size;
   p.num_kv_heads = cache->num_kv_heads;
   return hip_status(kvq::launch_dequant_prefix(p, cache->fmt, cache->head_dim, (hipStream_t)stream));
+}
+
+kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t num_workgroups, void* stream) {
+  if (bytes == 0) return KVQ_OK;
+  if (buf == nullptr || sink == nullptr) return KVQ_ERR_NULL;
+  if (!aligned16(buf) || bytes % 16 != 0 || ((uintptr_t)sink & 3u)) return KVQ_ERR_ALIGN;
+  if (num_workgroups > 65535 * 64) return KVQ_ERR_UNSUPPORTED;
+  const int wgs = num_workgroups > 0 ? num_workgroups : kStreamWorkgroups;
+  return hip_status(kvq::launch_stream_read(buf, (int64_t)bytes, sink, wgs, (hipStream_t)stream));
 }
 
 const char* kvq_status_string(int32_t status) {

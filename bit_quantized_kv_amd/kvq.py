@@ -56,6 +56,7 @@ def lib():
         "kvq_decode_workspace_size": (i32, [C, i32, i32, i32, i32, ctypes.POINTER(sz)]),
         "kvq_decode_attention": (i32, [C, P, i32, P, i32, P, i32, i32, f32, i32, P, i32, P, P, sz, P]),
         "kvq_dequant_prefix": (i32, [C, P, i32, P, P, i64, P]),
+        "kvq_stream_read": (i32, [P, sz, P, i32, P]),
         "kvq_status_string": (ctypes.c_char_p, [i32]),
         "kvq_last_hip_error": (i32, []),
     }
@@ -174,3 +175,11 @@ def kvq_dequant_prefix(cache: Cache, block_table_row: torch.Tensor, prefix_len: 
     _check("kvq_dequant_prefix", lib().kvq_dequant_prefix(ctypes.byref(d), _ptr(block_table_row), int(prefix_len),
                                                           _ptr(k_out), _ptr(v_out), k_out.stride(0),
                                                           _stream(stream)))
+
+
+def kvq_stream_read(buf: torch.Tensor, sink: torch.Tensor, num_workgroups: int = 0, stream=None):
+    """Plain streaming read of a contiguous device tensor (bandwidth reference)."""
+    assert buf.is_contiguous() and sink.dtype in (torch.int32, torch.uint32) and sink.numel() >= 1
+    nbytes = buf.numel() * buf.element_size() // 16 * 16
+    _check("kvq_stream_read", lib().kvq_stream_read(_ptr(buf), nbytes, _ptr(sink), int(num_workgroups),
+                                                    _stream(stream)))

@@ -112,7 +112,9 @@ kvq_status kvq_quantize_store(const kvq_cache* cache, const void* k, const void*
 
 /* The split count kvq_decode_attention uses when num_splits <= 0: each
  * (sequence, KV head) is cut into that many token ranges of whole 32-token
- * chunks, sized from (batch, num_kv_heads, max_seq_len) to fill the GPU. */
+ * chunks, sized from (format, batch, num_kv_heads, max_seq_len) and the
+ * current device's compute-unit count (256 when no device is visible) so the
+ * grid holds about one workgroup per CU (NVFP4) or two (INT4). */
 kvq_status kvq_decode_num_splits(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
                                  int32_t max_seq_len, int32_t* num_splits);
 
@@ -163,6 +165,14 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
  * prefix_len == 0 is a no-op. */
 kvq_status kvq_dequant_prefix(const kvq_cache* cache, const int32_t* block_table_row, int32_t prefix_len,
                               void* k_out, void* v_out, int64_t out_token_stride, void* stream);
+
+/* Measurement aid, not part of the cache path: a plain streaming read of
+ * `bytes` bytes of device memory (the practical HBM read ceiling against which
+ * the decode kernel's bandwidth is judged).  Nothing is computed from the data
+ * beyond an XOR that decides whether sink[0] is written (it practically never
+ * is).  buf 16-byte aligned, bytes a multiple of 16; num_workgroups <= 0 picks
+ * 2048 (8 per CU).  Asynchronous on `stream`. */
+kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t num_workgroups, void* stream);
 
 /* Static description of a status code. */
 const char* kvq_status_string(int32_t status);

@@ -67,6 +67,7 @@ def _load():
         "kvqo_decode_attention": (None, [i32, P, i32, i32, i32, P, P, i32, P, i32, P, i32, f64, i64, P, P]),
         "kvqo_dequant_prefix": (None, [i32, P, i32, i32, i32, P, P, i64, P, P, i64]),
         "kvqo_num_threads": (i32, []),
+        "kvqo_set_num_threads": (None, [i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -221,3 +222,8 @@ class Pool:
 
 def num_threads() -> int:
     return int(_load().kvqo_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP loops (for timing; results do not depend on it)."""
+    _load().kvqo_set_num_threads(int(n))

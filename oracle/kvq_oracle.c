@@ -431,3 +431,12 @@ int kvqo_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Set that number (timing only; results do not depend on it). */
+void kvqo_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

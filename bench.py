@@ -172,10 +172,15 @@ def summarize_trace(trace_dir: str, bench_json: str | None) -> str:
         key = (r["Kernel_Name"], grid)
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = ["| kernel | grid (x, y, z) | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
-    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        if sum(v) < 100.0:  # hide torch's small setup kernels
+    other = 0.0
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        if "kvq::" not in name:  # torch's input generation and copies
+            other += sum(v)
             continue
-        lines.append(f"| `{name[:90]}` | {grid} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        short = name.replace("(kvq::DecodeParams)", "").replace("(kvq::StoreParams)", "")
+        short = short.replace("(kvq::DequantParams)", "").replace("void kvq::", "")
+        lines.append(f"| `{short}` | {grid} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    lines.append(f"\nOther kernels (torch input generation, copies): {other / 1e3:.1f} ms in total.")
     if bench_json:
         with open(bench_json) as f:
             line = json.loads([l for l in f if l.startswith("{")][-1])

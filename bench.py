@@ -259,8 +259,9 @@ def populate(torch, kvq, inputs, w, layer_obj, layer, workload_id, chunk_tokens=
         vscale = torch.exp(torch.randn((HKV, D), generator=g, device=dev))
     g.manual_seed(inputs.seed_int(workload_id, layer, inputs.STREAM_K))
     tok = torch.arange(L, device=dev, dtype=torch.int64)
-    total_s, nbytes_in = 0.0, 0
+    total_s, nbytes_in, cal_s = 0.0, 0, 0.0
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    running = torch.zeros(2, dtype=torch.float32, device=dev)
     for b in range(B):
         for t0 in range(0, L, chunk_tokens):
             t1 = min(L, t0 + chunk_tokens)
@@ -273,6 +274,14 @@ def populate(torch, kvq, inputs, w, layer_obj, layer, workload_id, chunk_tokens=
                 v = student_t4(torch, g, (n, HKV, D)).to(torch.bfloat16)
             t = tok[t0:t1]
             slots = (layer_obj.bt[b, t // P].to(torch.int64) * P + t % P).to(torch.int32)
+            if w["fmt"] == 1 and layer == 0:
+                # global-scale calibration pass over the same rows (timed; the
+                # cache keeps gs = 1, the configuration the pages measured)
+                e0.record()
+                kvq.kvq_calibrate_amax(layer_obj.cache, k, v, running)
+                e1.record()
+                e1.synchronize()
+                cal_s += e0.elapsed_time(e1) / 1e3
             e0.record()
             kvq.kvq_quantize_store(layer_obj.cache, k, v, slots)
             e1.record()
@@ -280,6 +289,9 @@ def populate(torch, kvq, inputs, w, layer_obj, layer, workload_id, chunk_tokens=
             total_s += e0.elapsed_time(e1) / 1e3
             nbytes_in += 2 * k.numel() * 2
     nbytes_out = B * L * HKV * token_head_bytes(w["fmt"])
+    if cal_s > 0:
+        populate.calibration = {"seconds": cal_s, "read_bytes": nbytes_in, "gbs": nbytes_in / cal_s / 1e9,
+                                "amax": running.cpu().tolist(), "layer": 0}
     return total_s, nbytes_in, nbytes_out
 
 
@@ -365,6 +377,9 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
         "populate": {"seconds": pop_s, "read_bytes": pop_in, "write_bytes": pop_out,
                      "gbs": (pop_in + pop_out) / pop_s / 1e9 if pop_s > 0 else None},
     }
+    if fmt == 1 and getattr(populate, "calibration", None):
+        res["calibrate_amax"] = populate.calibration
+        populate.calibration = None
     res["decode_call_frac_hbm"] = res["decode_call_gbs"] / HBM_PEAK_GBS
     if chunk is not None:
         kc, vc, slots = chunk

@@ -224,6 +224,39 @@ kvq_status kvq_dequant_prefix(const kvq_cache* cache, const int32_t* block_table
   return hip_status(kvq::launch_dequant_prefix(p, cache->fmt, cache->head_dim, (hipStream_t)stream));
 }
 
+kvq_status kvq_calibrate_amax(const kvq_cache* cache, const void* k, const void* v, int32_t in_dtype,
+                              int64_t in_token_stride, int32_t num_tokens, float* running_amax, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (cache->fmt != KVQ_FMT_NVFP4) return KVQ_ERR_UNSUPPORTED;
+  if (num_tokens < 0) return KVQ_ERR_SHAPE;
+  if (in_dtype != KVQ_DT_F32 && in_dtype != KVQ_DT_BF16) return KVQ_ERR_UNSUPPORTED;
+  if (running_amax == nullptr) return KVQ_ERR_NULL;
+  if (num_tokens == 0) return KVQ_OK;
+  if (k == nullptr || v == nullptr) return KVQ_ERR_NULL;
+  if (in_token_stride < (int64_t)cache->num_kv_heads * cache->head_dim) return KVQ_ERR_SHAPE;
+  const int64_t esize = in_dtype == KVQ_DT_F32 ? 4 : 2;
+  if (!aligned16(k) || !aligned16(v) || (in_token_stride * esize) % 16 != 0 || ((uintptr_t)running_amax & 3u))
+    return KVQ_ERR_ALIGN;
+  kvq::StoreParams p{};
+  p.k = k;
+  p.v = v;
+  p.in_stride = in_token_stride;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = cache->num_kv_heads;
+  return hip_status(kvq::launch_calibrate_amax(p, cache->head_dim, in_dtype == KVQ_DT_BF16, running_amax,
+                                               (hipStream_t)stream));
+}
+
+kvq_status kvq_calibrate_global_scale(const kvq_cache* cache, const float* running_amax, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (cache->fmt != KVQ_FMT_NVFP4) return KVQ_ERR_UNSUPPORTED;
+  if (running_amax == nullptr) return KVQ_ERR_NULL;
+  if (((uintptr_t)running_amax & 3u) || ((uintptr_t)cache->global_scale & 3u)) return KVQ_ERR_ALIGN;
+  return hip_status(kvq::launch_global_scale(running_amax, (float*)cache->global_scale, (hipStream_t)stream));
+}
+
 kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t num_workgroups, void* stream) {
   if (bytes == 0) return KVQ_OK;
   if (buf == nullptr || sink == nullptr) return KVQ_ERR_NULL;

@@ -51,6 +51,8 @@ struct DecodeParams {
 
 hipError_t launch_quantize_store(const StoreParams& p, int fmt, int head_dim, int in_bf16, hipStream_t stream);
 hipError_t launch_dequant_prefix(const DequantParams& p, int fmt, int head_dim, hipStream_t stream);
+hipError_t launch_calibrate_amax(const StoreParams& p, int head_dim, int in_bf16, float* running, hipStream_t stream);
+hipError_t launch_global_scale(const float* running, float* gs, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
 

@@ -200,6 +200,61 @@ __global__ __launch_bounds__(256) void int4_store_kernel(StoreParams p) {
   if (b == 0) *(float*)(half + p.scales_off + off * 4) = s;
 }
 
+// Global-scale calibration: the running absolute maximum of a layer's K and
+// V over prefill rows.  Same grid as the store (token runs x (K|V, head));
+// the workgroup's maximum goes into running[kv] with one atomic max on the
+// fp32 bit pattern, which orders like the value for non-negative numbers.
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void amax_kernel(StoreParams p, float* running) {
+  constexpr int NB = D / 16;
+  const int kv = (int)blockIdx.y >= p.num_kv_heads ? 1 : 0;
+  const int g = (int)blockIdx.y - kv * p.num_kv_heads;
+  const int b = threadIdx.x % NB;
+  const int64_t i = store_token<D>(threadIdx.x);
+  float amax = 0.0f;
+  if (i < p.num_tokens) {
+    float x[16];
+    Row16<TIn>::load((const TIn*)(kv ? p.v : p.k) + i * p.in_stride + (int64_t)g * D + 16 * b, x);
+#pragma unroll
+    for (int e = 0; e < 16; e++) amax = fmaxf(amax, __builtin_fabsf(x[e]));
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    atomicMax((unsigned int*)(running + kv), as_u32(m));
+  }
+}
+
+// gs = fp32(amax / (6 * 448)) for K and V (1 for an all-zero tensor), so the
+// largest block scale of the calibrated data is E4M3's largest value.
+__global__ void global_scale_kernel(const float* running, float* gs) {
+  const int i = threadIdx.x;
+  if (i < 2) gs[i] = running[i] > 0.0f ? running[i] / 2688.0f : 1.0f;
+}
+
+hipError_t launch_calibrate_amax(const StoreParams& p, int head_dim, int in_bf16, float* running,
+                                 hipStream_t stream) {
+  const int tpw = 256 / (head_dim / 16);
+  const dim3 grid((unsigned)((p.num_tokens + tpw - 1) / tpw), (unsigned)(2 * p.num_kv_heads)), block(256);
+  if (head_dim == 256) {
+    if (in_bf16) hipLaunchKernelGGL((amax_kernel<256, uint16_t>), grid, block, 0, stream, p, running);
+    else hipLaunchKernelGGL((amax_kernel<256, float>), grid, block, 0, stream, p, running);
+  } else {
+    if (in_bf16) hipLaunchKernelGGL((amax_kernel<128, uint16_t>), grid, block, 0, stream, p, running);
+    else hipLaunchKernelGGL((amax_kernel<128, float>), grid, block, 0, stream, p, running);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_global_scale(const float* running, float* gs, hipStream_t stream) {
+  hipLaunchKernelGGL(global_scale_kernel, dim3(1), dim3(64), 0, stream, running, gs);
+  return hipGetLastError();
+}
+
 // Prefix dequantization.  A workgroup expands kDequantTokens = 64 consecutive
 // tokens (four 16-token groups, each inside one page since the page size is a
 // multiple of 16) of one (K|V, head) pair, blockIdx.y = kv * num_kv_heads +

@@ -57,6 +57,8 @@ def lib():
         "kvq_decode_attention": (i32, [C, P, i32, P, i32, P, i32, i32, f32, i32, P, i32, P, P, sz, P]),
         "kvq_dequant_prefix": (i32, [C, P, i32, P, P, i64, P]),
         "kvq_stream_read": (i32, [P, sz, P, i32, P]),
+        "kvq_calibrate_amax": (i32, [C, P, P, i32, i64, i32, P, P]),
+        "kvq_calibrate_global_scale": (i32, [C, P, P]),
         "kvq_status_string": (ctypes.c_char_p, [i32]),
         "kvq_last_hip_error": (i32, []),
     }
@@ -183,3 +185,21 @@ def kvq_stream_read(buf: torch.Tensor, sink: torch.Tensor, num_workgroups: int =
     nbytes = buf.numel() * buf.element_size() // 16 * 16
     _check("kvq_stream_read", lib().kvq_stream_read(_ptr(buf), nbytes, _ptr(sink), int(num_workgroups),
                                                     _stream(stream)))
+
+
+def kvq_calibrate_amax(cache: Cache, k: torch.Tensor, v: torch.Tensor, running_amax: torch.Tensor, stream=None):
+    """Raise running_amax (float32 [2] = {K, V}, zeroed before the first call) to max |k|, max |v|."""
+    assert k.dtype == v.dtype and k.dtype in (torch.float32, torch.bfloat16) and k.stride() == v.stride()
+    assert running_amax.dtype == torch.float32 and running_amax.numel() >= 2
+    dt = 1 if k.dtype == torch.bfloat16 else 0
+    d = cache.desc()
+    _check("kvq_calibrate_amax", lib().kvq_calibrate_amax(ctypes.byref(d), _ptr(k), _ptr(v), dt, k.stride(0),
+                                                          k.shape[0], _ptr(running_amax), _stream(stream)))
+
+
+def kvq_calibrate_global_scale(cache: Cache, running_amax: torch.Tensor, stream=None):
+    """cache.global_scale = running_amax / 2688 (1 where the amax is 0)."""
+    assert running_amax.dtype == torch.float32 and running_amax.numel() >= 2
+    d = cache.desc()
+    _check("kvq_calibrate_global_scale", lib().kvq_calibrate_global_scale(ctypes.byref(d), _ptr(running_amax),
+                                                                          _stream(stream)))

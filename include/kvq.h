@@ -166,6 +166,24 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
 kvq_status kvq_dequant_prefix(const kvq_cache* cache, const int32_t* block_table_row, int32_t prefix_len,
                               void* k_out, void* v_out, int64_t out_token_stride, void* stream);
 
+/* Global-scale calibration for NVFP4 ("SGLang's 4-bit KV cache ...",
+ * section '"Near-lossless" is narrower than it sounds': the measured NVFP4
+ * drops its per-tensor FP32 scale, which leaves the E4M3 block scale to carry
+ * the whole dynamic range; calibration is listed as ongoing work).
+ *
+ * kvq_calibrate_amax raises running_amax (device float[2] = {K, V}, zeroed by
+ * the caller before the first call) to the largest |value| of this call's K
+ * and V rows (same row arguments as kvq_quantize_store, no slots).  Run it
+ * over the prefill chunks of a layer, then kvq_calibrate_global_scale writes
+ * cache->global_scale[i] = fp32(running_amax[i] / (6 * 448)) (1 for an
+ * all-zero tensor), which puts the largest calibrated block scale on E4M3's
+ * 448.  Call it before the layer's first kvq_quantize_store: blocks already
+ * stored keep the scale they were written with.  NVFP4 caches only
+ * (KVQ_ERR_UNSUPPORTED otherwise). */
+kvq_status kvq_calibrate_amax(const kvq_cache* cache, const void* k, const void* v, int32_t in_dtype,
+                              int64_t in_token_stride, int32_t num_tokens, float* running_amax, void* stream);
+kvq_status kvq_calibrate_global_scale(const kvq_cache* cache, const float* running_amax, void* stream);
+
 /* Measurement aid, not part of the cache path: a plain streaming read of
  * `bytes` bytes of device memory (the practical HBM read ceiling against which
  * the decode kernel's bandwidth is judged).  Nothing is computed from the data

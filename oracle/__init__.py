@@ -68,6 +68,8 @@ def _load():
         "kvqo_dequant_prefix": (None, [i32, P, i32, i32, i32, P, P, i64, P, P, i64]),
         "kvqo_num_threads": (i32, []),
         "kvqo_set_num_threads": (None, [i32]),
+        "kvqo_amax": (f32, [P, i64]),
+        "kvqo_global_scale": (f32, [f32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -150,6 +152,17 @@ def int4_dequant_row(codes, scale) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- pool level
+
+def amax(x) -> float:
+    """Largest |x| (the running maximum a calibration pass keeps)."""
+    a = _f32(np.ascontiguousarray(x).ravel())
+    return float(_load().kvqo_amax(_ptr(a), a.size))
+
+
+def global_scale(amax_value: float) -> float:
+    """NVFP4 per-layer global scale from a calibrated amax: fp32(amax / 2688)."""
+    return float(_load().kvqo_global_scale(float(amax_value)))
+
 
 def slab_bytes(fmt: int, page_size: int, head_dim: int) -> int:
     return int(_load().kvqo_slab_bytes(fmt, page_size, head_dim))

@@ -423,6 +423,24 @@ void kvqo_dequant_prefix(int fmt, const uint8_t* pool, int P, int Hkv, int D, co
   }
 }
 
+/* Global-scale calibration ("SGLang's 4-bit KV cache ...", section
+ * '"Near-lossless" is narrower than it sounds': the measured NVFP4 runs
+ * without its per-tensor FP32 scale and calibration is listed as ongoing
+ * work).  Reading: gs is taken from the running absolute maximum of a
+ * layer's K (or V) over the prefill tokens so that the largest block scale
+ * lands on E4M3's largest finite value: gs = fp32(amax / (6 * 448)); an
+ * all-zero tensor keeps gs = 1. */
+float kvqo_amax(const float* x, int64_t n) {
+  float m = 0.0f;
+  for (int64_t i = 0; i < n; i++) {
+    const float a = fabsf(x[i]);
+    if (a > m) m = a;
+  }
+  return m;
+}
+
+float kvqo_global_scale(float amax) { return amax > 0.0f ? amax / 2688.0f : 1.0f; }
+
 /* Number of OpenMP threads the oracle's parallel loops use. */
 int kvqo_num_threads(void) {
 #ifdef _OPENMP

@@ -154,3 +154,22 @@ def test_stream_read_validation(lib):
     assert lib.kvq_stream_read(FAKE + 8, 64, FAKE, 0, None) == ERR_ALIGN
     assert lib.kvq_stream_read(FAKE, 60, FAKE, 0, None) == ERR_ALIGN
     assert lib.kvq_stream_read(FAKE, 64, FAKE + 2, 0, None) == ERR_ALIGN
+
+
+def test_calibration_validation(lib):
+    c = cache()
+    f = lib.kvq_calibrate_amax
+    assert f(ctypes.byref(c), FAKE, FAKE, 1, 1024, 0, FAKE, None) == OK          # no tokens
+    assert f(ctypes.byref(c), FAKE, FAKE, 1, 1024, -1, FAKE, None) == ERR_SHAPE
+    assert f(ctypes.byref(c), FAKE, FAKE, 1, 1024, 4, None, None) == ERR_NULL
+    assert f(ctypes.byref(c), 0, FAKE, 1, 1024, 4, FAKE, None) == ERR_NULL
+    assert f(ctypes.byref(c), FAKE, FAKE, 1, 512, 4, FAKE, None) == ERR_SHAPE     # stride < Hkv * D
+    assert f(ctypes.byref(c), FAKE, FAKE, 1, 1028, 4, FAKE, None) == ERR_ALIGN
+    assert f(ctypes.byref(c), FAKE, FAKE, 1, 1024, 4, FAKE + 2, None) == ERR_ALIGN
+    assert f(ctypes.byref(c), FAKE, FAKE, 7, 1024, 4, FAKE, None) == ERR_UNSUPPORTED
+    c4 = cache(fmt=2, gs=0)
+    assert f(ctypes.byref(c4), FAKE, FAKE, 1, 1024, 4, FAKE, None) == ERR_UNSUPPORTED  # INT4 has no global scale
+    g = lib.kvq_calibrate_global_scale
+    assert g(ctypes.byref(c), None, None) == ERR_NULL
+    assert g(ctypes.byref(c4), FAKE, None) == ERR_UNSUPPORTED
+    assert g(ctypes.byref(c), FAKE + 1, None) == ERR_ALIGN

@@ -11,7 +11,9 @@ Formats follow the pages "SGLang's 4-bit KV cache: the 56% is exact, the 1.78x
 is untested" (Figure 2 caption; section "The 56% survives its own scale, and
 names the block size") for NVFP4 and "KV cache in 4 bits: 8.8 instead of 4.7
 full sessions on the same four RTX 5090s" (section "What we changed") for the
-INT4 per-token-head cache.
+INT4 per-token-head cache; the FP8 E4M3 per-tensor-scaled cache is the
+comparator the first page measures NVFP4 against (section "The 56% survives
+its own scale, and names the block size").
 """
 from __future__ import annotations
 
@@ -23,6 +25,7 @@ import numpy as np
 
 NVFP4 = 1
 INT4 = 2
+FP8 = 3  # E4M3 with one FP32 scale per tensor: the comparator format
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
@@ -69,6 +72,7 @@ def _load():
         "kvqo_num_threads": (i32, []),
         "kvqo_set_num_threads": (None, [i32]),
         "kvqo_amax": (f32, [P, i64]),
+        "kvqo_fp8_encode": (i32, [f32, f32]),
         "kvqo_global_scale": (f32, [f32]),
     }
     for name, (res, args) in sig.items():
@@ -159,6 +163,11 @@ def amax(x) -> float:
     return float(_load().kvqo_amax(_ptr(a), a.size))
 
 
+def fp8_encode(x: float, scale: float) -> int:
+    """FP8 (E4M3, per-tensor scale) code of x: E4M3 of fp32(x / scale), sign kept."""
+    return int(_load().kvqo_fp8_encode(float(x), float(scale)))
+
+
 def global_scale(amax_value: float) -> float:
     """NVFP4 per-layer global scale from a calibrated amax: fp32(amax / 2688)."""
     return float(_load().kvqo_global_scale(float(amax_value)))
@@ -209,6 +218,8 @@ class Pool:
     def dequant_prefix(self, pages, prefix_len: int, out_token_stride: int | None = None):
         """Returns (k_out, v_out) as uint16 bf16 bit patterns [prefix_len][Hkv][D]
         (or [prefix_len][out_token_stride] when a wider stride is given)."""
+        if self.fmt == FP8:
+            raise ValueError("the FP8 comparator has no prefix dequantization")
         pages = _i32(pages)
         Hkv, D = self.num_kv_heads, self.head_dim
         stride = out_token_stride or Hkv * D
@@ -224,6 +235,9 @@ class Pool:
         """Exact fp64 value of one stored row (kv 0 = K, 1 = V)."""
         P, D = self.page_size, self.head_dim
         slab = self.data[page, g]
+        if self.fmt == FP8:
+            codes = slab[off * D:(off + 1) * D] if kv == 0 else slab[P * D + off::P][:D]
+            return np.array([e4m3_value(int(c)) for c in codes]) * float(self.gs[kv])
         half = slab[: self.slab // 2] if kv == 0 else slab[self.slab // 2:]
         codes = half[off * (D // 2):(off + 1) * (D // 2)]
         if self.fmt == NVFP4:

@@ -40,6 +40,7 @@
 
 #define KVQO_NVFP4 1
 #define KVQO_INT4 2
+#define KVQO_FP8 3
 
 /* ---------------------------------------------------------------------- */
 /* Element and scale formats                                               */
@@ -229,12 +230,36 @@ void kvqo_int4_dequant_row(const uint8_t* codes, float scale, int D, double* out
 static size_t row_code_bytes(int D) { return (size_t)D / 2; }
 static size_t row_scale_bytes(int fmt, int D) { return fmt == KVQO_NVFP4 ? (size_t)D / 16 : 4; }
 
+/* FP8 E4M3 with one FP32 scale per tensor (the comparator: "SGLang's 4-bit
+ * KV cache ...", section "The 56% survives its own scale, and names the block
+ * size", states that the comparison assumes a per-tensor-scaled FP8 cache):
+ * one byte per value, no per-token scales.  Slab of one (page, head):
+ * [K: P rows x D bytes][V transposed: D rows (channels) x P bytes], so that a
+ * channel's values for consecutive tokens are adjacent (the paged-attention
+ * value layout). */
 size_t kvqo_slab_bytes(int fmt, int P, int D) {
+  if (fmt == KVQO_FP8) return 2 * (size_t)P * (size_t)D;
   return 2 * (size_t)P * (row_code_bytes(D) + row_scale_bytes(fmt, D));
 }
 
 /* Bytes one token costs in one KV head (K and V, codes and scales). */
-size_t kvqo_token_head_bytes(int fmt, int D) { return 2 * (row_code_bytes(D) + row_scale_bytes(fmt, D)); }
+size_t kvqo_token_head_bytes(int fmt, int D) {
+  if (fmt == KVQO_FP8) return 2 * (size_t)D;
+  return 2 * (row_code_bytes(D) + row_scale_bytes(fmt, D));
+}
+
+/* FP8 value code: y = fp32(x / s), then E4M3 of |y| (nearest, ties to the
+ * even code, saturating at 448) with the sign of y (so -0 is 0x80). */
+int kvqo_fp8_encode(float x, float s) {
+  const float y = x / s;
+  return kvqo_e4m3_encode(fabsf(y)) | (signbit(y) ? 0x80 : 0);
+}
+
+/* Byte offset of value (token offset off, channel c) of K (kv = 0) or V
+ * (kv = 1) inside an FP8 slab. */
+static size_t fp8_offset(int P, int D, int off, int c, int kv) {
+  return kv ? (size_t)P * D + (size_t)c * P + off : (size_t)off * D + c;
+}
 
 typedef struct {
   uint8_t* codes;
@@ -258,7 +283,7 @@ static rowptr locate(uint8_t* pool, int fmt, int P, int Hkv, int D, int64_t page
  * slot / P and offset = slot % P; each KV head's K and V row is quantized
  * and stored there.  A negative slot skips the token.  k, v are
  * [n_tok][Hkv][D] fp32 (bf16 inputs widened exactly by the caller);
- * gs = {gs_K, gs_V} (NVFP4 only). */
+ * gs = {gs_K, gs_V} (NVFP4: global scales; FP8: the per-tensor scales). */
 void kvqo_quantize_store(int fmt, uint8_t* pool, int P, int Hkv, int D, const float* gs, const float* k,
                          const float* v, int n_tok, const int32_t* slot_mapping) {
 #pragma omp parallel for schedule(static)
@@ -270,6 +295,11 @@ void kvqo_quantize_store(int fmt, uint8_t* pool, int P, int Hkv, int D, const fl
     for (int g = 0; g < Hkv; g++) {
       for (int kv = 0; kv < 2; kv++) {
         const float* x = (kv ? v : k) + ((size_t)i * Hkv + g) * D;
+        if (fmt == KVQO_FP8) {
+          uint8_t* base = pool + ((size_t)page * Hkv + g) * kvqo_slab_bytes(fmt, P, D);
+          for (int c = 0; c < D; c++) base[fp8_offset(P, D, off, c, kv)] = (uint8_t)kvqo_fp8_encode(x[c], gs[kv]);
+          continue;
+        }
         rowptr r = locate(pool, fmt, P, Hkv, D, page, g, off, kv);
         if (fmt == KVQO_NVFP4) {
           kvqo_nvfp4_quantize_row(x, D, gs[kv], r.codes, r.scales);
@@ -287,6 +317,11 @@ void kvqo_quantize_store(int fmt, uint8_t* pool, int P, int Hkv, int D, const fl
  * t of a sequence whose page list is `pages`. */
 static void read_token(const uint8_t* pool, int fmt, int P, int Hkv, int D, const float* gs, const int32_t* pages,
                        int64_t t, int g, int kv, double* out) {
+  if (fmt == KVQO_FP8) {
+    const uint8_t* base = pool + ((size_t)pages[t / P] * Hkv + g) * kvqo_slab_bytes(fmt, P, D);
+    for (int c = 0; c < D; c++) out[c] = kvqo_e4m3_value(base[fp8_offset(P, D, (int)(t % P), c, kv)]) * gs[kv];
+    return;
+  }
   rowptr r = locate((uint8_t*)pool, fmt, P, Hkv, D, pages[t / P], g, (int)(t % P), kv);
   if (fmt == KVQO_NVFP4) {
     kvqo_nvfp4_dequant_row(r.codes, r.scales, D, gs[kv], out);
@@ -397,6 +432,7 @@ void kvqo_decode_attention(int fmt, const uint8_t* pool, int P, int Hkv, int D, 
 void kvqo_dequant_prefix(int fmt, const uint8_t* pool, int P, int Hkv, int D, const float* gs,
                          const int32_t* pages, int64_t prefix_len, uint16_t* k_out, uint16_t* v_out,
                          int64_t out_token_stride) {
+  if (fmt == KVQO_FP8) return; /* the FP8 comparator has no extend path */
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < prefix_len; t++) {
     for (int g = 0; g < Hkv; g++) {

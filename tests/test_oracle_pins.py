@@ -331,13 +331,14 @@ def _torch_attention(q, K, V, G, sm_scale):
 
 
 @pytest.mark.parametrize("fmt,P,G,Hkv,L", [(1, 16, 4, 1, 70), (1, 3, 6, 2, 40), (1, 1, 1, 2, 9),
-                                            (2, 16, 6, 2, 45), (2, 4, 4, 1, 33)])
+                                            (2, 16, 6, 2, 45), (2, 4, 4, 1, 33),
+                                            (3, 16, 6, 2, 45), (3, 5, 4, 1, 33)])
 def test_attention_matches_torch_fp64(oracle, fmt, P, G, Hkv, L):
-    D, B = 64 if fmt == 1 else 32, 2
+    D, B = 64 if fmt != 2 else 32, 2
     Hq = G * Hkv
     n_pages_seq = -(-L // P)
     bt = inputs.page_tables(99, B, n_pages_seq, num_pages=B * n_pages_seq + 5, shuffled=True)
-    pool = oracle.Pool(fmt, B * n_pages_seq + 5, P, Hkv, D, global_scale=(0.5, 2.0) if fmt == 1 else (1, 1))
+    pool = oracle.Pool(fmt, B * n_pages_seq + 5, P, Hkv, D, global_scale=(0.5, 2.0) if fmt != 2 else (1, 1))
     seq_lens = np.array([L, L - 5], np.int32)
     for b in range(B):
         k, v = inputs.kv_outlier_channels(7, b, int(seq_lens[b]), Hkv, D)
@@ -518,3 +519,50 @@ def test_calibration_rescues_out_of_range_tensors(oracle):
             return math.sqrt(err / float(np.sum(x.astype(np.float64) ** 2)))
         assert rel_rms(1.0) > 0.9, (scale, broken)
         assert rel_rms(oracle.global_scale(oracle.amax(x))) < 0.15
+
+
+# ----------------------------------------------------------------- FP8 E4M3 per-tensor comparator
+
+def test_fp8_footprint_matches_page_table(oracle):
+    g = golden("footprint_pages.json")
+    per_token = g["qwen38_27b_per_token_elements"]
+    heads = per_token["layers"] * per_token["kv_heads"]
+    assert oracle.token_head_bytes(oracle.FP8, 256) * heads == g["qwen38_27b_per_token_fp8_bytes"]["value"]
+    assert oracle.token_head_bytes(oracle.NVFP4, 256) * heads == g["qwen38_27b_per_token_nvfp4_bytes"]["value"]
+    assert oracle.token_head_bytes(oracle.NVFP4, 256) / oracle.token_head_bytes(oracle.FP8, 256) == \
+        g["nvfp4_ratio_vs_fp8"]["value"]
+    assert oracle.slab_bytes(oracle.FP8, 16, 256) == 16 * 2 * 256
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.5, 0.37, 3.0])
+def test_fp8_encode_matches_torch_cast(oracle, scale):
+    r = np.random.default_rng(11)
+    y = [0.0, -0.0]
+    y += list(2.0 ** r.uniform(-12, np.log2(448.0), 1500) * r.choice([-1, 1], 1500))
+    for c in range(0x7E):  # exact ties between neighbouring codes, both signs
+        m = (oracle.e4m3_value(c) + oracle.e4m3_value(c + 1)) / 2
+        y += [m, -m]
+    x = (np.array(y, np.float32) * np.float32(scale)).astype(np.float32)
+    ratio = (torch.from_numpy(x) / torch.tensor(scale, dtype=torch.float32)).numpy()  # fp32 division
+    keep = np.abs(ratio) <= 448.0
+    ref = _torch_e4m3_code(ratio[keep])
+    got = np.array([oracle.fp8_encode(v, scale) for v in x[keep]])
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(x[keep][i], got[i], ref[i]) for i in bad[:5]]
+    assert oracle.fp8_encode(-0.0, scale) == 0x80
+    for big in (449.0, 1e6, -1e6):
+        assert oracle.fp8_encode(big * scale, scale) == (0x7E | (0x80 if big < 0 else 0))
+
+
+def test_fp8_layout_keys_by_row_values_by_channel(oracle):
+    P, Hkv, D = 16, 2, 64
+    pool = oracle.Pool(oracle.FP8, 3, P, Hkv, D, global_scale=(1.0, 1.0))
+    k = np.zeros((1, Hkv, D), np.float32)
+    v = np.zeros((1, Hkv, D), np.float32)
+    k[0, 1, 5] = 2.0      # E4M3 2.0 = 0x40
+    v[0, 1, 7] = -0.5     # E4M3 -0.5 = 0xB0
+    pool.quantize_store(k, v, np.array([2 * P + 9], np.int32))   # page 2, row 9
+    slab = pool.data[2, 1]
+    assert slab[9 * D + 5] == 0x40                  # K: row 9, byte 5
+    assert slab[P * D + 7 * P + 9] == 0xB0          # V: channel 7's row, byte 9
+    assert np.count_nonzero(pool.data) == 2

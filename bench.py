@@ -49,12 +49,17 @@ WORKLOADS = {
     "int4_220k": dict(fmt=2, batch=8, ctx=220000, page=1600, shuffled=False, kind="student_t",
                       desc="INT4 per-token-head, batch 8, context 220,000, 1,600-token pages (last page half "
                            "full); 16 layers assumed"),
+    "fp8_32k": dict(fmt=3, batch=32, ctx=32768, page=16, shuffled=False, kind="lognormal",
+                    desc="comparator: the 32K headline shape with an FP8 E4M3 per-tensor cache (512 B per "
+                         "token and head against NVFP4's 288 B)"),
 }
 LAYERS, HKV, HQ, D = 16, 4, 24, 256
 
 
 def token_head_bytes(fmt: int) -> int:
     # packed codes + scales of one token in one KV head, K and V
+    if fmt == 3:
+        return 2 * D  # FP8: one byte per value, per-tensor scales
     return 2 * (D // 2 + (D // 16 if fmt == 1 else 4))
 
 
@@ -196,7 +201,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ctx32k", choices=sorted(WORKLOADS))
-    ap.add_argument("--secondary", default="ctx160k,ctx1m,int4_220k",
+    ap.add_argument("--secondary", default="ctx160k,ctx1m,int4_220k,fp8_32k",
                     help="comma-separated extra workloads to report ('' for none)")
     ap.add_argument("--secondary-steps", type=int, default=5)
     ap.add_argument("--layers", type=int, default=LAYERS)
@@ -366,7 +371,7 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
     decode_ms = sum(b.elapsed_time(c) for _, b, c in pairs) / len(pairs)
     kv_bytes_layer = B * L * HKV * token_head_bytes(fmt)
     res = {
-        "workload": name, "desc": w["desc"], "format": "nvfp4" if fmt == 1 else "int4_per_token_head",
+        "workload": name, "desc": w["desc"], "format": {1: "nvfp4", 2: "int4_per_token_head", 3: "fp8_e4m3_per_tensor"}[fmt],
         "batch": B, "context": L, "page_size": P, "layers": n_layers, "num_splits": splits,
         "step_ms": step_ms, "decode_call_us": decode_ms * 1e3, "store_call_us": store_ms * 1e3,
         "kv_bytes_per_layer": kv_bytes_layer,
@@ -578,6 +583,14 @@ def main():
         "populate": r["populate"],
         "secondary": secondary,
     }
+    if "fp8_32k" in secondary and args.workload == "ctx32k":
+        f8 = secondary["fp8_32k"]
+        line["fp8_comparator"] = {
+            "nvfp4_decode_call_us": r["decode_call_us"], "fp8_decode_call_us": f8["decode_call_us"],
+            "time_ratio_nvfp4_over_fp8": r["decode_call_us"] / f8["decode_call_us"],
+            "byte_ratio_nvfp4_over_fp8": token_head_bytes(1) / token_head_bytes(3),
+            "decode_speedup_vs_fp8": f8["decode_call_us"] / r["decode_call_us"],
+            "fp8_decode_call_gbs": f8["decode_call_gbs"]}
     print(json.dumps(line), flush=True)
 
 

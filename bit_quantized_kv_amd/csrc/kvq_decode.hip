@@ -59,31 +59,17 @@ struct ChunkRegs {
   uint32_t vsc[2];    // INT4: V scale (fp32 bits) of token 4j + r%4
 };
 
-template <int D, int FMT>
-struct Decoder {
-  static constexpr int VEC = D / 128;
-  static constexpr int VW = D / 128;
-  static constexpr int KCH = D / 32;  // QK MFMAs per half
-  static constexpr int VT = D / 16;   // PV MFMAs (16-channel tiles)
-  using Regs = ChunkRegs<D, FMT>;
-
+// Walking one (sequence, KV head)'s pages in 32-token chunks: page-table
+// entries, row offsets and the per-slab buffer descriptor.
+struct PageWalk {
   const DecodeParams& p;
-  const int lane, j, r, b, g, L;
+  const int L;
   const uint8_t* head_base;  // pool + g * slab
   const int32_t* pages;      // block_table row of sequence b
-  int vo_k, vo_ks, vo_vs_h, vo_sc, vo_sc_h, vo_v_h;  // per-lane byte offsets inside a slab
 
-  __device__ Decoder(const DecodeParams& p_, int lane_, int b_, int g_, int L_)
-      : p(p_), lane(lane_), j(lane_ >> 4), r(lane_ & 15), b(b_), g(g_), L(L_) {
+  __device__ PageWalk(const DecodeParams& p_, int b, int g, int L_) : p(p_), L(L_) {
     head_base = p.pool + (int64_t)g * p.slab;
     pages = p.block_table + (int64_t)b * p.max_pages;
-    // (the _h offsets include the K half, i.e. they address the V half)
-    vo_k = r * (D / 2) + 16 * j;                                            // K code row r
-    vo_ks = r * (D / 16) + 4 * (j >> 1);                                    // K scale row r
-    vo_vs_h = (int)p.half + (4 * j + (r & 3)) * (D / 16) + 4 * (((r >> 2) * D) / 256);
-    vo_sc = (4 * j + (r & 3)) * 4;                                          // INT4 scale of row 4j + r%4
-    vo_sc_h = (int)p.half + vo_sc;
-    vo_v_h = (int)p.half + 4 * j * (D / 2) + r * (D / 32);                  // V code rows 4j + i
   }
 
   // Position of a chunk in the page table, advanced without division: the
@@ -137,6 +123,30 @@ struct Decoder {
   __device__ inline __amdgpu_buffer_rsrc_t slab_rsrc(int page) const {
     const uint8_t* base = head_base + (int64_t)page * p.num_kv_heads * p.slab;
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)p.slab, 0x00020000);
+  }
+
+};
+
+template <int D, int FMT>
+struct Decoder : PageWalk {
+  static constexpr int VEC = D / 128;
+  static constexpr int VW = D / 128;
+  static constexpr int KCH = D / 32;  // QK MFMAs per half
+  static constexpr int VT = D / 16;   // PV MFMAs (16-channel tiles)
+  using Regs = ChunkRegs<D, FMT>;
+
+  const int lane, j, r;
+  int vo_k, vo_ks, vo_vs_h, vo_sc, vo_sc_h, vo_v_h;  // per-lane byte offsets inside a slab
+
+  __device__ Decoder(const DecodeParams& p_, int lane_, int b_, int g_, int L_)
+      : PageWalk(p_, b_, g_, L_), lane(lane_), j(lane_ >> 4), r(lane_ & 15) {
+    // (the _h offsets include the K half, i.e. they address the V half)
+    vo_k = r * (D / 2) + 16 * j;                                            // K code row r
+    vo_ks = r * (D / 16) + 4 * (j >> 1);                                    // K scale row r
+    vo_vs_h = (int)p.half + (4 * j + (r & 3)) * (D / 16) + 4 * (((r >> 2) * D) / 256);
+    vo_sc = (4 * j + (r & 3)) * 4;                                          // INT4 scale of row 4j + r%4
+    vo_sc_h = (int)p.half + vo_sc;
+    vo_v_h = (int)p.half + 4 * j * (D / 2) + r * (D / 32);                  // V code rows 4j + i
   }
 
   // Loads of one chunk: the descriptor and the chunk's row offsets are
@@ -610,6 +620,266 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   }
 }
 
+// ---------------------------------------------------------------- FP8 comparator
+// Decode over the FP8 E4M3 per-tensor cache (the format the first page's
+// 0.5625 ratio is taken against; "SGLang's 4-bit KV cache ...", section "The
+// 56% survives its own scale, and names the block size").  Same grid, split
+// plan, page walk, online softmax and merge as the 4-bit kernel; the step is
+// one 16-token half (a half's K and V are 8 KB at D 256, so one half in
+// flight matches the 4-bit kernel's register budget):
+//   QK  v_mfma_f32_16x16x32_f16, lane (j, r) loads 16 B of token r's K row at
+//       bytes 64w + 16j (w < D/64), i.e. channels 64w + 16j .. +16, which
+//       feed MFMAs 2w and 2w + 1; q is permuted the same way.
+//   PV  v_mfma_f32_16x16x16_f16 over the half's 16 tokens: the V section is
+//       stored by channel, so lane (j, r) reads the 4 bytes of tokens 4j..4j+3
+//       of channel 16t + r for tile t with one dword load, and the QK output
+//       layout (lane (j, n): tokens 4j..4j+3 of query n) is already the B
+//       operand of the PV product.
+//   E4M3 -> fp16 with v_cvt_scalef32_pk_f16_fp8 at unit scale (exact); the
+//   per-tensor scales go into the score scale (K) and the output (V).
+template <int D>
+struct Fp8Regs {
+  u32x4_t kw[D / 64];
+  uint32_t vw[D / 16];
+};
+
+template <int D, bool DUP>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void decode_fp8_kernel(
+    const DecodeParams p) {
+  constexpr int KW = D / 64, KCH = D / 32, VT = D / 16;
+  using Regs = Fp8Regs<D>;
+  extern __shared__ float smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int L = p.seq_lens[b];
+  const int G = p.group;
+  const int j = lane >> 4, n = lane & 15;
+  const int64_t part = ((int64_t)b * p.num_kv_heads + g) * p.num_splits + split;
+  float* ml = p.part_ml + part * G * 2;
+  float* po = p.part_o + part * G * D;
+
+  const int nchunks = (L + 31) / 32;
+  const int c0 = split * p.chunks_per_split;
+  const int c1 = min(nchunks, c0 + p.chunks_per_split);
+  if (c0 >= c1) {
+    for (int i = threadIdx.x; i < G * D; i += 64 * kWaves) po[i] = 0.0f;
+    if (threadIdx.x < G) {
+      ml[2 * threadIdx.x] = -__builtin_inff();
+      ml[2 * threadIdx.x + 1] = 0.0f;
+    }
+    return;
+  }
+  const int cw0 = c0 + wave;
+  PageWalk walk(p, b, g, L);
+  const int P = p.page_size;
+  const int vo_k = n * D + 16 * j;                   // K row n, bytes 16j (+ 64w)
+  const int vo_v = (int)p.half + n * P + 4 * j;      // V channel row n (+ 16t), tokens 4j..4j+3
+
+  auto load = [&](Regs& R, int page, int row0) {
+    const __amdgpu_buffer_rsrc_t rs = walk.slab_rsrc(__builtin_amdgcn_readfirstlane(page));
+    const int off = __builtin_amdgcn_readfirstlane(row0);
+#pragma unroll
+    for (int w = 0; w < KW; w++) R.kw[w] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo_k + 64 * w, off * D, 0);
+#pragma unroll
+    for (int t = 0; t < VT; t++)
+      R.vw[t] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_v, __builtin_amdgcn_readfirstlane(off + 16 * t * P), 0);
+  };
+
+  // q operand: lane (j, n) holds query n, channels 64(m/2) + 16j + 8(m%2) + e
+  // of MFMA m, scaled by 2^kq as in the 4-bit kernel
+  float qf[KCH][8];
+  float qmax = 0.0f;
+  {
+    const int qn = DUP ? (n & 7) : n;
+    const uint16_t* qrow = p.q + ((int64_t)b * p.num_q_heads + (int64_t)g * G + (qn < G ? qn : 0)) * D;
+#pragma unroll
+    for (int m = 0; m < KCH; m++) {
+      const uint4 raw = *(const uint4*)(qrow + 64 * (m / 2) + 16 * j + 8 * (m % 2));
+      const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float lo = qn < G ? as_f32(rw[e] << 16) : 0.0f;
+        const float hi = qn < G ? as_f32(rw[e] & 0xFFFF0000u) : 0.0f;
+        qf[m][2 * e] = lo;
+        qf[m][2 * e + 1] = hi;
+        qmax = fmaxf(qmax, fmaxf(__builtin_fabsf(lo), __builtin_fabsf(hi)));
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, m, 64));
+  int qexp = 0;
+  if (qmax > 0.0f) (void)frexpf(qmax, &qexp);
+  const int kq = qmax > 0.0f ? 15 - qexp : 0;
+  half8_t qop[KCH];
+#pragma unroll
+  for (int c = 0; c < KCH; c++) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) qop[c][e] = (_Float16)ldexpf(qf[c][e], kq);
+  }
+  const float sm = p.sm_scale * kLog2e * ldexpf(1.0f, -kq) * p.gs[0];
+  const float lo_sel = n < 8 ? 0.0f : 1.0f;
+
+  float4_t oacc[VT];
+#pragma unroll
+  for (int t = 0; t < VT; t++) oacc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -__builtin_inff();
+  float l_run = 0.0f;
+
+  // one 16-token half starting at token T
+  auto compute = [&](Regs& R, int T) {
+    float4_t sacc = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < KCH; m++) {
+      const u32x4_t kw = R.kw[m / 2];
+      const uint32_t d0 = (m % 2) ? kw.z : kw.x, d1 = (m % 2) ? kw.w : kw.y;
+      const half2_t a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
+      const half2_t a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
+      const half2_t a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
+      const half2_t a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
+      const half8_t a = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[m], sacc, 0, 0, 0);
+    }
+    // tokens past the end: score -inf, and their V bytes (never written, so
+    // possibly NaN codes) cleared so that p = 0 meets a finite value
+    const bool ragged = T + 16 > L;
+    float s[4];
+    float cmax = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float x = sacc[i] * sm;
+      s[i] = T + 4 * j + i < L ? x : -__builtin_inff();
+      cmax = fmaxf(cmax, s[i]);
+    }
+    if (ragged) {
+      const int nv = min(max(L - T - 4 * j, 0), 4);
+      const uint32_t mask = nv >= 4 ? 0xFFFFFFFFu : (1u << (8 * nv)) - 1u;
+#pragma unroll
+      for (int t = 0; t < VT; t++) R.vw[t] &= mask;
+    }
+    cmax = max_xor16_xor32(cmax);
+    if (__builtin_amdgcn_ballot_w64(cmax > m_run + kRescaleSlack) != 0) {
+      const float m_new = cmax > m_run + kRescaleSlack ? cmax : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < VT; t++) oacc[t] *= alpha;
+    }
+    half4_t pop, pop_lo;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float e = __builtin_amdgcn_exp2f(s[i] - m_run);
+      l_run += e;
+      const _Float16 hi = (_Float16)e;
+      if (DUP) {
+        pop[i] = (_Float16)(e - lo_sel * (float)hi);
+      } else {
+        pop[i] = hi;
+        pop_lo[i] = (_Float16)(e - (float)hi);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < VT; t++) {
+      const half2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(R.vw[t], 1.0f, false);
+      const half2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(R.vw[t], 1.0f, true);
+      const half4_t a = {v0[0], v0[1], v1[0], v1[1]};
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pop, oacc[t], 0, 0, 0);
+      if (!DUP) oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pop_lo, oacc[t], 0, 0, 0);
+    }
+  };
+
+  constexpr int S1 = kWaves;
+  if (cw0 < c1) {
+    const int clast = cw0 + (c1 - 1 - cw0) / S1 * S1;
+    const int dq = (32 * S1) / P, dr = (32 * S1) % P;
+    Regs RA, RB;
+    auto fc = walk.cursor_at(cw0);
+    auto ref0 = walk.fetch(fc);
+    walk.advance(fc, S1, clast, dq, dr);
+    auto ref1 = walk.fetch(fc);
+    walk.advance(fc, S1, clast, dq, dr);
+    load(RA, ref0.pg.x, ref0.row0);
+    for (int c = cw0; c <= clast; c += S1) {
+      load(RB, ref0.pg.y, ref0.row1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(RA, 32 * c);
+      __builtin_amdgcn_sched_barrier(0);
+      const auto ref2 = walk.fetch(fc);
+      walk.advance(fc, S1, clast, dq, dr);
+      load(RA, ref1.pg.x, ref1.row0);  // the next chunk's first half (the last chunk again at the end)
+      __builtin_amdgcn_sched_barrier(0);
+      compute(RB, 32 * c + 16);
+      __builtin_amdgcn_sched_barrier(0);
+      ref0 = ref1;
+      ref1 = ref2;
+    }
+  }
+
+  // ---- partial results, as in the 4-bit kernel; O^T tile t row 4j + rr is
+  // channel 16t + 4j + rr
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (DUP) {
+#pragma unroll
+    for (int t = 0; t < VT; t++) {
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) oacc[t][rr] += __shfl_xor(oacc[t][rr], 8, 64);
+    }
+  }
+  float* sm_o = smem;
+  float* sm_ml = smem + G * D;
+  if (j == 0 && n < G) {
+    sm_ml[(wave * G + n) * 2] = m_run;
+    sm_ml[(wave * G + n) * 2 + 1] = l_run;
+  }
+  __syncthreads();
+  float scale_o = 0.0f;
+  if (n < G) {
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, sm_ml[(w * G + n) * 2]);
+    scale_o = m_run == -__builtin_inff() ? 0.0f : exp2f(m_run - M) * p.gs[1];
+  }
+#pragma unroll
+  for (int w = 0; w < kWaves; w++) {
+    if (wave == w && n < G) {
+      float* dst = sm_o + n * D + 4 * j;
+#pragma unroll
+      for (int t = 0; t < VT; t++) {
+        float4 x = make_float4(oacc[t][0] * scale_o, oacc[t][1] * scale_o, oacc[t][2] * scale_o,
+                               oacc[t][3] * scale_o);
+        if (w > 0) {
+          const float4 y = *(float4*)(dst + 16 * t);
+          x.x += y.x;
+          x.y += y.y;
+          x.z += y.z;
+          x.w += y.w;
+        }
+        *(float4*)(dst + 16 * t) = x;
+      }
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < G * D; i += 64 * kWaves) po[i] = sm_o[i];
+  if (threadIdx.x < G) {
+    const int q = threadIdx.x;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, sm_ml[(w * G + q) * 2]);
+    float l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+      const float mw = sm_ml[(w * G + q) * 2];
+      if (mw != -__builtin_inff()) l += exp2f(mw - M) * sm_ml[(w * G + q) * 2 + 1];
+    }
+    ml[2 * q] = M;
+    ml[2 * q + 1] = l;
+  }
+}
+
 // Merge the splits of one (sequence, query head): M = max m_s,
 // o = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s, lse = (M + log2 sum) ln 2.
 //
@@ -737,14 +1007,25 @@ hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream
     if (dup) hipLaunchKernelGGL((decode_kernel<D, F, true>), grid, block, lds, stream, p);      \
     else hipLaunchKernelGGL((decode_kernel<D, F, false>), grid, block, lds, stream, p);         \
   } while (0)
-  if (head_dim == 256) {
+  if (fmt == FMT_FP8) {
+    if (head_dim == 256) {
+      if (dup) hipLaunchKernelGGL((decode_fp8_kernel<256, true>), grid, block, lds, stream, p);
+      else hipLaunchKernelGGL((decode_fp8_kernel<256, false>), grid, block, lds, stream, p);
+    } else {
+      if (dup) hipLaunchKernelGGL((decode_fp8_kernel<128, true>), grid, block, lds, stream, p);
+      else hipLaunchKernelGGL((decode_fp8_kernel<128, false>), grid, block, lds, stream, p);
+    }
+  } else if (head_dim == 256) {
     if (fmt == FMT_NVFP4) KVQ_DECODE(256, FMT_NVFP4);
     else KVQ_DECODE(256, FMT_INT4);
-    if (narrow) hipLaunchKernelGGL((merge_kernel<256>), mgrid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((merge_wide_kernel<256>), mgrid, dim3(256), 0, stream, p);
   } else {
     if (fmt == FMT_NVFP4) KVQ_DECODE(128, FMT_NVFP4);
     else KVQ_DECODE(128, FMT_INT4);
+  }
+  if (head_dim == 256) {
+    if (narrow) hipLaunchKernelGGL((merge_kernel<256>), mgrid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((merge_wide_kernel<256>), mgrid, dim3(256), 0, stream, p);
+  } else {
     if (narrow) hipLaunchKernelGGL((merge_kernel<128>), mgrid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((merge_wide_kernel<128>), mgrid, dim3(256), 0, stream, p);
   }

@@ -3,7 +3,8 @@
 // Formats (see include/kvq.h): NVFP4 = E2M1 elements, one OCP E4M3 scale per
 // 16 head-dim elements of a token row, FP32 per-layer global scale; INT4 =
 // symmetric -7..7 two's-complement nibbles with one FP32 scale per token and
-// head.  Even element in the low nibble.
+// head.  Even element in the low nibble.  FP8 (the comparator) = one OCP E4M3
+// byte per value with one FP32 scale per tensor, V stored by channel.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,6 +13,7 @@
 namespace kvq {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
@@ -19,7 +21,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-enum { FMT_NVFP4 = 1, FMT_INT4 = 2 };
+enum { FMT_NVFP4 = 1, FMT_INT4 = 2, FMT_FP8 = 3 };
 
 // Byte layout of one slab (one page of one KV head).
 struct SlabLayout {
@@ -32,6 +34,15 @@ struct SlabLayout {
 
 __host__ __device__ inline SlabLayout slab_layout(int fmt, int page_size, int head_dim) {
   SlabLayout s;
+  if (fmt == FMT_FP8) {
+    // [K: page_size rows x head_dim bytes][V: head_dim rows x page_size bytes]
+    s.code_row = head_dim;
+    s.scale_row = 0;
+    s.scales_off = (int64_t)page_size * head_dim;
+    s.half = (int64_t)page_size * head_dim;
+    s.slab = 2 * s.half;
+    return s;
+  }
   s.code_row = head_dim / 2;
   s.scale_row = fmt == FMT_NVFP4 ? head_dim / 16 : 4;
   s.scales_off = (int64_t)page_size * s.code_row;

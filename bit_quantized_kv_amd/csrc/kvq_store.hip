@@ -141,6 +141,42 @@ __global__ __launch_bounds__(256) void nvfp4_store_kernel(StoreParams p) {
   half[p.scales_off + off * NB + b] = (uint8_t)cs;
 }
 
+// FP8 E4M3 with one FP32 scale per tensor (the comparator format): K rows
+// are stored by token (D bytes), V by channel (the slab's V section holds D
+// rows of page_size bytes), so thread (i, b) writes 16 contiguous K bytes or
+// 16 single V bytes page_size apart.  code = E4M3(fp32(x / s)) with the sign
+// kept, saturating at 448.
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void fp8_store_kernel(StoreParams p) {
+  const int kv = (int)blockIdx.y >= p.num_kv_heads ? 1 : 0;
+  const int g = (int)blockIdx.y - kv * p.num_kv_heads;
+  const int b = threadIdx.x % (D / 16);
+  const int64_t i = store_token<D>(threadIdx.x);
+  if (i >= p.num_tokens) return;
+  float x[16];
+  Row16<TIn>::load((const TIn*)(kv ? p.v : p.k) + i * p.in_stride + (int64_t)g * D + 16 * b, x);
+  const int32_t slot = p.slots[i];
+  const float s = p.gs[kv];
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 16; e++) {
+    const float y = x[e] / s;
+    const uint32_t code = e4m3_encode(__builtin_fabsf(y)) | ((as_u32(y) >> 24) & 0x80u);
+    w[e / 4] |= code << (8 * (e % 4));
+  }
+  if (slot < 0) return;
+  const int64_t page = slot / p.page_size;
+  const int off = slot % p.page_size;
+  uint8_t* base = p.pool + (page * p.num_kv_heads + g) * p.slab;
+  if (kv == 0) {
+    *(uint4*)(base + (int64_t)off * D + 16 * b) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    uint8_t* col = base + (int64_t)p.page_size * D + (int64_t)(16 * b) * p.page_size + off;
+#pragma unroll
+    for (int e = 0; e < 16; e++) col[(int64_t)e * p.page_size] = (uint8_t)(w[e / 4] >> (8 * (e % 4)));
+  }
+}
+
 // INT4: the D/16 threads of one row reduce the row amax with lane shuffles.
 // q = rint(RN(x / s)) with RN(x / s) from the FMA-corrected quotient; where
 // that quotient lies within two ulps of a rounding boundary (a half-integer)
@@ -366,8 +402,10 @@ hipError_t launch_quantize_store(const StoreParams& p, int fmt, int head_dim, in
   do {                                                                             \
     if (fmt == FMT_NVFP4)                                                          \
       hipLaunchKernelGGL((nvfp4_store_kernel<D, T>), grid, block, 0, stream, p);   \
-    else                                                                           \
+    else if (fmt == FMT_INT4)                                                      \
       hipLaunchKernelGGL((int4_store_kernel<D, T>), grid, block, 0, stream, p);    \
+    else                                                                           \
+      hipLaunchKernelGGL((fp8_store_kernel<D, T>), grid, block, 0, stream, p);     \
   } while (0)
   if (head_dim == 256) {
     if (in_bf16) KVQ_STORE(256, uint16_t); else KVQ_STORE(256, float);

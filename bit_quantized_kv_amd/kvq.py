@@ -14,6 +14,7 @@ import torch
 
 NVFP4 = 1
 INT4_TOKHEAD = 2
+FP8_E4M3 = 3  # the per-tensor FP8 comparator format
 DT_F32 = 0
 DT_BF16 = 1
 
@@ -94,9 +95,9 @@ def kvq_slab_bytes(fmt: int, page_size: int, head_dim: int) -> int:
 
 
 class Cache:
-    """One layer's paged 4-bit cache: a device uint8 pool
-    [num_pages][num_kv_heads][slab] and, for NVFP4, the device float[2]
-    global scales {K, V}."""
+    """One layer's paged cache: a device uint8 pool
+    [num_pages][num_kv_heads][slab] and the device float[2] scales {K, V}
+    (NVFP4 global scales, FP8 per-tensor scales; unused for INT4)."""
 
     def __init__(self, fmt: int, num_pages: int, page_size: int, num_kv_heads: int, head_dim: int,
                  device="cuda", global_scale=(1.0, 1.0), pool: torch.Tensor | None = None):

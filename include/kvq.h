@@ -22,7 +22,13 @@
  *     264 bytes per head and token at head dim 256 ("KV cache in 4 bits: 8.8
  *     instead of 4.7 full sessions on the same four RTX 5090s", section "What
  *     we changed").
- *   Quantization rules (both formats): block/row amax; NVFP4 scale
+ *   KVQ_FMT_FP8_E4M3 (the comparator): one E4M3 byte per value with one FP32
+ *     scale per tensor (K and V of a layer) -- the per-tensor-scaled FP8 cache
+ *     the 0.5625 ratio is measured against ("SGLang's 4-bit KV cache ...",
+ *     section "The 56% survives its own scale, and names the block size").
+ *     code = E4M3(fp32(x / s)) with the sign kept, saturating at 448.  Store
+ *     and decode only (kvq_dequant_prefix and calibration: UNSUPPORTED).
+ *   Quantization rules (4-bit formats): block/row amax; NVFP4 scale
  *   E4M3(fp32(amax / fp32(6 * gs))), elements rounded to nearest-even under the
  *   stored scale fp32(E4M3 * gs), |x| >= 6 saturating; INT4 scale
  *   fp32(amax / 7), q = clamp(rint(fp32(x / s)), -7, 7).  Even element in the
@@ -33,7 +39,9 @@
  *   [K codes: page_size rows of head_dim/2 bytes][K scales]
  *   [V codes: page_size rows of head_dim/2 bytes][V scales]
  * Scales are page_size rows of head_dim/16 E4M3 bytes (NVFP4) or page_size
- * fp32 values (INT4).  Cache token t of a sequence lives in page
+ * fp32 values (INT4).  FP8 slabs are [K: page_size rows of head_dim bytes]
+ * [V: head_dim rows (channels) of page_size bytes], values stored by channel
+ * as in paged-attention value caches.  Cache token t of a sequence lives in page
  * block_table[t / page_size] at row t % page_size; a write slot is
  * page * page_size + row.
  *
@@ -74,7 +82,7 @@ typedef enum {
   KVQ_ERR_HIP = -6          /* a HIP launch failed; see kvq_last_hip_error() */
 } kvq_status;
 
-typedef enum { KVQ_FMT_NVFP4 = 1, KVQ_FMT_INT4_TOKHEAD = 2 } kvq_format;
+typedef enum { KVQ_FMT_NVFP4 = 1, KVQ_FMT_INT4_TOKHEAD = 2, KVQ_FMT_FP8_E4M3 = 3 } kvq_format;
 
 typedef enum { KVQ_DT_F32 = 0, KVQ_DT_BF16 = 1 } kvq_dtype;
 
@@ -87,14 +95,16 @@ typedef struct {
   int32_t head_dim;           /* 128 or 256 */
   void* pool;                 /* device, uint8 [num_pages][num_kv_heads][slab] */
   const float* global_scale;  /* device float[2] = {gs_K, gs_V}, positive and
-                                 finite; NVFP4 only (ignored for INT4) */
+                                 finite; NVFP4 global scales, FP8 per-tensor
+                                 scales (ignored for INT4) */
 } kvq_cache;
 
 /* Bytes of one slab (one page of one KV head, K and V with their scales);
  * 0 for an unknown format or a head_dim not divisible by 16.
  * NVFP4: 2 * page_size * (head_dim/2 + head_dim/16); INT4: 2 * page_size *
  * (head_dim/2 + 4), i.e. 422,400 bytes for a 1,600-token page at head dim
- * 256, the page size "KV cache in 4 bits ..." ("What we changed") prints. */
+ * 256, the page size "KV cache in 4 bits ..." ("What we changed") prints;
+ * FP8: 2 * page_size * head_dim. */
 size_t kvq_slab_bytes(int32_t fmt, int32_t page_size, int32_t head_dim);
 
 /* Quantize-on-write ("SGLang's 4-bit KV cache ...", Figure 2 caption: prefill

@@ -44,7 +44,7 @@ def test_slab_bytes_match_oracle_and_pages(lib, oracle):
     assert kvq.kvq_slab_bytes(2, 1600, 256) == 422400
     assert kvq.kvq_slab_bytes(2, 800, 256) == 211200
     assert kvq.kvq_slab_bytes(1, 16, 256) == 16 * 2 * (128 + 16)
-    assert kvq.kvq_slab_bytes(3, 16, 256) == 0
+    assert kvq.kvq_slab_bytes(7, 16, 256) == 0
 
 
 FAKE = 0x10000  # a 16-byte-aligned host address that is never dereferenced
@@ -62,7 +62,7 @@ def test_quantize_store_validation(lib):
     assert lib.kvq_quantize_store(None, FAKE, FAKE, 1, 1024, FAKE, 4, None) == ERR_NULL
     assert q_store(lib, cache(pool=0)) == ERR_NULL
     assert q_store(lib, cache(gs=0)) == ERR_NULL            # NVFP4 needs global scales
-    assert q_store(lib, cache(fmt=3)) == ERR_UNSUPPORTED
+    assert q_store(lib, cache(fmt=7)) == ERR_UNSUPPORTED
     assert q_store(lib, cache(D=64)) == ERR_UNSUPPORTED
     assert q_store(lib, cache(P=24)) == ERR_UNSUPPORTED
     assert q_store(lib, cache(pages=0)) == ERR_SHAPE
@@ -173,3 +173,15 @@ def test_calibration_validation(lib):
     assert g(ctypes.byref(c), None, None) == ERR_NULL
     assert g(ctypes.byref(c4), FAKE, None) == ERR_UNSUPPORTED
     assert g(ctypes.byref(c), FAKE + 1, None) == ERR_ALIGN
+
+
+def test_fp8_comparator_format(lib, oracle):
+    for P in (16, 48):
+        for D in (128, 256):
+            assert kvq.kvq_slab_bytes(3, P, D) == oracle.slab_bytes(3, P, D) == 2 * P * D
+    c = cache(fmt=3)
+    assert lib.kvq_dequant_prefix(ctypes.byref(c), FAKE, 16, FAKE, FAKE, 1024, None) == ERR_UNSUPPORTED
+    assert lib.kvq_calibrate_amax(ctypes.byref(c), FAKE, FAKE, 1, 1024, 4, FAKE, None) == ERR_UNSUPPORTED
+    c0 = cache(fmt=3, gs=0)
+    assert q_store(lib, c0) == ERR_NULL                      # the per-tensor scales are required
+    assert q_store(lib, c, n=0) == OK

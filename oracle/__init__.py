@@ -66,7 +66,8 @@ def _load():
         "kvqo_int4_dequant_row": (None, [P, f32, i32, P]),
         "kvqo_slab_bytes": (sz, [i32, i32, i32]),
         "kvqo_token_head_bytes": (sz, [i32, i32]),
-        "kvqo_quantize_store": (None, [i32, P, i32, i32, i32, P, P, P, i32, P]),
+        "kvqo_quantize_store": (None, [i32, P, i32, i32, i32, P, P, P, i32, P, i32]),
+        "kvqo_hadamard_row": (None, [P, i32]),
         "kvqo_decode_attention": (None, [i32, P, i32, i32, i32, P, P, i32, P, i32, P, i32, f64, i64, P, P]),
         "kvqo_dequant_prefix": (None, [i32, P, i32, i32, i32, P, P, i64, P, P, i64]),
         "kvqo_num_threads": (i32, []),
@@ -163,6 +164,17 @@ def amax(x) -> float:
     return float(_load().kvqo_amax(_ptr(a), a.size))
 
 
+def hadamard(x) -> np.ndarray:
+    """R x for every row of x (fp32, last axis D): R = H_D / sqrt(D), the fast
+    transform's stages in order, the scale applied last (see kvqo_hadamard_row)."""
+    a = _f32(x).copy()
+    D = a.shape[-1]
+    rows = a.reshape(-1, D)
+    for r in rows:
+        _load().kvqo_hadamard_row(r.ctypes.data_as(ctypes.c_void_p), D)
+    return rows.reshape(a.shape)
+
+
 def fp8_encode(x: float, scale: float) -> int:
     """FP8 (E4M3, per-tensor scale) code of x: E4M3 of fp32(x / scale), sign kept."""
     return int(_load().kvqo_fp8_encode(float(x), float(scale)))
@@ -185,8 +197,9 @@ class Pool:
     """One layer's paged cache on the host: uint8 [num_pages][Hkv][slab]."""
 
     def __init__(self, fmt: int, num_pages: int, page_size: int, num_kv_heads: int, head_dim: int,
-                 global_scale=(1.0, 1.0), fill: int = 0):
+                 global_scale=(1.0, 1.0), fill: int = 0, rotated: bool = False):
         self.fmt, self.num_pages, self.page_size = fmt, num_pages, page_size
+        self.rotated = bool(rotated)  # rows Hadamard-rotated before quantization
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
         self.slab = slab_bytes(fmt, page_size, head_dim)
         self.data = np.full((num_pages, num_kv_heads, self.slab), fill, np.uint8)
@@ -198,7 +211,7 @@ class Pool:
         n = slots.shape[0]
         assert k.shape == (n, self.num_kv_heads, self.head_dim) and v.shape == k.shape
         _load().kvqo_quantize_store(self.fmt, _ptr(self.data), self.page_size, self.num_kv_heads, self.head_dim,
-                                    _ptr(self.gs), _ptr(k), _ptr(v), n, _ptr(slots))
+                                    _ptr(self.gs), _ptr(k), _ptr(v), n, _ptr(slots), int(self.rotated))
 
     def decode_attention(self, q, block_table, seq_lens, sm_scale: float | None = None, split_tokens: int = 0):
         """q: [B][Hq][D] (bf16 values widened to fp32).  Returns (out fp64

@@ -279,13 +279,37 @@ static rowptr locate(uint8_t* pool, int fmt, int P, int Hkv, int D, int64_t page
   return r;
 }
 
+/* Orthogonal Walsh-Hadamard rotation of one row, in place, in fp32 ("SGLang's
+ * 4-bit KV cache ...", section "Against what this site already established":
+ * rotate every vector by an orthogonal matrix before quantizing it, as
+ * TurboQuant argues and as another engine's 4-bit cache does with a fixed FP32
+ * D256 Hadamard rotation).  Reading: R = H_D / sqrt(D) with H_D the Sylvester
+ * Hadamard matrix (H_1 = 1, H_2n = [[H_n, H_n], [H_n, -H_n]]), computed by the
+ * standard fast transform -- stages h = 1, 2, 4, ..., D/2, each replacing the
+ * pair (x_i, x_{i+h}) (bit h of i clear) by (x_i + x_{i+h}, x_i - x_{i+h}) in
+ * fp32 -- and the scale fp32(1 / sqrt(D)) applied last.  R is symmetric and
+ * its own inverse. */
+void kvqo_hadamard_row(float* x, int D) {
+  for (int h = 1; h < D; h <<= 1) {
+    for (int i = 0; i < D; i++) {
+      if (i & h) continue;
+      const float a = x[i], b = x[i + h];
+      x[i] = a + b;
+      x[i + h] = a - b;
+    }
+  }
+  const float s = (float)(1.0 / sqrt((double)D));
+  for (int i = 0; i < D; i++) x[i] = x[i] * s;
+}
+
 /* Quantize-on-write: for token i with slot = slot_mapping[i] >= 0, page =
  * slot / P and offset = slot % P; each KV head's K and V row is quantized
  * and stored there.  A negative slot skips the token.  k, v are
  * [n_tok][Hkv][D] fp32 (bf16 inputs widened exactly by the caller);
- * gs = {gs_K, gs_V} (NVFP4: global scales; FP8: the per-tensor scales). */
+ * gs = {gs_K, gs_V} (NVFP4: global scales; FP8: the per-tensor scales).
+ * rotate != 0: each row is Hadamard-rotated (kvqo_hadamard_row) first. */
 void kvqo_quantize_store(int fmt, uint8_t* pool, int P, int Hkv, int D, const float* gs, const float* k,
-                         const float* v, int n_tok, const int32_t* slot_mapping) {
+                         const float* v, int n_tok, const int32_t* slot_mapping, int rotate) {
 #pragma omp parallel for schedule(static)
   for (int i = 0; i < n_tok; i++) {
     int32_t slot = slot_mapping[i];
@@ -295,6 +319,12 @@ void kvqo_quantize_store(int fmt, uint8_t* pool, int P, int Hkv, int D, const fl
     for (int g = 0; g < Hkv; g++) {
       for (int kv = 0; kv < 2; kv++) {
         const float* x = (kv ? v : k) + ((size_t)i * Hkv + g) * D;
+        float xr[512];
+        if (rotate) {
+          memcpy(xr, x, sizeof(float) * (size_t)D);
+          kvqo_hadamard_row(xr, D);
+          x = xr;
+        }
         if (fmt == KVQO_FP8) {
           uint8_t* base = pool + ((size_t)page * Hkv + g) * kvqo_slab_bytes(fmt, P, D);
           for (int c = 0; c < D; c++) base[fp8_offset(P, D, off, c, kv)] = (uint8_t)kvqo_fp8_encode(x[c], gs[kv]);

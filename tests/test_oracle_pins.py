@@ -566,3 +566,60 @@ def test_fp8_layout_keys_by_row_values_by_channel(oracle):
     assert slab[9 * D + 5] == 0x40                  # K: row 9, byte 5
     assert slab[P * D + 7 * P + 9] == 0xB0          # V: channel 7's row, byte 9
     assert np.count_nonzero(pool.data) == 2
+
+
+# ----------------------------------------------------------------- Hadamard rotation
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_hadamard_matches_library_matrix(oracle, D):
+    import scipy.linalg
+    x = np.random.default_rng(D).standard_normal((5, D)).astype(np.float32)
+    ref = x.astype(np.float64) @ scipy.linalg.hadamard(D).T.astype(np.float64) / math.sqrt(D)
+    got = oracle.hadamard(x)
+    assert np.abs(got - ref).max() <= 4e-6 * np.abs(ref).max()
+    # orthogonal and its own inverse
+    assert np.abs(oracle.hadamard(got) - x).max() <= 1e-5 * np.abs(x).max()
+    np.testing.assert_allclose(np.linalg.norm(got, axis=1), np.linalg.norm(x, axis=1), rtol=1e-5)
+
+
+def test_hadamard_closed_forms(oracle):
+    import scipy.linalg
+    H = scipy.linalg.hadamard(256)
+    for k in (0, 1, 77, 255):
+        e = np.zeros(256, np.float32)
+        e[k] = 1.0
+        assert np.array_equal(oracle.hadamard(e), (H[:, k] / 16.0).astype(np.float32))   # exact: +-1/16
+    assert np.array_equal(oracle.hadamard(np.full(256, 3.0, np.float32)), np.eye(256, dtype=np.float32)[0] * 48.0)
+
+
+def test_rotated_store_is_store_of_rotated_rows(oracle):
+    k, v = inputs.kv_outlier_channels(5, 0, 40, 2, 256)
+    slots = np.arange(40, dtype=np.int32)
+    for fmt in (1, 2, 3):
+        a = oracle.Pool(fmt, 3, 16, 2, 256, global_scale=(0.5, 0.25), rotated=True)
+        a.quantize_store(k, v, slots)
+        b = oracle.Pool(fmt, 3, 16, 2, 256, global_scale=(0.5, 0.25))
+        b.quantize_store(oracle.hadamard(k), oracle.hadamard(v), slots)
+        assert np.array_equal(a.data, b.data), fmt
+
+
+def test_rotation_improves_outlier_quality(oracle):
+    # A format property (no GPU involved): with a few x8 outlier channels the
+    # rotated 4-bit cache is closer to unquantized attention than the plain one.
+    D, Hkv, G, P, L = 256, 1, 4, 16, 512
+    k, v = inputs.kv_outlier_channels(1, 0, L, Hkv, D)
+    q = inputs.query(1, 99, 1, Hkv * G, D)
+    bt = np.arange(L // P, dtype=np.int32)[None]
+    full = _torch_attention(q[0].astype(np.float64), k.astype(np.float64), v.astype(np.float64), G, 1 / 16)[0]
+    for fmt in (1, 2):
+        plain = oracle.Pool(fmt, L // P, P, Hkv, D)
+        plain.quantize_store(k, v, np.arange(L, dtype=np.int32))
+        o_plain, _ = plain.decode_attention(q, bt, np.array([L], np.int32))
+        rot = oracle.Pool(fmt, L // P, P, Hkv, D, rotated=True)
+        rot.quantize_store(k, v, np.arange(L, dtype=np.int32))
+        o_rot, _ = rot.decode_attention(oracle.hadamard(q), bt, np.array([L], np.int32))
+        o_rot = oracle.hadamard(o_rot.astype(np.float32)).astype(np.float64)
+        def cos(a, b):
+            return float(np.sum(a * b) / (np.linalg.norm(a) * np.linalg.norm(b)))
+        c_plain, c_rot = cos(o_plain[0], full), cos(o_rot[0], full)
+        assert c_rot > c_plain, (fmt, c_plain, c_rot)

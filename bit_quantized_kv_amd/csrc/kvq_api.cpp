@@ -30,8 +30,11 @@ kvq_status check_cache(const kvq_cache* c) {
   if (c->head_dim != 128 && c->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
   if (c->page_size % 16 != 0) return KVQ_ERR_UNSUPPORTED;
   if (!aligned16(c->pool)) return KVQ_ERR_ALIGN;
+  if (c->flags & ~KVQ_FLAG_HADAMARD) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
+
+float rotation_scale(int32_t head_dim) { return (float)(1.0 / __builtin_sqrt((double)head_dim)); }
 
 kvq_status hip_status(hipError_t e) {
   if (e == hipSuccess) return KVQ_OK;
@@ -128,6 +131,8 @@ kvq_status kvq_quantize_store(const kvq_cache* cache, const void* k, const void*
   p.num_tokens = num_tokens;
   p.page_size = cache->page_size;
   p.num_kv_heads = cache->num_kv_heads;
+  p.rotate = (cache->flags & KVQ_FLAG_HADAMARD) != 0;
+  p.rot_scale = rotation_scale(cache->head_dim);
   return hip_status(kvq::launch_quantize_store(p, cache->fmt, cache->head_dim, in_dtype == KVQ_DT_BF16,
                                                (hipStream_t)stream));
 }
@@ -247,6 +252,8 @@ kvq_status kvq_calibrate_amax(const kvq_cache* cache, const void* k, const void*
   p.in_stride = in_token_stride;
   p.num_tokens = num_tokens;
   p.num_kv_heads = cache->num_kv_heads;
+  p.rotate = (cache->flags & KVQ_FLAG_HADAMARD) != 0;
+  p.rot_scale = rotation_scale(cache->head_dim);
   return hip_status(kvq::launch_calibrate_amax(p, cache->head_dim, in_dtype == KVQ_DT_BF16, running_amax,
                                                (hipStream_t)stream));
 }
@@ -258,6 +265,29 @@ kvq_status kvq_calibrate_global_scale(const kvq_cache* cache, const float* runni
   if (running_amax == nullptr) return KVQ_ERR_NULL;
   if (((uintptr_t)running_amax & 3u) || ((uintptr_t)cache->global_scale & 3u)) return KVQ_ERR_ALIGN;
   return hip_status(kvq::launch_global_scale(running_amax, (float*)cache->global_scale, (hipStream_t)stream));
+}
+
+kvq_status kvq_hadamard_rotate(const void* in, int32_t in_dtype, int64_t in_row_stride, void* out, int32_t out_dtype,
+                               int64_t out_row_stride, int32_t rows, int32_t head_dim, void* stream) {
+  if (rows < 0) return KVQ_ERR_SHAPE;
+  if (head_dim != 128 && head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  if ((in_dtype != KVQ_DT_F32 && in_dtype != KVQ_DT_BF16) || (out_dtype != KVQ_DT_F32 && out_dtype != KVQ_DT_BF16))
+    return KVQ_ERR_UNSUPPORTED;
+  if (rows == 0) return KVQ_OK;
+  if (in == nullptr || out == nullptr) return KVQ_ERR_NULL;
+  if (in_row_stride < head_dim || out_row_stride < head_dim) return KVQ_ERR_SHAPE;
+  const int64_t ies = in_dtype == KVQ_DT_F32 ? 4 : 2, oes = out_dtype == KVQ_DT_F32 ? 4 : 2;
+  if (!aligned16(in) || !aligned16(out) || (in_row_stride * ies) % 16 || (out_row_stride * oes) % 16)
+    return KVQ_ERR_ALIGN;
+  kvq::RotateParams p;
+  p.in = in;
+  p.out = out;
+  p.in_stride = in_row_stride;
+  p.out_stride = out_row_stride;
+  p.rows = rows;
+  p.scale = rotation_scale(head_dim);
+  return hip_status(kvq::launch_hadamard(p, head_dim, in_dtype == KVQ_DT_BF16, out_dtype == KVQ_DT_BF16,
+                                         (hipStream_t)stream));
 }
 
 kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t num_workgroups, void* stream) {

@@ -12,13 +12,23 @@ constexpr int kDecodeWaves = 4;
 
 struct StoreParams {
   uint8_t* pool;
-  const float* gs;  // {gs_K, gs_V} (NVFP4)
+  const float* gs;  // {gs_K, gs_V} (NVFP4 global / FP8 per-tensor scales)
   const void* k;
   const void* v;
   const int32_t* slots;
   int64_t in_stride;  // elements between tokens
   int64_t slab, half, scales_off;
   int32_t num_tokens, page_size, num_kv_heads;
+  int32_t rotate;     // Hadamard-rotate each row before quantizing
+  float rot_scale;    // fp32(1 / sqrt(head_dim))
+};
+
+struct RotateParams {
+  const void* in;
+  void* out;
+  int64_t in_stride, out_stride;  // elements between rows
+  int32_t rows;
+  float scale;  // fp32(1 / sqrt(head_dim))
 };
 
 struct DequantParams {
@@ -53,6 +63,7 @@ hipError_t launch_quantize_store(const StoreParams& p, int fmt, int head_dim, in
 hipError_t launch_dequant_prefix(const DequantParams& p, int fmt, int head_dim, hipStream_t stream);
 hipError_t launch_calibrate_amax(const StoreParams& p, int head_dim, int in_bf16, float* running, hipStream_t stream);
 hipError_t launch_global_scale(const float* running, float* gs, hipStream_t stream);
+hipError_t launch_hadamard(const RotateParams& p, int head_dim, int in_bf16, int out_bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
 

@@ -55,6 +55,38 @@ struct Row16<uint16_t> {  // bf16 bit patterns, widened exactly
   }
 };
 
+// Orthogonal Hadamard rotation of one row held as 16 elements per lane by
+// the D/16 consecutive lanes of the row (lane b holds elements 16b..16b+15):
+// the fast transform's stages h = 1, 2, 4, 8 inside the lane, then h = 16,
+// 32, ... across lanes (partner lane b ^ (h/16)); each stage maps the pair
+// (x_i, x_{i+h}) to (x_i + x_{i+h}, x_i - x_{i+h}) in fp32, and the scale
+// 1/sqrt(D) is applied last -- the same operations, on the same operands, as
+// a scalar loop over the stages, so the rotated row is bit-reproducible.
+template <int D>
+__device__ inline void hadamard_row(float x[16], int b, float scale) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      if (i & h) continue;
+      const float a = x[i], c = x[i + h];
+      x[i] = a + c;
+      x[i + h] = a - c;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < D / 16; m <<= 1) {
+    const bool upper = (b & m) != 0;
+#pragma unroll
+    for (int e = 0; e < 16; e++) {
+      const float partner = __shfl_xor(x[e], m, 64);
+      x[e] = upper ? partner - x[e] : x[e] + partner;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; e++) x[e] *= scale;
+}
+
 // A workgroup takes kStoreTokens(D) = 256 / (D/16) consecutive input tokens of
 // one (K|V, head) pair, blockIdx.y = kv * num_kv_heads + head; thread (i, b)
 // quantizes block b (16 head-dim elements) of token t0 + i.  No 64-bit
@@ -109,6 +141,7 @@ __global__ __launch_bounds__(256) void nvfp4_store_kernel(StoreParams p) {
   float x[16];
   const TIn* src = (const TIn*)(kv ? p.v : p.k) + i * p.in_stride + (int64_t)g * D + 16 * b;
   Row16<TIn>::load(src, x);
+  if (p.rotate) hadamard_row<D>(x, b, p.rot_scale);
   const int32_t slot = p.slots[i];
 
   float amax = 0.0f;
@@ -155,6 +188,7 @@ __global__ __launch_bounds__(256) void fp8_store_kernel(StoreParams p) {
   if (i >= p.num_tokens) return;
   float x[16];
   Row16<TIn>::load((const TIn*)(kv ? p.v : p.k) + i * p.in_stride + (int64_t)g * D + 16 * b, x);
+  if (p.rotate) hadamard_row<D>(x, b, p.rot_scale);
   const int32_t slot = p.slots[i];
   const float s = p.gs[kv];
   uint32_t w[4] = {0u, 0u, 0u, 0u};
@@ -193,6 +227,7 @@ __global__ __launch_bounds__(256) void int4_store_kernel(StoreParams p) {
   float x[16];
   const TIn* src = (const TIn*)(kv ? p.v : p.k) + i * p.in_stride + (int64_t)g * D + 16 * b;
   Row16<TIn>::load(src, x);
+  if (p.rotate) hadamard_row<D>(x, b, p.rot_scale);
   const int32_t slot = p.slots[i];
   float amax = 0.0f;
 #pragma unroll
@@ -251,6 +286,7 @@ __global__ __launch_bounds__(256) void amax_kernel(StoreParams p, float* running
   if (i < p.num_tokens) {
     float x[16];
     Row16<TIn>::load((const TIn*)(kv ? p.v : p.k) + i * p.in_stride + (int64_t)g * D + 16 * b, x);
+    if (p.rotate) hadamard_row<D>(x, b, p.rot_scale);  // a rotated cache stores rotated rows
 #pragma unroll
     for (int e = 0; e < 16; e++) amax = fmaxf(amax, __builtin_fabsf(x[e]));
   }
@@ -288,6 +324,48 @@ hipError_t launch_calibrate_amax(const StoreParams& p, int head_dim, int in_bf16
 
 hipError_t launch_global_scale(const float* running, float* gs, hipStream_t stream) {
   hipLaunchKernelGGL(global_scale_kernel, dim3(1), dim3(64), 0, stream, running, gs);
+  return hipGetLastError();
+}
+
+// Standalone rotation of rows (queries before decode over a rotated cache,
+// and the decode output back): thread per 16-element block, rows of D/16
+// consecutive lanes.
+template <int D, typename TIn, bool OUT_BF16>
+__global__ __launch_bounds__(256) void hadamard_kernel(RotateParams p) {
+  constexpr int NB = D / 16;
+  const int b = threadIdx.x % NB;
+  const int64_t row = (int64_t)blockIdx.x * (256 / NB) + threadIdx.x / NB;
+  if (row >= p.rows) return;  // whole rows
+  float x[16];
+  Row16<TIn>::load((const TIn*)p.in + row * p.in_stride + 16 * b, x);
+  hadamard_row<D>(x, b, p.scale);
+  if (OUT_BF16) {
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) w[e] = bf16x2_rne((float2_t){x[2 * e], x[2 * e + 1]});
+    uint4* dst = (uint4*)((uint16_t*)p.out + row * p.out_stride + 16 * b);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {
+    float4* dst = (float4*)((float*)p.out + row * p.out_stride + 16 * b);
+#pragma unroll
+    for (int e = 0; e < 4; e++) dst[e] = make_float4(x[4 * e], x[4 * e + 1], x[4 * e + 2], x[4 * e + 3]);
+  }
+}
+
+hipError_t launch_hadamard(const RotateParams& p, int head_dim, int in_bf16, int out_bf16, hipStream_t stream) {
+  const int rpw = 256 / (head_dim / 16);
+  const dim3 grid((unsigned)((p.rows + rpw - 1) / rpw)), block(256);
+#define KVQ_ROT(D)                                                                                         \
+  do {                                                                                                     \
+    if (in_bf16 && out_bf16) hipLaunchKernelGGL((hadamard_kernel<D, uint16_t, true>), grid, block, 0, stream, p); \
+    else if (in_bf16) hipLaunchKernelGGL((hadamard_kernel<D, uint16_t, false>), grid, block, 0, stream, p);     \
+    else if (out_bf16) hipLaunchKernelGGL((hadamard_kernel<D, float, true>), grid, block, 0, stream, p);        \
+    else hipLaunchKernelGGL((hadamard_kernel<D, float, false>), grid, block, 0, stream, p);                     \
+  } while (0)
+  if (head_dim == 256) KVQ_ROT(256);
+  else KVQ_ROT(128);
+#undef KVQ_ROT
   return hipGetLastError();
 }
 

@@ -38,7 +38,11 @@ class kvq_cache(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("pool", ctypes.c_void_p),
         ("global_scale", ctypes.c_void_p),
+        ("flags", ctypes.c_int32),
     ]
+
+
+FLAG_HADAMARD = 1  # rows Hadamard-rotated before quantization
 
 
 def lib():
@@ -60,6 +64,7 @@ def lib():
         "kvq_stream_read": (i32, [P, sz, P, i32, P]),
         "kvq_calibrate_amax": (i32, [C, P, P, i32, i64, i32, P, P]),
         "kvq_calibrate_global_scale": (i32, [C, P, P]),
+        "kvq_hadamard_rotate": (i32, [P, i32, i64, P, i32, i64, i32, i32, P]),
         "kvq_status_string": (ctypes.c_char_p, [i32]),
         "kvq_last_hip_error": (i32, []),
     }
@@ -100,8 +105,9 @@ class Cache:
     (NVFP4 global scales, FP8 per-tensor scales; unused for INT4)."""
 
     def __init__(self, fmt: int, num_pages: int, page_size: int, num_kv_heads: int, head_dim: int,
-                 device="cuda", global_scale=(1.0, 1.0), pool: torch.Tensor | None = None):
+                 device="cuda", global_scale=(1.0, 1.0), pool: torch.Tensor | None = None, rotated: bool = False):
         self.fmt, self.num_pages, self.page_size = fmt, num_pages, page_size
+        self.flags = FLAG_HADAMARD if rotated else 0
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
         self.slab = kvq_slab_bytes(fmt, page_size, head_dim)
         if pool is None:
@@ -111,7 +117,7 @@ class Cache:
 
     def desc(self) -> kvq_cache:
         return kvq_cache(self.fmt, self.num_pages, self.page_size, self.num_kv_heads, self.head_dim,
-                         self.pool.data_ptr(), self.global_scale.data_ptr())
+                         self.pool.data_ptr(), self.global_scale.data_ptr(), self.flags)
 
 
 def _desc(cache):
@@ -204,3 +210,20 @@ def kvq_calibrate_global_scale(cache: Cache, running_amax: torch.Tensor, stream=
     d = cache.desc()
     _check("kvq_calibrate_global_scale", lib().kvq_calibrate_global_scale(ctypes.byref(d), _ptr(running_amax),
                                                                           _stream(stream)))
+
+
+def kvq_hadamard_rotate(x: torch.Tensor, out: torch.Tensor | None = None, out_dtype: torch.dtype | None = None,
+                        stream=None) -> torch.Tensor:
+    """R x over the last axis (head_dim 128 or 256) of a device tensor whose
+    rows are contiguous; returns out (same shape, out_dtype or x.dtype)."""
+    D = x.shape[-1]
+    xr = x.reshape(-1, D)
+    assert xr.stride(1) == 1
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    orr = out.reshape(-1, D)
+    dt = {torch.float32: DT_F32, torch.bfloat16: DT_BF16}
+    _check("kvq_hadamard_rotate", lib().kvq_hadamard_rotate(_ptr(xr), dt[x.dtype], xr.stride(0), _ptr(orr),
+                                                            dt[out.dtype], orr.stride(0), xr.shape[0], D,
+                                                            _stream(stream)))
+    return out

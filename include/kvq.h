@@ -97,7 +97,21 @@ typedef struct {
   const float* global_scale;  /* device float[2] = {gs_K, gs_V}, positive and
                                  finite; NVFP4 global scales, FP8 per-tensor
                                  scales (ignored for INT4) */
+  int32_t flags;              /* 0, or KVQ_FLAG_HADAMARD */
 } kvq_cache;
+
+/* Rotated cache ("SGLang's 4-bit KV cache ...", section "Against what this
+ * site already established": rotate every vector by an orthogonal matrix
+ * before quantizing it, as TurboQuant argues; another engine's 4-bit cache
+ * applies a fixed FP32 D256 Hadamard rotation to both operands).  With this
+ * flag every K and V row is multiplied by R = H_D / sqrt(D) (Sylvester
+ * Hadamard matrix; the fast transform's stages in order in fp32, the scale
+ * last) before it is quantized; calibration sees the rotated rows and prefix
+ * dequantization returns them.  Decode is unchanged: since R is orthogonal
+ * and its own inverse, attention over the rotated cache with the rotated
+ * query R q yields R o, so callers pass R q (kvq_hadamard_rotate) and rotate
+ * the output back the same way. */
+#define KVQ_FLAG_HADAMARD 1
 
 /* Bytes of one slab (one page of one KV head, K and V with their scales);
  * 0 for an unknown format or a head_dim not divisible by 16.
@@ -193,6 +207,15 @@ kvq_status kvq_dequant_prefix(const kvq_cache* cache, const int32_t* block_table
 kvq_status kvq_calibrate_amax(const kvq_cache* cache, const void* k, const void* v, int32_t in_dtype,
                               int64_t in_token_stride, int32_t num_tokens, float* running_amax, void* stream);
 kvq_status kvq_calibrate_global_scale(const kvq_cache* cache, const float* running_amax, void* stream);
+
+/* out_row = R in_row (R = H_D / sqrt(D), as KVQ_FLAG_HADAMARD) for `rows`
+ * rows of head_dim elements: queries before decode over a rotated cache, and
+ * the decode output back (R is its own inverse).  in_dtype / out_dtype
+ * KVQ_DT_F32 or KVQ_DT_BF16 (bf16 output rounded to nearest even); strides in
+ * elements, rows 16-byte aligned; head_dim 128 or 256.  in and out may be the
+ * same buffer when the dtypes and strides match. */
+kvq_status kvq_hadamard_rotate(const void* in, int32_t in_dtype, int64_t in_row_stride, void* out, int32_t out_dtype,
+                               int64_t out_row_stride, int32_t rows, int32_t head_dim, void* stream);
 
 /* Measurement aid, not part of the cache path: a plain streaming read of
  * `bytes` bytes of device memory (the practical HBM read ceiling against which

@@ -185,3 +185,20 @@ def test_fp8_comparator_format(lib, oracle):
     c0 = cache(fmt=3, gs=0)
     assert q_store(lib, c0) == ERR_NULL                      # the per-tensor scales are required
     assert q_store(lib, c, n=0) == OK
+
+
+def test_rotation_flag_and_rotate_validation(lib):
+    c = cache()
+    c.flags = 2                                                   # unknown flag bit
+    assert q_store(lib, c) == ERR_UNSUPPORTED
+    c.flags = kvq.FLAG_HADAMARD
+    assert q_store(lib, c, n=0) == OK
+    f = lib.kvq_hadamard_rotate
+    assert f(FAKE, 1, 256, FAKE, 0, 256, 0, 256, None) == OK        # no rows
+    assert f(FAKE, 1, 256, FAKE, 0, 256, -1, 256, None) == ERR_SHAPE
+    assert f(FAKE, 1, 256, FAKE, 0, 256, 4, 64, None) == ERR_UNSUPPORTED
+    assert f(FAKE, 5, 256, FAKE, 0, 256, 4, 256, None) == ERR_UNSUPPORTED
+    assert f(None, 1, 256, FAKE, 0, 256, 4, 256, None) == ERR_NULL
+    assert f(FAKE, 1, 128, FAKE, 0, 256, 4, 256, None) == ERR_SHAPE
+    assert f(FAKE, 1, 260, FAKE, 0, 260, 4, 256, None) == ERR_ALIGN
+    assert f(FAKE + 4, 1, 256, FAKE, 0, 256, 4, 256, None) == ERR_ALIGN

@@ -1,0 +1,82 @@
+"""GPU parity of the Hadamard-rotated cache through the C ABI: the standalone
+rotation bit for bit (fp32 out; bf16 out as the round-to-nearest-even of the
+oracle's fp32 rotation), rotated stores bit for bit for all three formats,
+and decode over a rotated cache (rotated query in, output rotated back)
+against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_quantized_kv_amd import inputs, kvq
+from gpu_cases import check_attention
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_rotation_kernel_bitexact(D):
+    print(f"case: rotation kernel D {D}", flush=True)
+    rng = np.random.default_rng(D)
+    x = (rng.standard_normal((77, D)) * np.exp(rng.standard_normal(D))).astype(np.float32)
+    x[3] = 0.0
+    x[5, :7] = -0.0
+    ref = oracle.hadamard(x)
+    xd = torch.from_numpy(x).cuda()
+    got = kvq.kvq_hadamard_rotate(xd).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    gotb = kvq.kvq_hadamard_rotate(xd, out_dtype=torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16)
+    refb = np.array([[oracle.bf16_rne(float(v)) for v in row] for row in ref], np.uint16)
+    assert np.array_equal(gotb, refb)
+    # bf16 input, strided rows (a [rows][2][D] tensor's first half)
+    xb = torch.from_numpy(x).cuda().to(torch.bfloat16)
+    wide = torch.zeros((77, 2, D), dtype=torch.bfloat16, device="cuda")
+    wide[:, 0] = xb
+    out = torch.empty((77, D), dtype=torch.float32, device="cuda")
+    import ctypes
+    st = kvq.lib().kvq_hadamard_rotate(ctypes.c_void_p(wide.data_ptr()), 1, 2 * D, ctypes.c_void_p(out.data_ptr()), 0,
+                                       D, 77, D, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), oracle.hadamard(xb.float().cpu().numpy()).view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt,G,lens,kind,dtype,gs", [
+    (1, 6, [300, 47, 1], "outliers", torch.bfloat16, (1.0, 1.0)),
+    (1, 4, [129], "lognormal", torch.float32, (0.37, 2.5)),
+    (2, 6, [300, 47, 1], "outliers", torch.bfloat16, (1.0, 1.0)),
+    (3, 6, [200, 33], "lognormal", torch.bfloat16, (0.05, 0.04)),
+])
+def test_rotated_cache_store_and_decode(fmt, G, lens, kind, dtype, gs):
+    print(f"case: rotated cache fmt {fmt} G {G} lens {lens} {kind} {dtype}", flush=True)
+    D, Hkv, P = 256, 2, 16
+    lens_np = np.array(lens, np.int32)
+    B = len(lens)
+    pps = -(-max(lens) // P)
+    num_pages = B * pps + 2
+    bt = inputs.page_tables(77, B, pps, num_pages, shuffled=True)
+    cache = kvq.Cache(fmt, num_pages, P, Hkv, D, device="cuda", global_scale=gs, rotated=True)
+    cache.pool.fill_(0xFF)
+    ref = oracle.Pool(fmt, num_pages, P, Hkv, D, global_scale=gs, fill=0xFF, rotated=True)
+    gen = {"outliers": inputs.kv_outlier_channels, "lognormal": inputs.kv_lognormal_channels}[kind]
+    for b, L in enumerate(lens):
+        k, v = gen(77, b, L, Hkv, D)
+        kd, vd = torch.from_numpy(k).cuda().to(dtype), torch.from_numpy(v).cuda().to(dtype)
+        slots = inputs.slots_for(bt, P, b, 0, L)
+        kvq.kvq_quantize_store(cache, kd, vd, torch.from_numpy(slots).cuda())
+        ref.quantize_store(kd.float().cpu().numpy(), vd.float().cpu().numpy(), slots)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.pool.cpu().numpy(), ref.data)
+    q = inputs.query(77, 5, B, Hkv * G, D)
+    qd = torch.from_numpy(q).cuda().to(torch.bfloat16)
+    qr = kvq.kvq_hadamard_rotate(qd)                   # bf16 R q
+    out_r = kvq.kvq_decode_attention(cache, qr, torch.from_numpy(bt).cuda(), torch.from_numpy(lens_np).cuda(),
+                                     max(lens), out_dtype=torch.float32)
+    o = kvq.kvq_hadamard_rotate(out_r).cpu().numpy()    # back to the unrotated space
+    torch.cuda.synchronize()
+    qr_host = qr.float().cpu().numpy()
+    ref_r, _ = ref.decode_attention(qr_host, bt, lens_np)
+    ref_o = oracle.hadamard(ref_r.astype(np.float32)).astype(np.float64)
+    s = max(1.0, float(np.abs(ref_o).max()))
+    check_attention(out_r.cpu().numpy() / s, ref_r / s, lens_np, label="rotated space")
+    check_attention(o / s, ref_o / s, lens_np, label="unrotated")

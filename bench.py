@@ -49,6 +49,9 @@ WORKLOADS = {
     "int4_220k": dict(fmt=2, batch=8, ctx=220000, page=1600, shuffled=False, kind="student_t",
                       desc="INT4 per-token-head, batch 8, context 220,000, 1,600-token pages (last page half "
                            "full); 16 layers assumed"),
+    "rot_32k": dict(fmt=1, batch=32, ctx=32768, page=16, shuffled=False, kind="lognormal", rotated=True,
+                    desc="the 32K headline shape with a Hadamard-rotated NVFP4 cache: rotated stores, R q in, "
+                         "R o rotated back (the decode call here includes both rotations)"),
     "fp8_32k": dict(fmt=3, batch=32, ctx=32768, page=16, shuffled=False, kind="lognormal",
                     desc="comparator: the 32K headline shape with an FP8 E4M3 per-tensor cache (512 B per "
                          "token and head against NVFP4's 288 B)"),
@@ -201,7 +204,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ctx32k", choices=sorted(WORKLOADS))
-    ap.add_argument("--secondary", default="ctx160k,ctx1m,int4_220k,fp8_32k",
+    ap.add_argument("--secondary", default="ctx160k,ctx1m,int4_220k,fp8_32k,rot_32k",
                     help="comma-separated extra workloads to report ('' for none)")
     ap.add_argument("--secondary-steps", type=int, default=5)
     ap.add_argument("--layers", type=int, default=LAYERS)
@@ -226,7 +229,7 @@ class Layer:
         B, L, P = w["batch"], w["ctx"], w["page"]
         self.pages_per_seq = -(-L // P)
         num_pages = B * self.pages_per_seq
-        self.cache = kvq.Cache(w["fmt"], num_pages, P, HKV, D, device=dev)
+        self.cache = kvq.Cache(w["fmt"], num_pages, P, HKV, D, device=dev, rotated=w.get("rotated", False))
         self.bt = bt
         self.lens = torch.full((B,), L, dtype=torch.int32, device=dev)
         g = torch.Generator(device=dev)
@@ -240,6 +243,10 @@ class Layer:
         last = L - 1
         self.slots_new = (bt[:, last // P] * P + last % P).to(torch.int32).contiguous()
         self.out = torch.empty((B, HQ, D), dtype=torch.bfloat16, device=dev)
+        if w.get("rotated"):
+            # rotated cache: R q in, R o out (fp32), rotated back into out
+            self.q_rot = torch.empty_like(self.q)
+            self.out_rot = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
 
 
 def student_t4(torch, g, shape):
@@ -345,8 +352,14 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
             kvq.kvq_quantize_store(lay.cache, lay.k_new, lay.v_new, lay.slots_new)
             if a is not None:
                 b_.record(stream)
-            kvq.kvq_decode_attention(lay.cache, lay.q, lay.bt, lay.lens, L, out=lay.out, workspace=ws,
-                                     num_splits=splits)
+            if w.get("rotated"):
+                kvq.kvq_hadamard_rotate(lay.q, out=lay.q_rot)
+                kvq.kvq_decode_attention(lay.cache, lay.q_rot, lay.bt, lay.lens, L, out=lay.out_rot, workspace=ws,
+                                         num_splits=splits)
+                kvq.kvq_hadamard_rotate(lay.out_rot, out=lay.out)
+            else:
+                kvq.kvq_decode_attention(lay.cache, lay.q, lay.bt, lay.lens, L, out=lay.out, workspace=ws,
+                                         num_splits=splits)
             if a is not None:
                 c.record(stream)
                 timed_pairs.append((a, b_, c))
@@ -581,6 +594,7 @@ def main():
         "cpu_baseline": cpu,
         "store_call_us": r["store_call_us"],
         "populate": r["populate"],
+        "calibrate_amax": r.get("calibrate_amax"),
         "secondary": secondary,
     }
     if "fp8_32k" in secondary and args.workload == "ctx32k":

@@ -68,6 +68,7 @@ def _load():
         "kvqo_token_head_bytes": (sz, [i32, i32]),
         "kvqo_quantize_store": (None, [i32, P, i32, i32, i32, P, P, P, i32, P, i32]),
         "kvqo_hadamard_row": (None, [P, i32]),
+        "kvqo_extend_attention": (None, [P, i64, i32, P, P, i64, i32, i32, i64, i64, f64, P, P]),
         "kvqo_decode_attention": (None, [i32, P, i32, i32, i32, P, P, i32, P, i32, P, i32, f64, i64, P, P]),
         "kvqo_dequant_prefix": (None, [i32, P, i32, i32, i32, P, P, i64, P, P, i64]),
         "kvqo_num_threads": (i32, []),
@@ -173,6 +174,23 @@ def hadamard(x) -> np.ndarray:
     for r in rows:
         _load().kvqo_hadamard_row(r.ctypes.data_as(ctypes.c_void_p), D)
     return rows.reshape(a.shape)
+
+
+def extend_attention(q, k_ws, v_ws, prefix_len: int, sm_scale: float | None = None):
+    """Chunk queries q [n][Hq][D] over workspace rows k_ws, v_ws [>= prefix_len + n][Hkv][D]
+    (bf16 values widened to fp32), query i seeing keys 0 .. prefix_len + i.
+    Returns (out fp64 [n][Hq][D], lse fp64 [n][Hq])."""
+    q, k, v = _f32(q), _f32(k_ws), _f32(v_ws)
+    n, Hq, D = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == v.shape and k.shape[2] == D and k.shape[0] >= prefix_len + n and Hq % Hkv == 0
+    if sm_scale is None or sm_scale <= 0:
+        sm_scale = 1.0 / np.sqrt(D)
+    out = np.zeros((n, Hq, D), np.float64)
+    lse = np.zeros((n, Hq), np.float64)
+    _load().kvqo_extend_attention(_ptr(q), Hq * D, Hq, _ptr(k), _ptr(v), Hkv * D, Hkv, D, int(prefix_len), n,
+                                  float(sm_scale), _ptr(out), _ptr(lse))
+    return out, lse
 
 
 def fp8_encode(x: float, scale: float) -> int:

@@ -489,6 +489,51 @@ void kvqo_dequant_prefix(int fmt, const uint8_t* pool, int P, int Hkv, int D, co
   }
 }
 
+/* Extend attention ("SGLang's 4-bit KV cache ...", Figure 2 caption: the
+ * chunked-prefill / extend path dequantizes the cached prefix into a reused
+ * workspace and attends over prefix plus current chunk).  Reading: the
+ * workspace holds bf16 K and V rows [prefix_len + chunk_len][Hkv][D] (token
+ * stride kv_stride elements) -- the dequantized prefix followed by the
+ * chunk's own K/V -- and chunk query i (at sequence position prefix_len + i)
+ * attends causally to keys 0 .. prefix_len + i: standard scaled dot-product
+ * attention, query head h reading KV head h / G, in fp64.  q is
+ * [chunk_len][Hq][D] (token stride q_stride); out [chunk_len][Hq][D],
+ * lse [chunk_len][Hq] (natural log). */
+void kvqo_extend_attention(const float* q, int64_t q_stride, int Hq, const float* k_ws, const float* v_ws,
+                           int64_t kv_stride, int Hkv, int D, int64_t prefix_len, int64_t chunk_len,
+                           double sm_scale, double* out, double* lse) {
+  const int G = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic) collapse(2)
+  for (int64_t i = 0; i < chunk_len; i++) {
+    for (int h = 0; h < Hq; h++) {
+      const int g = h / G;
+      const float* qh = q + i * q_stride + (int64_t)h * D;
+      const int64_t nk = prefix_len + i + 1;
+      double* s = (double*)malloc(sizeof(double) * (size_t)nk);
+      double m = -INFINITY;
+      for (int64_t j = 0; j < nk; j++) {
+        const float* kj = k_ws + j * kv_stride + (int64_t)g * D;
+        double dot = 0.0;
+        for (int c = 0; c < D; c++) dot += (double)qh[c] * (double)kj[c];
+        s[j] = dot * sm_scale;
+        if (s[j] > m) m = s[j];
+      }
+      double l = 0.0;
+      double* o = out + ((size_t)i * Hq + h) * D;
+      for (int c = 0; c < D; c++) o[c] = 0.0;
+      for (int64_t j = 0; j < nk; j++) {
+        const double p = exp(s[j] - m);
+        l += p;
+        const float* vj = v_ws + j * kv_stride + (int64_t)g * D;
+        for (int c = 0; c < D; c++) o[c] += p * (double)vj[c];
+      }
+      for (int c = 0; c < D; c++) o[c] /= l;
+      lse[(size_t)i * Hq + h] = m + log(l);
+      free(s);
+    }
+  }
+}
+
 /* Global-scale calibration ("SGLang's 4-bit KV cache ...", section
  * '"Near-lossless" is narrower than it sounds': the measured NVFP4 runs
  * without its per-tensor FP32 scale and calibration is listed as ongoing

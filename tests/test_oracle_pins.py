@@ -623,3 +623,40 @@ def test_rotation_improves_outlier_quality(oracle):
             return float(np.sum(a * b) / (np.linalg.norm(a) * np.linalg.norm(b)))
         c_plain, c_rot = cos(o_plain[0], full), cos(o_rot[0], full)
         assert c_rot > c_plain, (fmt, c_plain, c_rot)
+
+
+# ----------------------------------------------------------------- extend attention (workspace path)
+
+@pytest.mark.parametrize("Lp,n,G,Hkv,D", [(0, 9, 1, 1, 64), (37, 16, 4, 2, 64), (100, 33, 6, 1, 128)])
+def test_extend_attention_matches_torch_sdpa(oracle, Lp, n, G, Hkv, D):
+    rng = np.random.default_rng(Lp + n)
+    Hq = G * Hkv
+    q = rng.standard_normal((n, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((Lp + n + 3, Hkv, D)).astype(np.float32)   # rows past the chunk are never read
+    v = rng.standard_normal((Lp + n + 3, Hkv, D)).astype(np.float32)
+    out, lse = oracle.extend_attention(q, k, v, Lp)
+    Lk = Lp + n
+    qt = torch.from_numpy(q).double().transpose(0, 1)                               # [Hq][n][D]
+    kt = torch.from_numpy(k[:Lk]).double().repeat_interleave(G, dim=1).transpose(0, 1)  # [Hq][Lk][D]
+    vt = torch.from_numpy(v[:Lk]).double().repeat_interleave(G, dim=1).transpose(0, 1)
+    mask = torch.arange(Lk)[None, :] <= (Lp + torch.arange(n))[:, None]              # query i sees keys <= Lp + i
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=1 / math.sqrt(D))
+    np.testing.assert_allclose(out, ref.transpose(0, 1).numpy(), rtol=1e-10, atol=1e-12)
+    s = (qt @ kt.transpose(1, 2)) / math.sqrt(D)
+    s = s.masked_fill(~mask, float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).transpose(0, 1).numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_extend_attention_closed_forms(oracle):
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((3, 2, 32)).astype(np.float32)
+    k = rng.standard_normal((3, 1, 32)).astype(np.float32)
+    v = rng.standard_normal((3, 1, 32)).astype(np.float32)
+    out, lse = oracle.extend_attention(q, k, v, 0)
+    # with no prefix, the first chunk query sees only itself: o = v_0, lse = s_00
+    np.testing.assert_array_equal(out[0, 0], v[0, 0].astype(np.float64))
+    assert abs(lse[0, 1] - float(q[0, 1].astype(np.float64) @ k[0, 0].astype(np.float64)) / math.sqrt(32)) < 1e-12
+    # identical keys: o = mean of the visible values
+    k2 = np.repeat(k[:1], 3, axis=0)
+    out2, _ = oracle.extend_attention(q, k2, v, 0)
+    np.testing.assert_allclose(out2[2, 0], v[:3, 0].astype(np.float64).mean(axis=0), rtol=1e-12, atol=1e-12)

@@ -267,6 +267,46 @@ kvq_status kvq_calibrate_global_scale(const kvq_cache* cache, const float* runni
   return hip_status(kvq::launch_global_scale(running_amax, (float*)cache->global_scale, (hipStream_t)stream));
 }
 
+kvq_status kvq_extend_attention(const void* q, int64_t q_token_stride, int32_t num_q_heads, const void* k_ws,
+                                const void* v_ws, int64_t kv_token_stride, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t prefix_len, int32_t chunk_len, float sm_scale, void* out, int32_t out_dtype,
+                                int64_t out_token_stride, float* lse_out, void* stream) {
+  if (prefix_len < 0 || chunk_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0) return KVQ_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return KVQ_ERR_SHAPE;
+  if (head_dim != 128 && head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  if (out_dtype != KVQ_DT_F32 && out_dtype != KVQ_DT_BF16) return KVQ_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (chunk_len == 0) return KVQ_OK;
+  if (q == nullptr || k_ws == nullptr || v_ws == nullptr || out == nullptr) return KVQ_ERR_NULL;
+  if (q_token_stride < (int64_t)num_q_heads * head_dim || kv_token_stride < (int64_t)num_kv_heads * head_dim ||
+      out_token_stride < (int64_t)num_q_heads * head_dim)
+    return KVQ_ERR_SHAPE;
+  const int64_t oes = out_dtype == KVQ_DT_F32 ? 4 : 2;
+  if (!aligned16(q) || !aligned16(k_ws) || !aligned16(v_ws) || !aligned16(out) || (q_token_stride * 2) % 16 ||
+      (kv_token_stride * 2) % 16 || (out_token_stride * oes) % 16 || (lse_out && ((uintptr_t)lse_out & 3u)))
+    return KVQ_ERR_ALIGN;
+  const int64_t rows = (int64_t)chunk_len * (num_q_heads / num_kv_heads);
+  if ((rows + 63) / 64 > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
+  kvq::ExtendParams p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k_ws;
+  p.v = (const uint16_t*)v_ws;
+  p.out = out;
+  p.lse = lse_out;
+  p.q_stride = q_token_stride;
+  p.kv_stride = kv_token_stride;
+  p.out_stride = out_token_stride;
+  p.lse_stride = num_q_heads;
+  p.sm_scale = sm_scale > 0.0f ? sm_scale : 1.0f / __builtin_sqrtf((float)head_dim);
+  p.prefix_len = prefix_len;
+  p.chunk_len = chunk_len;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.out_bf16 = out_dtype == KVQ_DT_BF16;
+  return hip_status(kvq::launch_extend(p, head_dim, (hipStream_t)stream));
+}
+
 kvq_status kvq_hadamard_rotate(const void* in, int32_t in_dtype, int64_t in_row_stride, void* out, int32_t out_dtype,
                                int64_t out_row_stride, int32_t rows, int32_t head_dim, void* stream) {
   if (rows < 0) return KVQ_ERR_SHAPE;

@@ -59,12 +59,24 @@ struct DecodeParams {
   int32_t out_bf16;
 };
 
+struct ExtendParams {
+  const uint16_t* q;  // bf16 [chunk_len][q_stride], head h at h * head_dim
+  const uint16_t* k;  // bf16 workspace [prefix_len + chunk_len][kv_stride]
+  const uint16_t* v;
+  void* out;          // [chunk_len][out_stride], bf16 or fp32
+  float* lse;         // [chunk_len][lse_stride] or null
+  int64_t q_stride, kv_stride, out_stride, lse_stride;
+  float sm_scale;
+  int32_t prefix_len, chunk_len, num_q_heads, num_kv_heads, group, out_bf16;
+};
+
 hipError_t launch_quantize_store(const StoreParams& p, int fmt, int head_dim, int in_bf16, hipStream_t stream);
 hipError_t launch_dequant_prefix(const DequantParams& p, int fmt, int head_dim, hipStream_t stream);
 hipError_t launch_calibrate_amax(const StoreParams& p, int head_dim, int in_bf16, float* running, hipStream_t stream);
 hipError_t launch_global_scale(const float* running, float* gs, hipStream_t stream);
 hipError_t launch_hadamard(const RotateParams& p, int head_dim, int in_bf16, int out_bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream_t stream);
+hipError_t launch_extend(const ExtendParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
 
 }  // namespace kvq

@@ -65,6 +65,7 @@ def lib():
         "kvq_calibrate_amax": (i32, [C, P, P, i32, i64, i32, P, P]),
         "kvq_calibrate_global_scale": (i32, [C, P, P]),
         "kvq_hadamard_rotate": (i32, [P, i32, i64, P, i32, i64, i32, i32, P]),
+        "kvq_extend_attention": (i32, [P, i64, i32, P, P, i64, i32, i32, i32, i32, f32, P, i32, i64, P, P]),
         "kvq_status_string": (ctypes.c_char_p, [i32]),
         "kvq_last_hip_error": (i32, []),
     }
@@ -226,4 +227,25 @@ def kvq_hadamard_rotate(x: torch.Tensor, out: torch.Tensor | None = None, out_dt
     _check("kvq_hadamard_rotate", lib().kvq_hadamard_rotate(_ptr(xr), dt[x.dtype], xr.stride(0), _ptr(orr),
                                                             dt[out.dtype], orr.stride(0), xr.shape[0], D,
                                                             _stream(stream)))
+    return out
+
+
+def kvq_extend_attention(q: torch.Tensor, k_ws: torch.Tensor, v_ws: torch.Tensor, prefix_len: int,
+                         out: torch.Tensor | None = None, lse: torch.Tensor | None = None, sm_scale: float = 0.0,
+                         out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """q: bf16 [n][Hq][D]; k_ws, v_ws: bf16 [>= prefix_len + n][Hkv][D] (or rows
+    of >= Hkv*D elements).  Returns out [n][Hq][D]."""
+    n, Hq, D = q.shape
+    assert q.dtype == torch.bfloat16 and k_ws.dtype == torch.bfloat16 and v_ws.dtype == torch.bfloat16
+    assert q.stride(2) == 1 and q.stride(1) == D and k_ws.stride(0) == v_ws.stride(0)
+    Hkv = k_ws.shape[1] if k_ws.dim() == 3 else k_ws.shape[1] // D
+    assert k_ws.shape[0] >= prefix_len + n
+    if out is None:
+        out = torch.empty((n, Hq, D), dtype=out_dtype, device=q.device)
+    odt = {torch.float32: DT_F32, torch.bfloat16: DT_BF16}[out.dtype]
+    if lse is not None:
+        assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() >= n * Hq
+    _check("kvq_extend_attention", lib().kvq_extend_attention(
+        _ptr(q), q.stride(0), Hq, _ptr(k_ws), _ptr(v_ws), k_ws.stride(0), Hkv, D, int(prefix_len), n,
+        float(sm_scale), _ptr(out), odt, out.stride(0), _ptr(lse) if lse is not None else None, _stream(stream)))
     return out

@@ -190,6 +190,26 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
 kvq_status kvq_dequant_prefix(const kvq_cache* cache, const int32_t* block_table_row, int32_t prefix_len,
                               void* k_out, void* v_out, int64_t out_token_stride, void* stream);
 
+/* Extend attention over the bf16 workspace ("SGLang's 4-bit KV cache ...",
+ * Figure 2 caption: chunked prefill / extend dequantizes the cached prefix
+ * into a reused workspace and attends over prefix plus current chunk).
+ *   k_ws, v_ws  device bf16 [prefix_len + chunk_len][kv_token_stride]: rows
+ *               [0, prefix_len) hold the prefix (kvq_dequant_prefix), rows
+ *               [prefix_len, prefix_len + chunk_len) the chunk's own K / V;
+ *               head g of a row at element g * head_dim
+ *   q           device bf16 [chunk_len][q_token_stride], head h at h * head_dim
+ *   out         device [chunk_len][out_token_stride], bf16 or fp32 per out_dtype
+ *   lse_out     device fp32 [chunk_len][num_q_heads] (natural log), or NULL
+ * Chunk query i (sequence position prefix_len + i) of head h attends to the
+ * keys 0 .. prefix_len + i of KV head h / (num_q_heads / num_kv_heads) with
+ * softmax(sm_scale q k); sm_scale <= 0 means 1/sqrt(head_dim).  head_dim 128
+ * or 256; chunk_len == 0 is a no-op.  The path is the workspace variant of the
+ * pages' extend step (bf16 here instead of FP8, lossless at gs = 1). */
+kvq_status kvq_extend_attention(const void* q, int64_t q_token_stride, int32_t num_q_heads, const void* k_ws,
+                                const void* v_ws, int64_t kv_token_stride, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t prefix_len, int32_t chunk_len, float sm_scale, void* out, int32_t out_dtype,
+                                int64_t out_token_stride, float* lse_out, void* stream);
+
 /* Global-scale calibration for NVFP4 ("SGLang's 4-bit KV cache ...",
  * section '"Near-lossless" is narrower than it sounds': the measured NVFP4
  * drops its per-tensor FP32 scale, which leaves the E4M3 block scale to carry

@@ -202,3 +202,32 @@ def test_rotation_flag_and_rotate_validation(lib):
     assert f(FAKE, 1, 128, FAKE, 0, 256, 4, 256, None) == ERR_SHAPE
     assert f(FAKE, 1, 260, FAKE, 0, 260, 4, 256, None) == ERR_ALIGN
     assert f(FAKE + 4, 1, 256, FAKE, 0, 256, 4, 256, None) == ERR_ALIGN
+
+
+def test_extend_attention_validation(lib):
+    f = lib.kvq_extend_attention
+    ok = (FAKE, 24 * 256, 24, FAKE, FAKE, 4 * 256, 4, 256, 100, 0, 0.0, FAKE, 1, 24 * 256, None, None)
+    assert f(*ok) == OK                                           # empty chunk
+    a = list(ok)
+    a[9] = 8
+    args = list(a)
+    args[0] = None
+    assert f(*args) == ERR_NULL
+    args = list(a)
+    args[2] = 25
+    assert f(*args) == ERR_SHAPE                                  # Hq not a multiple of Hkv
+    args = list(a)
+    args[7] = 64
+    assert f(*args) == ERR_UNSUPPORTED
+    args = list(a)
+    args[5] = 4 * 256 - 8
+    assert f(*args) == ERR_SHAPE
+    args = list(a)
+    args[1] = 24 * 256 + 4
+    assert f(*args) == ERR_ALIGN
+    args = list(a)
+    args[12] = 9
+    assert f(*args) == ERR_UNSUPPORTED
+    args = list(a)
+    args[8] = -1
+    assert f(*args) == ERR_SHAPE

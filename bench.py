@@ -450,7 +450,34 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
         res["dequant_prefix"] = {"us": us, "read_bytes": rd, "write_bytes": wr,
                                  "gbs": (rd + wr) / (us * 1e-6) / 1e9,
                                  "frac_hbm": (rd + wr) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
-        del k_ws, v_ws
+        # extend attention of a 4,096-token chunk over [prefix | chunk] in the same
+        # workspace (the chunk's K/V in its last rows), for two prefix lengths
+        n = 4096
+        g = torch.Generator(device="cuda")
+        g.manual_seed(inputs.seed_int(wid, 0, 50))
+        k_ws[L:L + n] = torch.randn((n, HKV * D), generator=g, device="cuda").to(torch.bfloat16)
+        v_ws[L:L + n] = torch.randn((n, HKV * D), generator=g, device="cuda").to(torch.bfloat16)
+        qc = torch.randn((n, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
+        oc = torch.empty((n, HQ, D), dtype=torch.bfloat16, device="cuda")
+        ext = {}
+        for lp in (32768, L):
+            # the chunk rows follow the prefix: use rows [L - lp, L + n) as the workspace
+            kw, vw = k_ws[L - lp:], v_ws[L - lp:]
+            reps = 1 if lp == L else 5
+            kvq.kvq_extend_attention(qc, kw, vw, lp, out=oc)
+            a, b_ = ev(), ev()
+            a.record(stream)
+            for _ in range(reps):
+                kvq.kvq_extend_attention(qc, kw, vw, lp, out=oc)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b_) / reps * 1e3
+            flops = 4.0 * HQ * D * (n * lp + n * (n + 1) / 2)
+            ext[str(lp)] = {"prefix_len": lp, "chunk_len": n, "us": us, "flops": flops,
+                            "tflops": flops / (us * 1e-6) / 1e12,
+                            "frac_bf16_mfma_peak": flops / (us * 1e-6) / 2.5e15}
+        res["extend_attention"] = ext
+        del k_ws, v_ws, qc, oc
     keep = layers[0] if keep_for_cpu else None
     del layers, ws, chunk
     torch.cuda.empty_cache()

@@ -272,23 +272,36 @@ __global__ __launch_bounds__(256) void int4_store_kernel(StoreParams p) {
 }
 
 // Global-scale calibration: the running absolute maximum of a layer's K and
-// V over prefill rows.  Same grid as the store (token runs x (K|V, head));
-// the workgroup's maximum goes into running[kv] with one atomic max on the
-// fp32 bit pattern, which orders like the value for non-negative numbers.
+// V over prefill rows.  Grid (token-run workgroups, K|V x head) with the
+// token runs walked grid-stride so that only a bounded number of workgroups
+// (kAmaxWorkgroups per pair) each add one atomic max on the fp32 bit pattern
+// of running[kv], which orders like the value for non-negative numbers.
+constexpr int kAmaxWorkgroups = 512;
+
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void amax_kernel(StoreParams p, float* running) {
-  constexpr int NB = D / 16;
+  constexpr int NB = D / 16, TPW = 256 / NB;
   const int kv = (int)blockIdx.y >= p.num_kv_heads ? 1 : 0;
   const int g = (int)blockIdx.y - kv * p.num_kv_heads;
   const int b = threadIdx.x % NB;
-  const int64_t i = store_token<D>(threadIdx.x);
   float amax = 0.0f;
-  if (i < p.num_tokens) {
-    float x[16];
-    Row16<TIn>::load((const TIn*)(kv ? p.v : p.k) + i * p.in_stride + (int64_t)g * D + 16 * b, x);
-    if (p.rotate) hadamard_row<D>(x, b, p.rot_scale);  // a rotated cache stores rotated rows
+  // four token runs per pass with their loads in flight together; a run past
+  // the end re-reads the last token, which leaves a maximum unchanged
+  const int64_t stride = (int64_t)gridDim.x * TPW;
+  const TIn* src = (const TIn*)(kv ? p.v : p.k) + (int64_t)g * D + 16 * b;
+  for (int64_t i0 = (int64_t)blockIdx.x * TPW + threadIdx.x / NB; i0 < p.num_tokens; i0 += 4 * stride) {
+    float x[4][16];
 #pragma unroll
-    for (int e = 0; e < 16; e++) amax = fmaxf(amax, __builtin_fabsf(x[e]));
+    for (int u = 0; u < 4; u++) {
+      const int64_t i = min(i0 + u * stride, (int64_t)p.num_tokens - 1);
+      Row16<TIn>::load(src + i * p.in_stride, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      if (p.rotate) hadamard_row<D>(x[u], b, p.rot_scale);  // a rotated cache stores rotated rows
+#pragma unroll
+      for (int e = 0; e < 16; e++) amax = fmaxf(amax, __builtin_fabsf(x[u][e]));
+    }
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
@@ -311,7 +324,9 @@ __global__ void global_scale_kernel(const float* running, float* gs) {
 hipError_t launch_calibrate_amax(const StoreParams& p, int head_dim, int in_bf16, float* running,
                                  hipStream_t stream) {
   const int tpw = 256 / (head_dim / 16);
-  const dim3 grid((unsigned)((p.num_tokens + tpw - 1) / tpw), (unsigned)(2 * p.num_kv_heads)), block(256);
+  const int64_t runs = (p.num_tokens + tpw - 1) / tpw;
+  const dim3 grid((unsigned)(runs < kAmaxWorkgroups ? runs : kAmaxWorkgroups), (unsigned)(2 * p.num_kv_heads));
+  const dim3 block(256);
   if (head_dim == 256) {
     if (in_bf16) hipLaunchKernelGGL((amax_kernel<256, uint16_t>), grid, block, 0, stream, p, running);
     else hipLaunchKernelGGL((amax_kernel<256, float>), grid, block, 0, stream, p, running);

@@ -272,29 +272,32 @@ __global__ __launch_bounds__(256) void int4_store_kernel(StoreParams p) {
 }
 
 // Global-scale calibration: the running absolute maximum of a layer's K and
-// V over prefill rows.  Grid (token-run workgroups, K|V x head) with the
-// token runs walked grid-stride so that only a bounded number of workgroups
-// (kAmaxWorkgroups per pair) each add one atomic max on the fp32 bit pattern
-// of running[kv], which orders like the value for non-negative numbers.
-constexpr int kAmaxWorkgroups = 512;
+// V over prefill rows.  Grid (up to kAmaxWorkgroups, K|V): the workgroups walk
+// the (token, head) rows grid-stride, four row runs at a time with their loads
+// in flight together; a workgroup adds its maximum with one atomic max on the
+// fp32 bit pattern of running[kv] (which orders like the value for
+// non-negative numbers), and only when it exceeds the value it reads there,
+// so that few of the atomics -- which serialize on one address -- happen.
+constexpr int kAmaxWorkgroups = 1024;
 
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void amax_kernel(StoreParams p, float* running) {
-  constexpr int NB = D / 16, TPW = 256 / NB;
-  const int kv = (int)blockIdx.y >= p.num_kv_heads ? 1 : 0;
-  const int g = (int)blockIdx.y - kv * p.num_kv_heads;
+  constexpr int NB = D / 16, RPW = 256 / NB;
+  const int kv = blockIdx.y;
   const int b = threadIdx.x % NB;
+  const int64_t rows = (int64_t)p.num_tokens * p.num_kv_heads;
+  const int64_t stride = (int64_t)gridDim.x * RPW;
+  const TIn* src = (const TIn*)(kv ? p.v : p.k) + 16 * b;
   float amax = 0.0f;
-  // four token runs per pass with their loads in flight together; a run past
-  // the end re-reads the last token, which leaves a maximum unchanged
-  const int64_t stride = (int64_t)gridDim.x * TPW;
-  const TIn* src = (const TIn*)(kv ? p.v : p.k) + (int64_t)g * D + 16 * b;
-  for (int64_t i0 = (int64_t)blockIdx.x * TPW + threadIdx.x / NB; i0 < p.num_tokens; i0 += 4 * stride) {
+  // a run past the end re-reads the last row, which leaves a maximum unchanged
+  for (int64_t r0 = (int64_t)blockIdx.x * RPW + threadIdx.x / NB; r0 < rows; r0 += 4 * stride) {
     float x[4][16];
 #pragma unroll
     for (int u = 0; u < 4; u++) {
-      const int64_t i = min(i0 + u * stride, (int64_t)p.num_tokens - 1);
-      Row16<TIn>::load(src + i * p.in_stride, x[u]);
+      const int64_t r = min(r0 + u * stride, rows - 1);
+      const int64_t i = r / p.num_kv_heads;
+      const int g = (int)(r - i * p.num_kv_heads);
+      Row16<TIn>::load(src + i * p.in_stride + (int64_t)g * D, x[u]);
     }
 #pragma unroll
     for (int u = 0; u < 4; u++) {
@@ -310,7 +313,9 @@ __global__ __launch_bounds__(256) void amax_kernel(StoreParams p, float* running
   __syncthreads();
   if (threadIdx.x == 0) {
     const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    atomicMax((unsigned int*)(running + kv), as_u32(m));
+    // the running maximum only grows, so a workgroup whose maximum does not
+    // exceed a (possibly stale) read of it has nothing to add
+    if (m > __builtin_nontemporal_load(running + kv)) atomicMax((unsigned int*)(running + kv), as_u32(m));
   }
 }
 
@@ -323,10 +328,9 @@ __global__ void global_scale_kernel(const float* running, float* gs) {
 
 hipError_t launch_calibrate_amax(const StoreParams& p, int head_dim, int in_bf16, float* running,
                                  hipStream_t stream) {
-  const int tpw = 256 / (head_dim / 16);
-  const int64_t runs = (p.num_tokens + tpw - 1) / tpw;
-  const dim3 grid((unsigned)(runs < kAmaxWorkgroups ? runs : kAmaxWorkgroups), (unsigned)(2 * p.num_kv_heads));
-  const dim3 block(256);
+  const int rpw = 256 / (head_dim / 16);
+  const int64_t runs = ((int64_t)p.num_tokens * p.num_kv_heads + rpw - 1) / rpw;
+  const dim3 grid((unsigned)(runs < kAmaxWorkgroups ? runs : kAmaxWorkgroups), 2u), block(256);
   if (head_dim == 256) {
     if (in_bf16) hipLaunchKernelGGL((amax_kernel<256, uint16_t>), grid, block, 0, stream, p, running);
     else hipLaunchKernelGGL((amax_kernel<256, float>), grid, block, 0, stream, p, running);

@@ -32,12 +32,17 @@ static constexpr float kExtLog2e = 1.4426950408889634f;
 static constexpr float kExtLn2 = 0.6931471805599453f;
 static constexpr float kExtSlack = 8.0f;
 
+// LDS strides chosen against bank conflicts (64 banks of 4 bytes): a K row
+// is 4 banks off the previous one; a V^T row is 19 dwords long, so the
+// 16-channel groups one wavefront writes (16 rows apart) start 48 banks apart
+// (conflict-free writes) and an operand read spreads over the banks with at
+// most 3 dwords per bank.
 template <int D>
 struct ExtLds {
   static constexpr int KP = 2 * D + 16;        // bytes per staged K row (token), padded
-  static constexpr int VP = 2 * kExtStep + 16; // bytes per staged V^T row (channel), padded
+  static constexpr int VPD = kExtStep / 2 + 3; // dwords per staged V^T row (channel): 16 used + 3 pad
   static constexpr int KB = kExtStep * KP;
-  static constexpr int BUF = KB + D * VP;
+  static constexpr int BUF = KB + D * VPD * 4;
   static constexpr int TOTAL = 2 * BUF;
 };
 
@@ -81,9 +86,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   }
   const float sm = p.sm_scale * kExtLog2e;
 
-  // ---- staging: thread t loads K row t/8 (16-byte vectors seg*KV16 ..) and the
-  // V values of tokens 2(t%16), 2(t%16)+1, channels (t/16)*CPT ..
-  const int krow = tid >> 3, kseg = tid & 7;
+  // ---- staging: thread t loads 16-byte vectors kseg*KV16 .. of K row krow, and
+  // the V values of tokens 2(t%16), 2(t%16)+1, channels (t/16)*CPT ...  At head
+  // dim 256 a quarter-wavefront covers 4 rows x 4 segments (distinct banks on
+  // the LDS write, 256 contiguous bytes per row on the global read); at 128 it
+  // covers 2 rows x 8 segments, already conflict-free.
+  const int krow = D == 256 ? ((tid >> 2) & 3) + 4 * (tid >> 5) : tid >> 3;
+  const int kseg = D == 256 ? (tid & 3) + 4 * ((tid >> 4) & 1) : tid & 7;
   const int vpair = tid & 15, vcb = tid >> 4;
   u32x4_t kreg[KV16], va[CPT / 8], vb[CPT / 8];
   auto gload = [&](int step) {
@@ -106,7 +115,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 #pragma unroll
     for (int v = 0; v < KV16; v++)
       *(u32x4_t*)(base + krow * Lds::KP + kseg * (D / 4) + 16 * v) = kreg[v];
-    uint8_t* vt = base + Lds::KB;
+    uint32_t* vt = (uint32_t*)(base + Lds::KB);
 #pragma unroll
     for (int v = 0; v < CPT / 8; v++) {
       const uint32_t a4[4] = {va[v].x, va[v].y, va[v].z, va[v].w};
@@ -115,8 +124,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       for (int e = 0; e < 4; e++) {
         const int c = vcb * CPT + 8 * v + 2 * e;
         // (token a, token b) of channel c, then of channel c + 1
-        *(uint32_t*)(vt + c * Lds::VP + 4 * vpair) = byte_perm(b4[e], a4[e], 0x05040100u);
-        *(uint32_t*)(vt + (c + 1) * Lds::VP + 4 * vpair) = byte_perm(b4[e], a4[e], 0x07060302u);
+        vt[c * Lds::VPD + vpair] = byte_perm(b4[e], a4[e], 0x05040100u);
+        vt[(c + 1) * Lds::VPD + vpair] = byte_perm(b4[e], a4[e], 0x07060302u);
       }
     }
   };
@@ -128,7 +137,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 
   auto compute = [&](int buf, int64_t t0) {
     const uint8_t* kb = lds + buf * Lds::BUF;
-    const uint8_t* vt = kb + Lds::KB;
+    const uint32_t* vt = (const uint32_t*)(kb + Lds::KB);
     float4_t sacc[2];
 #pragma unroll
     for (int hh = 0; hh < 2; hh++) {
@@ -173,10 +182,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 #pragma unroll
     for (int t = 0; t < VT; t++) {
       // channel 16t + n, tokens 4j..4j+3 and 16+4j..16+4j+3 (the order of P's k index)
-      const uint8_t* vr = vt + (16 * t + n) * Lds::VP + 8 * j;
-      const u32x2_t w0 = *(const u32x2_t*)vr;
-      const u32x2_t w1 = *(const u32x2_t*)(vr + 32);
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (u32x4_t){w0.x, w0.y, w1.x, w1.y});
+      const uint32_t* vr = vt + (16 * t + n) * Lds::VPD + 2 * j;  // 4-byte aligned rows: dword reads
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (u32x4_t){vr[0], vr[1], vr[8], vr[9]});
       oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, oacc[t], 0, 0, 0);
       oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, oacc[t], 0, 0, 0);
     }

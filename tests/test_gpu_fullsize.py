@@ -177,3 +177,41 @@ def test_full_int4_220k_page1600():
     lay = FullLayer(5, 2, 8, 220000, 1600, False, "student_t")
     pool = lay.check_packing()
     lay.check_decode(pool, seqs=[0, 7], heads_per_group=1)
+
+
+def test_full_32k_fp8_comparator_batch32():
+    # the comparator at the headline shape: FP8 E4M3 per-tensor cache, 32 sequences x 32,768 tokens
+    print("case: full 32K FP8 comparator layer", flush=True)
+    lay = FullLayer(6, 3, 32, 32768, 16, False, "lognormal")
+    pool = lay.cache.pool.cpu().numpy()
+    for b, t, krow, vrow in lay.samples:
+        page, row = int(lay.bt[b, t // 16]), t % 16
+        for g in range(HKV):
+            sl = pool[page, g]
+            kc = np.array([oracle.fp8_encode(x, 1.0) for x in krow[g]], np.uint8)
+            vc = np.array([oracle.fp8_encode(x, 1.0) for x in vrow[g]], np.uint8)
+            assert np.array_equal(sl[row * D:(row + 1) * D], kc), (b, t, g)
+            assert np.array_equal(sl[16 * D + row::16][:D], vc), (b, t, g)
+    lay.check_decode(pool, seqs=[0, 31], heads_per_group=1)
+
+
+def test_full_extend_4096_over_32k_prefix():
+    # extend attention of a 4,096-token chunk over a 32K prefix workspace (the
+    # bench's shape), sampled query rows against the oracle run row by row
+    print("case: full extend 4096 over 32K", flush=True)
+    Lp, n = 32768, 4096
+    g = torch.Generator(device="cuda")
+    g.manual_seed(inputs.seed_int(7, 0, inputs.STREAM_K))
+    k = torch.randn((Lp + n, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((Lp + n, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((n, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
+    lse = torch.empty((n, HQ), dtype=torch.float32, device="cuda")
+    out = kvq.kvq_extend_attention(q, k, v, Lp, lse=lse, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kh, vh, qh = k.float().cpu().numpy(), v.float().cpu().numpy(), q.float().cpu().numpy()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for i in (0, 1, 63, 64, 2047, 4095):
+        # query i alone, as a one-token chunk at position Lp + i
+        ref, ref_lse = oracle.extend_attention(qh[i:i + 1], kh, vh, Lp + i)
+        check_attention(out[i:i + 1], ref, np.ones(1, np.int32), lse=lse[i:i + 1], ref_lse=ref_lse,
+                        label=f"extend row {i}")

@@ -200,11 +200,10 @@ struct Decoder : PageWalk {
       a2 = e2m1x2_to_h2_x256<2>(word) * s2;
       a3 = e2m1x2_to_h2_x256<3>(word) * s2;
     } else {
-      const uint32_t wb = word ^ 0x88888888u;
-      a0 = int4x2_to_h2<0>(wb);
-      a1 = int4x2_to_h2<1>(wb);
-      a2 = int4x2_to_h2<2>(wb);
-      a3 = int4x2_to_h2<3>(wb);
+      a0 = int4x2_to_h2<0>(word);
+      a1 = int4x2_to_h2<1>(word);
+      a2 = int4x2_to_h2<2>(word);
+      a3 = int4x2_to_h2<3>(word);
     }
     return (half8_t){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
   }
@@ -481,7 +480,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
             for (int pp = 0; pp < 2; pp++) {
               const uint32_t a = R.vw[h][2 * pp][d], bb = R.vw[h][2 * pp + 1][d];
-              pw[h][pp] = byte_perm(bb, a, sel == 0 ? 0x05040100u : 0x07060302u) ^ 0x88888888u;
+              pw[h][pp] = byte_perm(bb, a, sel == 0 ? 0x05040100u : 0x07060302u);
             }
           }
 #pragma unroll

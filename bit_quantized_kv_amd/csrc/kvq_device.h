@@ -144,13 +144,15 @@ __device__ inline half2_t e2m1x2_to_h2_x256(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, SEL);
 }
 
-// Two-nibble INT4 pairs: given w' = w ^ 0x88888888 (offset-8 nibbles), the
-// nibbles at positions p and p + 4 become fp16 (q_p, q_{p+4}) exactly: the
-// nibble u is placed in the low mantissa bits of 1024 (0x6400), then 1032 is
-// subtracted.
+// Two-nibble INT4 pairs: the two's-complement nibbles at positions p and
+// p + 4 of w become fp16 (q_p, q_{p+4}) exactly.  Each nibble u lands in the
+// low mantissa bits of 1024 (0x6400) with its sign bit flipped (the XOR with
+// 0x0008 turns u into q + 8), then 1032 is subtracted: mask, bias and the
+// 0x6400 fill are one AND + XOR (a single v_bitop3), so no separate pass over
+// the word is needed.
 template <int P>
-__device__ inline half2_t int4x2_to_h2(uint32_t wbiased) {
-  uint32_t t = ((wbiased >> (4 * P)) & 0x000F000Fu) | 0x64006400u;
+__device__ inline half2_t int4x2_to_h2(uint32_t w) {
+  uint32_t t = ((w >> (4 * P)) & 0x000F000Fu) ^ 0x64086408u;
   return u32_as_h2(t) - (half2_t){(_Float16)1032.0f, (_Float16)1032.0f};
 }
 

@@ -477,7 +477,27 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
                             "tflops": flops / (us * 1e-6) / 1e12,
                             "frac_bf16_mfma_peak": flops / (us * 1e-6) / 2.5e15}
         res["extend_attention"] = ext
-        del k_ws, v_ws, qc, oc
+        # the fused extend: the prefix straight from the 4-bit pages, no workspace
+        fused = {}
+        kc_rows, vc_rows = k_ws[L:L + n], v_ws[L:L + n]
+        lay = layers[0]
+        for lp in (32768, L):
+            reps = 1 if lp == L else 5
+            kvq.kvq_extend_attention_paged(lay.cache, lay.bt[0], lp, qc, kc_rows, vc_rows, out=oc)
+            a, b_ = ev(), ev()
+            a.record(stream)
+            for _ in range(reps):
+                kvq.kvq_extend_attention_paged(lay.cache, lay.bt[0], lp, qc, kc_rows, vc_rows, out=oc)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b_) / reps * 1e3
+            flops = 4.0 * HQ * D * (n * lp + n * (n + 1) / 2)
+            fused[str(lp)] = {"prefix_len": lp, "chunk_len": n, "us": us, "flops": flops,
+                              "tflops": flops / (us * 1e-6) / 1e12,
+                              "frac_bf16_mfma_peak": flops / (us * 1e-6) / 2.5e15,
+                              "workspace_bytes": 0}
+        res["extend_attention_fused"] = fused
+        del k_ws, v_ws, qc, oc, kc_rows, vc_rows
     keep = layers[0] if keep_for_cpu else None
     del layers, ws, chunk
     torch.cuda.empty_cache()
@@ -624,6 +644,9 @@ def main():
         "calibrate_amax": r.get("calibrate_amax"),
         "secondary": secondary,
     }
+    for k in ("chunk_store_us", "split_sweep", "dequant_prefix", "extend_attention", "extend_attention_fused"):
+        if k in r:
+            line[k] = r[k]
     if "fp8_32k" in secondary and args.workload == "ctx32k":
         f8 = secondary["fp8_32k"]
         line["fp8_comparator"] = {

@@ -287,7 +287,7 @@ kvq_status kvq_extend_attention(const void* q, int64_t q_token_stride, int32_t n
     return KVQ_ERR_ALIGN;
   const int64_t rows = (int64_t)chunk_len * (num_q_heads / num_kv_heads);
   if ((rows + 63) / 64 > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
-  kvq::ExtendParams p;
+  kvq::ExtendParams p{};
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k_ws;
   p.v = (const uint16_t*)v_ws;
@@ -304,7 +304,59 @@ kvq_status kvq_extend_attention(const void* q, int64_t q_token_stride, int32_t n
   p.num_kv_heads = num_kv_heads;
   p.group = num_q_heads / num_kv_heads;
   p.out_bf16 = out_dtype == KVQ_DT_BF16;
-  return hip_status(kvq::launch_extend(p, head_dim, (hipStream_t)stream));
+  return hip_status(kvq::launch_extend(p, head_dim, 0, (hipStream_t)stream));
+}
+
+kvq_status kvq_extend_attention_paged(const kvq_cache* cache, const int32_t* block_table_row, int32_t prefix_len,
+                                      const void* q, int64_t q_token_stride, int32_t num_q_heads, const void* k_chunk,
+                                      const void* v_chunk, int64_t chunk_token_stride, int32_t chunk_len,
+                                      float sm_scale, void* out, int32_t out_dtype, int64_t out_token_stride,
+                                      float* lse_out, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (cache->fmt == KVQ_FMT_FP8_E4M3) return KVQ_ERR_UNSUPPORTED;
+  const int32_t Hkv = cache->num_kv_heads, D = cache->head_dim;
+  if (prefix_len < 0 || chunk_len < 0 || num_q_heads <= 0 || num_q_heads % Hkv != 0) return KVQ_ERR_SHAPE;
+  if (out_dtype != KVQ_DT_F32 && out_dtype != KVQ_DT_BF16) return KVQ_ERR_UNSUPPORTED;
+  if (Hkv > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (chunk_len == 0) return KVQ_OK;
+  if (q == nullptr || k_chunk == nullptr || v_chunk == nullptr || out == nullptr) return KVQ_ERR_NULL;
+  if (prefix_len > 0 && block_table_row == nullptr) return KVQ_ERR_NULL;
+  if (q_token_stride < (int64_t)num_q_heads * D || chunk_token_stride < (int64_t)Hkv * D ||
+      out_token_stride < (int64_t)num_q_heads * D)
+    return KVQ_ERR_SHAPE;
+  const int64_t oes = out_dtype == KVQ_DT_F32 ? 4 : 2;
+  if (!aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(out) || (q_token_stride * 2) % 16 ||
+      (chunk_token_stride * 2) % 16 || (out_token_stride * oes) % 16 || (lse_out && ((uintptr_t)lse_out & 3u)))
+    return KVQ_ERR_ALIGN;
+  const int64_t rows = (int64_t)chunk_len * (num_q_heads / Hkv);
+  if ((rows + 63) / 64 > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
+  const kvq::SlabLayout lay = kvq::slab_layout(cache->fmt, cache->page_size, D);
+  kvq::ExtendParams p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k_chunk;
+  p.v = (const uint16_t*)v_chunk;
+  p.out = out;
+  p.lse = lse_out;
+  p.q_stride = q_token_stride;
+  p.kv_stride = chunk_token_stride;
+  p.out_stride = out_token_stride;
+  p.lse_stride = num_q_heads;
+  p.sm_scale = sm_scale > 0.0f ? sm_scale : 1.0f / __builtin_sqrtf((float)D);
+  p.prefix_len = prefix_len;
+  p.chunk_len = chunk_len;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = Hkv;
+  p.group = num_q_heads / Hkv;
+  p.out_bf16 = out_dtype == KVQ_DT_BF16;
+  p.pool = (const uint8_t*)cache->pool;
+  p.gs = cache->global_scale;
+  p.pages = block_table_row;
+  p.slab = lay.slab;
+  p.half = lay.half;
+  p.scales_off = lay.scales_off;
+  p.page_size = cache->page_size;
+  return hip_status(kvq::launch_extend(p, D, cache->fmt, (hipStream_t)stream));
 }
 
 kvq_status kvq_hadamard_rotate(const void* in, int32_t in_dtype, int64_t in_row_stride, void* out, int32_t out_dtype,

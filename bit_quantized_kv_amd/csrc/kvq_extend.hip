@@ -19,6 +19,14 @@
 //   online softmax in base 2 per row, lazily rescaled as in decode;
 //   PV  O^T[ch][row] += V^T[ch][token] P^T[token][row], P split into bf16
 //       hi + lo parts (two MFMAs) so the product keeps ~16 bits of each p.
+//
+// Paged variant (SRC = the cache format): the same kernel reads the prefix
+// straight from the 4-bit pages instead of a bf16 workspace -- the fused
+// extend that needs no workspace -- and the chunk's own K/V from bf16 rows.
+// Prefix codes are expanded to bf16 exactly while staged (NVFP4 e2m1 * e4m3;
+// INT4 q) and the remaining factor of each token (NVFP4: the global scale;
+// INT4: the token's scale; chunk tokens: 1) is staged per token and applied
+// to its score (K) and to its probability in the PV product (V).
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -42,11 +50,14 @@ struct ExtLds {
   static constexpr int KP = 2 * D + 16;        // bytes per staged K row (token), padded
   static constexpr int VPD = kExtStep / 2 + 3; // dwords per staged V^T row (channel): 16 used + 3 pad
   static constexpr int KB = kExtStep * KP;
-  static constexpr int BUF = KB + D * VPD * 4;
+  static constexpr int VB = D * VPD * 4;
+  static constexpr int BUF = KB + VB + 2 * kExtStep * 4;  // + per-token K and V factors
   static constexpr int TOTAL = 2 * BUF;
 };
 
-template <int D>
+constexpr int kExtWorkspace = 0;  // SRC: every key from the bf16 workspace (else the cache format)
+
+template <int D, int SRC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void extend_kernel(const ExtendParams p) {
   using Lds = ExtLds<D>;
   constexpr int KCH = D / 32, VT = D / 16;
@@ -94,27 +105,141 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   const int krow = D == 256 ? ((tid >> 2) & 3) + 4 * (tid >> 5) : tid >> 3;
   const int kseg = D == 256 ? (tid & 3) + 4 * ((tid >> 4) & 1) : tid & 7;
   const int vpair = tid & 15, vcb = tid >> 4;
+  constexpr bool PAGED = SRC != kExtWorkspace;
+  const int64_t Lp = p.prefix_len;
+  // bf16 rows: the workspace holds every token; the paged variant's rows are the chunk's
+  const int64_t row_base = PAGED ? Lp : 0;
   u32x4_t kreg[KV16], va[CPT / 8], vb[CPT / 8];
+  // paged prefix tokens: raw codes and scale words, expanded in lstore
+  u32x4_t kcode = {0u, 0u, 0u, 0u};
+  uint32_t kscw = 0u, vcode_a[CPT / 8 * 2], vcode_b[CPT / 8 * 2], vscw_a = 0u, vscw_b = 0u;
+  bool kpaged = false, vapaged = false, vbpaged = false;
+  auto page_of = [&](int64_t t, int& off) -> const uint8_t* {
+    const int64_t pi = t / p.page_size;
+    off = (int)(t - pi * p.page_size);
+    return p.pool + ((int64_t)p.pages[pi] * p.num_kv_heads + g) * p.slab;
+  };
   auto gload = [&](int step) {
     const int64_t t0 = (int64_t)step * kExtStep;
     const int64_t tk = t0 + krow;
-    const uint16_t* kp = p.k + tk * p.kv_stride + (int64_t)g * D + kseg * (D / 8);
+    kpaged = PAGED && tk < Lp;
+    if (kpaged) {
+      int off;
+      const uint8_t* sl = page_of(tk, off);
+      // elements kseg * D/8 .. : D/16 code bytes and D/128 scale bytes (NVFP4) or the row scale (INT4)
+      if (D == 256) kcode = ld_global<u32x4_t>(sl + (int64_t)off * (D / 2) + kseg * (D / 16));
+      else kcode.xy = ld_global<u32x2_t>(sl + (int64_t)off * (D / 2) + kseg * (D / 16));
+      if (SRC == FMT_NVFP4)
+        kscw = D == 256 ? ld_global<uint16_t>(sl + p.scales_off + (int64_t)off * (D / 16) + 2 * kseg)
+                        : ld_global<uint8_t>(sl + p.scales_off + (int64_t)off * (D / 16) + kseg);
+      else
+        kscw = ld_global<uint32_t>(sl + p.scales_off + (int64_t)off * 4);
+    } else {
+      const uint16_t* kp = p.k + (tk - row_base) * p.kv_stride + (int64_t)g * D + kseg * (D / 8);
 #pragma unroll
-    for (int v = 0; v < KV16; v++) kreg[v] = tk < Lk ? ld_global<u32x4_t>(kp + 8 * v) : (u32x4_t){0u, 0u, 0u, 0u};
+      for (int v = 0; v < KV16; v++)
+        kreg[v] = tk < Lk ? ld_global<u32x4_t>(kp + 8 * v) : (u32x4_t){0u, 0u, 0u, 0u};
+    }
     const int64_t ta = t0 + 2 * vpair, tb = ta + 1;
-    const uint16_t* pa = p.v + ta * p.kv_stride + (int64_t)g * D + vcb * CPT;
-    const uint16_t* pb = pa + p.kv_stride;
+    vapaged = PAGED && ta < Lp;
+    vbpaged = PAGED && tb < Lp;
 #pragma unroll
-    for (int v = 0; v < CPT / 8; v++) {
-      va[v] = ta < Lk ? ld_global<u32x4_t>(pa + 8 * v) : (u32x4_t){0u, 0u, 0u, 0u};
-      vb[v] = tb < Lk ? ld_global<u32x4_t>(pb + 8 * v) : (u32x4_t){0u, 0u, 0u, 0u};
+    for (int half = 0; half < 2; half++) {
+      const int64_t tv = half ? tb : ta;
+      const bool pg = half ? vbpaged : vapaged;
+      if (pg) {
+        int off;
+        const uint8_t* sl = page_of(tv, off) + p.half;
+        // CPT channels from vcb * CPT: CPT/2 code bytes, one NVFP4 block scale (CPT == 16) or the row scale
+        const uint8_t* cp = sl + (int64_t)off * (D / 2) + vcb * (CPT / 2);
+        uint32_t* vc = half ? vcode_b : vcode_a;
+        if (CPT == 16) {
+          const u32x2_t w = ld_global<u32x2_t>(cp);
+          vc[0] = w.x;
+          vc[1] = w.y;
+        } else {
+          vc[0] = ld_global<uint32_t>(cp);
+        }
+        uint32_t sw;
+        if (SRC == FMT_NVFP4)
+          sw = ld_global<uint8_t>(sl + p.scales_off + (int64_t)off * (D / 16) + vcb * CPT / 16);
+        else
+          sw = ld_global<uint32_t>(sl + p.scales_off + (int64_t)off * 4);
+        if (half) vscw_b = sw;
+        else vscw_a = sw;
+      } else {
+        const uint16_t* pv = p.v + (tv - row_base) * p.kv_stride + (int64_t)g * D + vcb * CPT;
+#pragma unroll
+        for (int v = 0; v < CPT / 8; v++) {
+          const u32x4_t x = tv < Lk ? ld_global<u32x4_t>(pv + 8 * v) : (u32x4_t){0u, 0u, 0u, 0u};
+          if (half) vb[v] = x;
+          else va[v] = x;
+        }
+      }
+    }
+  };
+  // bf16 pairs of 8 codes (element 0 low): NVFP4 e2m1 * block scale, exact;
+  // INT4 the integers q, exact
+  auto expand8 = [&](uint32_t w, float s, uint32_t out[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      float2_t x;
+      if (SRC == FMT_NVFP4) {
+        switch (e) {
+          case 0: x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
+          case 1: x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
+          case 2: x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
+          default: x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
+        }
+        x[0] *= s;
+        x[1] *= s;
+      } else {
+        x[0] = (float)((int)(w << (28 - 8 * e)) >> 28);
+        x[1] = (float)((int)(w << (24 - 8 * e)) >> 28);
+      }
+      out[e] = bf16x2_rne(x);
     }
   };
   auto lstore = [&](int buf) {
     uint8_t* base = lds + buf * Lds::BUF;
+    float* kfac = (float*)(base + Lds::KB + Lds::VB);
+    float* vfac = kfac + kExtStep;
+    if (PAGED && kpaged) {
+      // D/8 elements = KV16 16-byte bf16 vectors from D/32 code dwords
+      const uint32_t cw[4] = {kcode.x, kcode.y, kcode.z, kcode.w};
+#pragma unroll
+      for (int v = 0; v < KV16; v++) {
+        uint32_t o[4];
+        const float s = SRC == FMT_NVFP4 ? e4m3_decode((kscw >> (8 * (v / 2))) & 0xFFu) : 1.0f;
+        expand8(cw[v], s, o);
+        kreg[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
+      }
+    }
+    if (PAGED && kseg == 0) kfac[krow] = kpaged ? (SRC == FMT_NVFP4 ? p.gs[0] : as_f32(kscw)) : 1.0f;
 #pragma unroll
     for (int v = 0; v < KV16; v++)
       *(u32x4_t*)(base + krow * Lds::KP + kseg * (D / 4) + 16 * v) = kreg[v];
+    if (PAGED) {
+#pragma unroll
+      for (int half = 0; half < 2; half++) {
+        const bool pg = half ? vbpaged : vapaged;
+        if (!pg) continue;
+        const uint32_t* vc = half ? vcode_b : vcode_a;
+        const uint32_t sw = half ? vscw_b : vscw_a;
+        const float s = SRC == FMT_NVFP4 ? e4m3_decode(sw & 0xFFu) : 1.0f;
+#pragma unroll
+        for (int v = 0; v < CPT / 8; v++) {
+          uint32_t o[4];
+          expand8(vc[v], s, o);
+          if (half) vb[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
+          else va[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
+        }
+      }
+      if (vcb == 0) {
+        vfac[2 * vpair] = vapaged ? (SRC == FMT_NVFP4 ? p.gs[1] : as_f32(vscw_a)) : 1.0f;
+        vfac[2 * vpair + 1] = vbpaged ? (SRC == FMT_NVFP4 ? p.gs[1] : as_f32(vscw_b)) : 1.0f;
+      }
+    }
     uint32_t* vt = (uint32_t*)(base + Lds::KB);
 #pragma unroll
     for (int v = 0; v < CPT / 8; v++) {
@@ -149,12 +274,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
         sacc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[m], sacc[hh], 0, 0, 0);
       }
     }
-    float s[8];
+    float s[8], vf[8];
+    const float* kfac = (const float*)(kb + Lds::KB + Lds::VB);
+    const float* vfac = kfac + kExtStep;
     float cmax = -__builtin_inff();
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-      const int64_t kp = t0 + 16 * (e / 4) + 4 * j + (e % 4);
-      const float x = sacc[e / 4][e % 4] * sm;
+      const int tok = 16 * (e / 4) + 4 * j + (e % 4);
+      const int64_t kp = t0 + tok;
+      float x = sacc[e / 4][e % 4] * sm;
+      if (PAGED) {
+        x *= kfac[tok];
+        vf[e] = vfac[tok];
+      }
       s[e] = kp <= lim ? x : -__builtin_inff();
       cmax = fmaxf(cmax, s[e]);
     }
@@ -170,8 +302,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(s[e] - m_run), p1 = __builtin_amdgcn_exp2f(s[e + 1] - m_run);
+      float p0 = __builtin_amdgcn_exp2f(s[e] - m_run), p1 = __builtin_amdgcn_exp2f(s[e + 1] - m_run);
       l_run += p0 + p1;
+      if (PAGED) {  // the value factor of each token rides on its probability
+        p0 *= vf[e];
+        p1 *= vf[e + 1];
+      }
       const uint32_t hw = bf16x2_rne((float2_t){p0, p1});
       const float h0 = as_f32(hw << 16), h1 = as_f32(hw & 0xFFFF0000u);
       hi[e / 2] = hw;
@@ -222,24 +358,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     p.lse[(int64_t)irow * p.lse_stride + h] = l_run > 0.0f ? (m_run + log2f(l_run)) * kExtLn2 : -__builtin_inff();
 }
 
-hipError_t launch_extend(const ExtendParams& p, int head_dim, hipStream_t stream) {
+template <int D, int SRC>
+static hipError_t launch_extend_t(const ExtendParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.chunk_len * p.group;
   const dim3 grid((unsigned)((rows + kExtRows - 1) / kExtRows), (unsigned)p.num_kv_heads), block(256);
-  // the double-buffered staging (73 KB at head dim 256) is above HIP's default
+  // the double-buffered staging (74 KB at head dim 256) is above HIP's default
   // 64 KB dynamic-LDS limit per workgroup; gfx950 has 160 KB per CU
-  hipError_t e;
-  if (head_dim == 256) {
-    e = hipFuncSetAttribute((const void*)extend_kernel<256>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            ExtLds<256>::TOTAL);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((extend_kernel<256>), grid, block, ExtLds<256>::TOTAL, stream, p);
-  } else {
-    e = hipFuncSetAttribute((const void*)extend_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            ExtLds<128>::TOTAL);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((extend_kernel<128>), grid, block, ExtLds<128>::TOTAL, stream, p);
-  }
+  const hipError_t e = hipFuncSetAttribute((const void*)extend_kernel<D, SRC>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, ExtLds<D>::TOTAL);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((extend_kernel<D, SRC>), grid, block, ExtLds<D>::TOTAL, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_extend(const ExtendParams& p, int head_dim, int src_fmt, hipStream_t stream) {
+  if (head_dim == 256) {
+    if (src_fmt == FMT_NVFP4) return launch_extend_t<256, FMT_NVFP4>(p, stream);
+    if (src_fmt == FMT_INT4) return launch_extend_t<256, FMT_INT4>(p, stream);
+    return launch_extend_t<256, kExtWorkspace>(p, stream);
+  }
+  if (src_fmt == FMT_NVFP4) return launch_extend_t<128, FMT_NVFP4>(p, stream);
+  if (src_fmt == FMT_INT4) return launch_extend_t<128, FMT_INT4>(p, stream);
+  return launch_extend_t<128, kExtWorkspace>(p, stream);
 }
 
 }  // namespace kvq

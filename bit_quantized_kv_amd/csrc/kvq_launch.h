@@ -61,13 +61,19 @@ struct DecodeParams {
 
 struct ExtendParams {
   const uint16_t* q;  // bf16 [chunk_len][q_stride], head h at h * head_dim
-  const uint16_t* k;  // bf16 workspace [prefix_len + chunk_len][kv_stride]
+  const uint16_t* k;  // bf16: workspace [prefix_len + chunk_len][kv_stride], or (paged) the chunk's rows
   const uint16_t* v;
   void* out;          // [chunk_len][out_stride], bf16 or fp32
   float* lse;         // [chunk_len][lse_stride] or null
   int64_t q_stride, kv_stride, out_stride, lse_stride;
   float sm_scale;
   int32_t prefix_len, chunk_len, num_q_heads, num_kv_heads, group, out_bf16;
+  // paged prefix (the 4-bit cache read directly; unused for the workspace variant)
+  const uint8_t* pool;
+  const float* gs;
+  const int32_t* pages;
+  int64_t slab, half, scales_off;
+  int32_t page_size;
 };
 
 hipError_t launch_quantize_store(const StoreParams& p, int fmt, int head_dim, int in_bf16, hipStream_t stream);
@@ -76,7 +82,7 @@ hipError_t launch_calibrate_amax(const StoreParams& p, int head_dim, int in_bf16
 hipError_t launch_global_scale(const float* running, float* gs, hipStream_t stream);
 hipError_t launch_hadamard(const RotateParams& p, int head_dim, int in_bf16, int out_bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream_t stream);
-hipError_t launch_extend(const ExtendParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_extend(const ExtendParams& p, int head_dim, int src_fmt, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
 
 }  // namespace kvq

@@ -66,6 +66,7 @@ def lib():
         "kvq_calibrate_global_scale": (i32, [C, P, P]),
         "kvq_hadamard_rotate": (i32, [P, i32, i64, P, i32, i64, i32, i32, P]),
         "kvq_extend_attention": (i32, [P, i64, i32, P, P, i64, i32, i32, i32, i32, f32, P, i32, i64, P, P]),
+        "kvq_extend_attention_paged": (i32, [C, P, i32, P, i64, i32, P, P, i64, i32, f32, P, i32, i64, P, P]),
         "kvq_status_string": (ctypes.c_char_p, [i32]),
         "kvq_last_hip_error": (i32, []),
     }
@@ -248,4 +249,27 @@ def kvq_extend_attention(q: torch.Tensor, k_ws: torch.Tensor, v_ws: torch.Tensor
     _check("kvq_extend_attention", lib().kvq_extend_attention(
         _ptr(q), q.stride(0), Hq, _ptr(k_ws), _ptr(v_ws), k_ws.stride(0), Hkv, D, int(prefix_len), n,
         float(sm_scale), _ptr(out), odt, out.stride(0), _ptr(lse) if lse is not None else None, _stream(stream)))
+    return out
+
+
+def kvq_extend_attention_paged(cache: Cache, block_table_row: torch.Tensor, prefix_len: int, q: torch.Tensor,
+                               k_chunk: torch.Tensor, v_chunk: torch.Tensor, out: torch.Tensor | None = None,
+                               lse: torch.Tensor | None = None, sm_scale: float = 0.0,
+                               out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """Extend attention over [4-bit cached prefix | bf16 chunk]: q bf16 [n][Hq][D];
+    k_chunk, v_chunk bf16 [n][Hkv][D] (or rows of >= Hkv*D elements)."""
+    n, Hq, D = q.shape
+    assert q.dtype == torch.bfloat16 and k_chunk.dtype == torch.bfloat16 and v_chunk.dtype == torch.bfloat16
+    assert q.stride(2) == 1 and q.stride(1) == D and k_chunk.stride(0) == v_chunk.stride(0)
+    assert k_chunk.shape[0] >= n and block_table_row.dtype == torch.int32
+    if out is None:
+        out = torch.empty((n, Hq, D), dtype=out_dtype, device=q.device)
+    odt = {torch.float32: DT_F32, torch.bfloat16: DT_BF16}[out.dtype]
+    if lse is not None:
+        assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() >= n * Hq
+    d = cache.desc()
+    _check("kvq_extend_attention_paged", lib().kvq_extend_attention_paged(
+        ctypes.byref(d), _ptr(block_table_row), int(prefix_len), _ptr(q), q.stride(0), Hq, _ptr(k_chunk),
+        _ptr(v_chunk), k_chunk.stride(0), n, float(sm_scale), _ptr(out), odt, out.stride(0),
+        _ptr(lse) if lse is not None else None, _stream(stream)))
     return out

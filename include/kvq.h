@@ -210,6 +210,22 @@ kvq_status kvq_extend_attention(const void* q, int64_t q_token_stride, int32_t n
                                 int32_t prefix_len, int32_t chunk_len, float sm_scale, void* out, int32_t out_dtype,
                                 int64_t out_token_stride, float* lse_out, void* stream);
 
+/* Fused extend attention: as kvq_extend_attention, but the prefix is read
+ * straight from the 4-bit pages (cache tokens 0 .. prefix_len - 1 of the
+ * sequence whose page list is block_table_row) and decoded while staged, so
+ * no bf16 workspace is needed -- the 1M-token case of the extend path would
+ * otherwise hold a 4.3 GB workspace ("SGLang's 4-bit KV cache ...", section
+ * "The 1.78x is arithmetic ...": the 1M run handed 15 % of the GPU back for
+ * prefill workspace).  The chunk's own K/V come as bf16 rows k_chunk, v_chunk
+ * [chunk_len][chunk_token_stride] (head g at g * head_dim).  NVFP4 and INT4
+ * caches (FP8: KVQ_ERR_UNSUPPORTED); for a rotated cache the caller passes
+ * rotated q and chunk rows and rotates the output back. */
+kvq_status kvq_extend_attention_paged(const kvq_cache* cache, const int32_t* block_table_row, int32_t prefix_len,
+                                      const void* q, int64_t q_token_stride, int32_t num_q_heads, const void* k_chunk,
+                                      const void* v_chunk, int64_t chunk_token_stride, int32_t chunk_len,
+                                      float sm_scale, void* out, int32_t out_dtype, int64_t out_token_stride,
+                                      float* lse_out, void* stream);
+
 /* Global-scale calibration for NVFP4 ("SGLang's 4-bit KV cache ...",
  * section '"Near-lossless" is narrower than it sounds': the measured NVFP4
  * drops its per-tensor FP32 scale, which leaves the E4M3 block scale to carry

@@ -231,3 +231,33 @@ def test_extend_attention_validation(lib):
     args = list(a)
     args[8] = -1
     assert f(*args) == ERR_SHAPE
+
+
+def test_extend_attention_paged_validation(lib):
+    f = lib.kvq_extend_attention_paged
+    c = cache()
+    ok = [ctypes.byref(c), FAKE, 100, FAKE, 24 * 256, 24, FAKE, FAKE, 4 * 256, 0, 0.0, FAKE, 1, 24 * 256, None, None]
+    assert f(*ok) == OK                                           # empty chunk
+    a = list(ok)
+    a[9] = 8
+    for i, v, want in [(1, None, ERR_NULL),                       # a prefix needs its page list
+                       (3, None, ERR_NULL), (6, None, ERR_NULL), (11, None, ERR_NULL),
+                       (5, 25, ERR_SHAPE),                        # Hq not a multiple of Hkv
+                       (2, -1, ERR_SHAPE), (8, 4 * 256 - 8, ERR_SHAPE), (4, 24 * 256 - 8, ERR_SHAPE),
+                       (3, FAKE + 4, ERR_ALIGN), (4, 24 * 256 + 4, ERR_ALIGN),
+                       (12, 9, ERR_UNSUPPORTED)]:
+        args = list(a)
+        args[i] = v
+        assert f(*args) == want, (i, v, want)
+    args = list(a)
+    args[1], args[2] = None, 0                                    # no prefix: no page list needed
+    args[9] = 0
+    assert f(*args) == OK
+    fp8 = cache(fmt=3)
+    args = list(a)
+    args[0] = ctypes.byref(fp8)
+    assert f(*args) == ERR_UNSUPPORTED                            # the FP8 comparator has no fused extend
+    bad = cache(fmt=7)
+    args = list(a)
+    args[0] = ctypes.byref(bad)
+    assert f(*args) != OK

@@ -66,3 +66,79 @@ def test_extend_path_over_a_4bit_prefix(fmt):
     ref, _ = oracle.extend_attention(q.float().cpu().numpy(), kw.float().cpu().numpy(), vw.float().cpu().numpy(), Lp)
     s = max(1.0, float(np.abs(ref).max()))
     check_attention(out.cpu().numpy() / s, ref / s, np.ones(n, np.int32), label="extend path")
+
+
+PAGED = [
+    # fmt, D, Hkv, G, P, prefix_len, chunk_len, gs
+    (1, 256, 2, 6, 16, 700, 96, (0.37, 2.5)),
+    (2, 256, 2, 6, 16, 700, 96, (1.0, 1.0)),
+    (1, 256, 1, 4, 32, 64, 33, (1.0, 1.0)),
+    (2, 256, 1, 16, 48, 5, 40, (1.0, 1.0)),
+    (1, 128, 2, 4, 16, 37, 70, (1.0, 0.125)),
+    (2, 128, 3, 3, 16, 300, 17, (1.0, 1.0)),
+    (1, 256, 2, 6, 16, 0, 50, (0.5, 0.5)),
+]
+
+
+def _prefix_values(c, Lp):
+    """The cached prefix of sequence 0 as the oracle's exact dequantized rows [Lp][Hkv][D]."""
+    P = c.P
+    k = np.zeros((Lp, c.Hkv, c.D))
+    v = np.zeros((Lp, c.Hkv, c.D))
+    for t in range(Lp):
+        page, off = int(c.bt[0, t // P]), t % P
+        for g in range(c.Hkv):
+            k[t, g] = c.ref.dequant_token(page, g, off, 0)
+            v[t, g] = c.ref.dequant_token(page, g, off, 1)
+    return k, v
+
+
+@pytest.mark.parametrize("fmt,D,Hkv,G,P,Lp,n,gs", PAGED)
+def test_extend_paged_matches_oracle(fmt, D, Hkv, G, P, Lp, n, gs):
+    """The fused extend reads the prefix from the 4-bit pages: same result as the
+    oracle's extend over [exactly dequantized prefix | bf16 chunk]."""
+    print(f"case: paged extend fmt {fmt} D {D} Hkv {Hkv} G {G} P {P} Lp {Lp} n {n} gs {gs}", flush=True)
+    from gpu_cases import ATOL, Case, bf16_half_ulp
+    c = Case(fmt, D, Hkv, G, P, [max(Lp, 1)], kind="lognormal", in_dtype=torch.bfloat16, gs=gs, seed=500 + Lp + D)
+    Hq = Hkv * G
+    kc, vc = inputs.kv_lognormal_channels(57, Lp, n, Hkv, D)
+    kc_d, vc_d = bf16(kc).cuda(), bf16(vc).cuda()
+    q = bf16(inputs.query(57, 7, n, Hq, D).reshape(n, Hq, D)).cuda()
+    lse = torch.empty((n, Hq), dtype=torch.float32, device="cuda")
+    bt = c.bt_dev[0].contiguous()
+    out = kvq.kvq_extend_attention_paged(c.cache, bt, Lp, q, kc_d, vc_d, lse=lse, out_dtype=torch.float32)
+    outb = kvq.kvq_extend_attention_paged(c.cache, bt, Lp, q, kc_d, vc_d, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    kp, vp = _prefix_values(c, Lp)
+    k_all = np.concatenate([kp, kc_d.float().cpu().numpy()])
+    v_all = np.concatenate([vp, vc_d.float().cpu().numpy()])
+    ref, ref_lse = oracle.extend_attention(q.float().cpu().numpy(), k_all, v_all, Lp)
+    s = max(1.0, float(np.abs(ref).max()))
+    check_attention(out.cpu().numpy() / s, ref / s, np.ones(n, np.int32), lse=lse.cpu().numpy(), ref_lse=ref_lse,
+                    label="paged fp32")
+    err = np.abs(outb.float().cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= ATOL * s + bf16_half_ulp(ref)), err.max()
+
+
+def test_extend_paged_agrees_with_workspace_path():
+    """Fused and workspace extend over the same NVFP4 prefix: the same keys and
+    values reach the MFMAs (the fused path folds the global scale into score and
+    probability), so the outputs agree to fp32 rounding."""
+    print("case: paged vs workspace extend", flush=True)
+    from gpu_cases import Case
+    D, Hkv, G, P, Lp, n = 256, 2, 4, 16, 1000, 128
+    c = Case(1, D, Hkv, G, P, [Lp], kind="outliers", in_dtype=torch.bfloat16, gs=(0.25, 4.0), seed=77)
+    kc, vc = inputs.kv_lognormal_channels(58, 0, n, Hkv, D)
+    q = bf16(inputs.query(58, 1, n, Hkv * G, D).reshape(n, Hkv * G, D)).cuda()
+    kw = torch.empty((Lp + n, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    vw = torch.empty_like(kw)
+    kvq.kvq_dequant_prefix(c.cache, c.bt_dev[0], Lp, kw, vw)
+    kw[Lp:] = bf16(kc).cuda()
+    vw[Lp:] = bf16(vc).cuda()
+    ws = kvq.kvq_extend_attention(q, kw, vw, Lp, out_dtype=torch.float32)
+    fused = kvq.kvq_extend_attention_paged(c.cache, c.bt_dev[0].contiguous(), Lp, q, kw[Lp:], vw[Lp:],
+                                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    a, b = ws.cpu().numpy(), fused.cpu().numpy()
+    s = max(1.0, float(np.abs(a).max()))
+    assert np.abs(a - b).max() <= 1e-3 * s

@@ -5,20 +5,30 @@
 
 namespace kvq {
 
-// Grid-stride read of n16 16-byte vectors, consecutive lanes on consecutive
-// vectors; the XOR of everything read decides one conditional store, so no
-// load can be dropped.  (A variant with four loads a grid-stride apart in
-// flight per thread measured slower.)
-__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restrict__ a, int64_t n16,
+// Grid-stride read of n16 16-byte vectors with the loads the decode kernel
+// uses for cache pages (raw buffer loads, sc0 + nt policy): a workgroup takes
+// 256 consecutive vectors per iteration through one descriptor, one vector
+// per lane; the XOR of everything read decides one conditional store, so no
+// load can be dropped.  Measured over 4 GiB: 2048 workgroups of 256 at
+// 7.1-7.2 TB/s; 1024 or 4096 workgroups, 512- or 1024-thread workgroups, a
+// contiguous range per workgroup with 1-8 loads in flight per thread: no
+// faster; without the nt policy 5.7-6.4 TB/s.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* __restrict__ a, int64_t n16,
                                                           uint32_t* sink) {
   u32x4_t acc = {0u, 0u, 0u, 0u};
   const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) acc ^= ld_global<u32x4_t>(a + i);
+  for (int64_t i0 = (int64_t)blockIdx.x * 256; i0 < n16; i0 += stride) {
+    // the descriptor's record count clips the last, partial block
+    const int nrec = (int)(min((int64_t)256, n16 - i0) * 16);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a + i0 * 16), (short)0, nrec, 0x00020000);
+    acc ^= __builtin_amdgcn_raw_buffer_load_b128(r, (int)threadIdx.x * 16, 0, kLoadStream);
+  }
   if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[0] = 1u;
 }
 
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t stream) {
-  hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(256), 0, stream, (const u32x4_t*)buf, bytes / 16,
+  hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(256), 0, stream, (const uint8_t*)buf, bytes / 16,
                      sink);
   return hipGetLastError();
 }

@@ -163,27 +163,29 @@ struct Decoder : PageWalk {
       const int so = (int)p.scales_off + off * (FMT == FMT_NVFP4 ? D / 16 : 4);
       // K codes: row off + r, bytes 64v + 16j
 #pragma unroll
-      for (int v = 0; v < VEC; v++) R.kw[h][v] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo_k + 64 * v, ko, 0);
+      for (int v = 0; v < VEC; v++)
+        R.kw[h][v] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo_k + 64 * v, ko, kLoadStream);
       if (FMT == FMT_NVFP4) {
 #pragma unroll
-        for (int v = 0; v < VEC; v++) R.ks[h][v] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_ks + 8 * v, so, 0);
+        for (int v = 0; v < VEC; v++)
+          R.ks[h][v] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_ks + 8 * v, so, kLoadStream);
         // Lane (j, r) with quad Q = r / 4 loads the dword of V-scale row 4j + r%4
         // that holds block (r * D / 256), the block every lane of quad Q needs;
         // compute() broadcasts row i of the quad with a DPP quad_perm.
-        R.vs[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_vs_h, so, 0);
+        R.vs[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_vs_h, so, kLoadStream);
       } else {
-        R.ksc[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_sc, so, 0);
-        R.vsc[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_sc_h, so, 0);
+        R.ksc[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_sc, so, kLoadStream);
+        R.vsc[h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_sc_h, so, kLoadStream);
       }
       // V codes: rows off + 4j + i, the lane's D/32-byte segment r
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         if (VW == 2) {
-          const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo_v_h + i * (D / 2), ko, 0);
+          const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo_v_h + i * (D / 2), ko, kLoadStream);
           R.vw[h][i][0] = w.x;
           R.vw[h][i][VW - 1] = w.y;
         } else {
-          R.vw[h][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_v_h + i * (D / 2), ko, 0);
+          R.vw[h][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_v_h + i * (D / 2), ko, kLoadStream);
         }
       }
     }
@@ -680,10 +682,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     const __amdgpu_buffer_rsrc_t rs = walk.slab_rsrc(__builtin_amdgcn_readfirstlane(page));
     const int off = __builtin_amdgcn_readfirstlane(row0);
 #pragma unroll
-    for (int w = 0; w < KW; w++) R.kw[w] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo_k + 64 * w, off * D, 0);
+    for (int w = 0; w < KW; w++)
+      R.kw[w] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo_k + 64 * w, off * D, kLoadStream);
 #pragma unroll
     for (int t = 0; t < VT; t++)
-      R.vw[t] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_v, __builtin_amdgcn_readfirstlane(off + 16 * t * P), 0);
+      R.vw[t] =
+          __builtin_amdgcn_raw_buffer_load_b32(rs, vo_v, __builtin_amdgcn_readfirstlane(off + 16 * t * P), kLoadStream);
   };
 
   // q operand: lane (j, n) holds query n, channels 64(m/2) + 16j + 8(m%2) + e

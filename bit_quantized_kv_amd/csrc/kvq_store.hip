@@ -26,14 +26,14 @@ struct Row16;
 template <>
 struct Row16<float> {
   __device__ static void load(const void* p, float x[16]) {
-    const float4* v = (const float4*)p;
+    const u32x4_t* v = (const u32x4_t*)p;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      float4 a = v[i];
-      x[4 * i + 0] = a.x;
-      x[4 * i + 1] = a.y;
-      x[4 * i + 2] = a.z;
-      x[4 * i + 3] = a.w;
+      const u32x4_t a = ld_stream<u32x4_t>(v + i);  // rows are read once: non-temporal
+      x[4 * i + 0] = as_f32(a.x);
+      x[4 * i + 1] = as_f32(a.y);
+      x[4 * i + 2] = as_f32(a.z);
+      x[4 * i + 3] = as_f32(a.w);
     }
   }
 };
@@ -41,10 +41,10 @@ struct Row16<float> {
 template <>
 struct Row16<uint16_t> {  // bf16 bit patterns, widened exactly
   __device__ static void load(const void* p, float x[16]) {
-    const uint4* v = (const uint4*)p;
+    const u32x4_t* v = (const u32x4_t*)p;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-      uint4 a = v[i];
+      const u32x4_t a = ld_stream<u32x4_t>(v + i);
       uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
       for (int j = 0; j < 4; j++) {
@@ -436,11 +436,11 @@ __device__ inline void dequant_rows(const DequantParams& p, int kv, int g, int t
       half = pool + (int64_t)p.pages[pidx] * page_bytes;
       off = poff + rr;
     }
-    w[k] = ld_global<uint32_t>(half + (uint32_t)(off * (D / 2) + 4 * c));
+    w[k] = ld_stream<uint32_t>(half + (uint32_t)(off * (D / 2) + 4 * c));
     if (FMT == FMT_NVFP4)
-      sc[k] = ld_global<uint8_t>(half + (uint32_t)(p.scales_off + off * NB + (c >> 1)));
+      sc[k] = ld_stream<uint8_t>(half + (uint32_t)(p.scales_off + off * NB + (c >> 1)));
     else
-      sc[k] = ld_global<uint32_t>(half + (uint32_t)(p.scales_off + off * 4));
+      sc[k] = ld_stream<uint32_t>(half + (uint32_t)(p.scales_off + off * 4));
   }
   const float gs = FMT == FMT_NVFP4 ? p.gs[kv] : 1.0f;
   uint16_t* out = (kv ? p.v_out : p.k_out) + (int64_t)g * D + 8 * c;

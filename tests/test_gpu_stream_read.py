@@ -1,0 +1,28 @@
+"""The bandwidth reference kernel reads every byte it is given: each lane
+XORs the 16-byte vectors it reads and sets the sink when the result is the
+mark, so one marked vector placed anywhere (including a ragged last block)
+must be seen, and two marks read by the same lane must cancel."""
+import pytest
+import torch
+
+from bit_quantized_kv_amd import kvq
+
+pytestmark = pytest.mark.gpu
+
+MARK = 0x9E3779B9
+
+
+@pytest.mark.parametrize("n16,where,wgs,want", [
+    (256 * 5 + 37, [256 * 5 + 36], 0, 1), (256 * 5 + 37, [3], 2, 1), (4096, [4095], 7, 1), (1, [0], 0, 1),
+    (300, [17, 273], 1, 0),   # one workgroup: lane 17 reads both marks, they cancel
+    (300, [17, 299], 1, 1),   # different lanes
+])
+def test_stream_read_sees_every_vector(n16, where, wgs, want):
+    print(f"case: stream read n16 {n16} marks {where} wgs {wgs}", flush=True)
+    buf = torch.zeros((n16, 4), dtype=torch.int32, device="cuda")
+    for i in where:
+        buf[i, 1] = MARK - (1 << 32)  # int32 view of the mark
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kvq.kvq_stream_read(buf, sink, num_workgroups=wgs)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == want

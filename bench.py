@@ -210,7 +210,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--num-splits", type=int, default=0, help="decode split count (0 = the library's plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+                    help="target wall time of one CPU-oracle run (the median of 3 is reported)")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (profiler counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -395,11 +396,14 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
     torch.cuda.synchronize()
     store_ms = sum(a.elapsed_time(b) for a, b, _ in pairs) / len(pairs)
     decode_ms = sum(b.elapsed_time(c) for _, b, c in pairs) / len(pairs)
+    decode_sorted = sorted(b.elapsed_time(c) for _, b, c in pairs)
+    decode_median_ms = decode_sorted[len(decode_sorted) // 2]
     kv_bytes_layer = B * L * HKV * token_head_bytes(fmt)
     res = {
         "workload": name, "desc": w["desc"], "format": {1: "nvfp4", 2: "int4_per_token_head", 3: "fp8_e4m3_per_tensor"}[fmt],
         "batch": B, "context": L, "page_size": P, "layers": n_layers, "num_splits": splits,
-        "step_ms": step_ms, "decode_call_us": decode_ms * 1e3, "store_call_us": store_ms * 1e3,
+        "step_ms": step_ms, "decode_call_us": decode_ms * 1e3, "decode_call_us_median": decode_median_ms * 1e3,
+        "decode_call_calls_timed": len(decode_sorted), "store_call_us": store_ms * 1e3,
         "kv_bytes_per_layer": kv_bytes_layer,
         "effective_kv_gbs": n_layers * kv_bytes_layer / (step_ms * 1e-3) / 1e9,
         "decode_call_gbs": kv_bytes_layer / (decode_ms * 1e-3) / 1e9,
@@ -558,11 +562,18 @@ def cpu_baseline(torch, lay, w, target_s):
         pool.decode_attention(q, bt, np.full(nseq, L, np.int32))
         return time.perf_counter() - t
 
-    t1 = run(1)
+    t1 = run(1)  # also the warm-up
     n = int(max(1, min(w["batch"], round(target_s / max(t1, 1e-3)))))
-    t = run(n) if n > 1 else t1
+    runs = sorted(run(n) for _ in range(3))
+    t = runs[1]  # median of 3
     nbytes = n * L * HKV * token_head_bytes(w["fmt"])
     threads = oracle.num_threads()
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((x.split(":", 1)[1].strip() for x in f if x.startswith("model name")), "")
+    except OSError:
+        pass
     # the same oracle on one thread, one sequence
     oracle.set_num_threads(1)
     try:
@@ -571,8 +582,10 @@ def cpu_baseline(torch, lay, w, target_s):
         oracle.set_num_threads(threads)
     return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"1 layer, {n} of {w['batch']} sequences x {L} tokens, all {HQ} query heads, fp64 attention "
-                      f"over the same packed pages ({t:.1f} s)",
-            "seconds": t, "tokens_per_s_16_layers_extrapolated": n / (t * LAYERS),
+                      f"over the same packed pages (median of 3 runs of {t:.1f} s after a warm-up)",
+            "seconds": t, "seconds_runs": runs, "nproc": os.cpu_count(), "cpu_model": cpu_model,
+            "tokens_per_s_16_layers_extrapolated": n / (t * LAYERS),
+            "extrapolation": "one layer timed, x16 layers assumed for the stack",
             "one_thread": {"value": L * HKV * token_head_bytes(w["fmt"]) / t_one / 1e9, "unit": "GB/s",
                            "sample": f"1 sequence, 1 thread ({t_one:.1f} s)"}}
 
@@ -650,6 +663,7 @@ def main():
                      "kernel": "kvq_decode_attention call (decode_kernel + merge_kernel)",
                      "algorithmic_bytes_per_launch": r["kv_bytes_per_layer"],
                      "avg_launch_us": r["decode_call_us"],
+                     "median_launch_us": r["decode_call_us_median"],
                      "frac_of_measured_read_ceiling": r["decode_call_gbs"] / ceiling["gbs"]},
         "hbm_read_ceiling": ceiling,
         "cpu_baseline": cpu,

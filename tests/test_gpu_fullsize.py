@@ -215,3 +215,52 @@ def test_full_extend_4096_over_32k_prefix():
         ref, ref_lse = oracle.extend_attention(qh[i:i + 1], kh, vh, Lp + i)
         check_attention(out[i:i + 1], ref, np.ones(1, np.int32), lse=lse[i:i + 1], ref_lse=ref_lse,
                         label=f"extend row {i}")
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_full_fused_extend_4096_over_32k_cached_prefix(fmt):
+    # the fused extend at the bench's shape: a 4,096-token bf16 chunk over a
+    # 32K prefix read from the 4-bit pages; the same input rows quantized by
+    # the oracle give the prefix values (the two pools are compared byte for
+    # byte first), sampled query rows against the oracle run row by row
+    print(f"case: full fused extend 4096 over 32K, fmt {fmt}", flush=True)
+    Lp, n, P = 32768, 4096, 16
+    pps = Lp // P
+    g = torch.Generator(device="cuda")
+    g.manual_seed(inputs.seed_int(8, fmt, inputs.STREAM_K))
+    kp = torch.randn((Lp, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    vp = torch.randn((Lp, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    kc = torch.randn((n, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((n, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((n, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
+    bt = inputs.page_tables(8, 1, pps, pps, shuffled=True)[0]
+    slots = inputs.slots_for(bt[None], P, 0, 0, Lp)
+    cache = kvq.Cache(fmt, pps, P, HKV, D, device="cuda")
+    kvq.kvq_quantize_store(cache, kp, vp, torch.from_numpy(slots).cuda())
+    lse = torch.empty((n, HQ), dtype=torch.float32, device="cuda")
+    out = kvq.kvq_extend_attention_paged(cache, torch.from_numpy(bt).cuda(), Lp, q, kc, vc, lse=lse,
+                                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_pool = oracle.Pool(fmt, pps, P, HKV, D)
+    ref_pool.quantize_store(kp.float().cpu().numpy(), vp.float().cpu().numpy(), slots)
+    assert np.array_equal(cache.pool.cpu().numpy(), ref_pool.data), "cache bytes differ from the oracle's"
+    # prefix values: exact dequantization (bf16 holds e2m1 x e4m3 exactly at gs = 1; INT4 rows as q x s)
+    if fmt == 1:
+        kq, vq = ref_pool.dequant_prefix(bt, Lp)
+        kq = (kq.astype(np.uint32) << 16).view(np.float32)
+        vq = (vq.astype(np.uint32) << 16).view(np.float32)
+    else:
+        kq = np.zeros((Lp, HKV, D), np.float32)
+        vq = np.zeros((Lp, HKV, D), np.float32)
+        for t in range(Lp):
+            for h in range(HKV):
+                kq[t, h] = ref_pool.dequant_token(int(bt[t // P]), h, t % P, 0)
+                vq[t, h] = ref_pool.dequant_token(int(bt[t // P]), h, t % P, 1)
+    kh = np.concatenate([kq, kc.float().cpu().numpy()])
+    vh = np.concatenate([vq, vc.float().cpu().numpy()])
+    qh = q.float().cpu().numpy()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for i in (0, 1, 63, 64, 2047, 4095):
+        ref, ref_lse = oracle.extend_attention(qh[i:i + 1], kh, vh, Lp + i)
+        check_attention(out[i:i + 1], ref, np.ones(1, np.int32), lse=lse[i:i + 1], ref_lse=ref_lse,
+                        label=f"fused extend row {i}")

@@ -202,10 +202,12 @@ struct Decoder : PageWalk {
       a2 = e2m1x2_to_h2_x256<2>(word) * s2;
       a3 = e2m1x2_to_h2_x256<3>(word) * s2;
     } else {
+      // pairs 1 and 3 come out times 16; their query channels carry 1/16
+      const uint32_t w8 = word >> 8;
       a0 = int4x2_to_h2<0>(word);
-      a1 = int4x2_to_h2<1>(word);
-      a2 = int4x2_to_h2<2>(word);
-      a3 = int4x2_to_h2<3>(word);
+      a1 = int4x2_hi_to_h2_x16(word);
+      a2 = int4x2_to_h2<0>(w8);
+      a3 = int4x2_hi_to_h2_x16(w8);
     }
     return (half8_t){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
   }
@@ -296,7 +298,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
   for (int c = 0; c < KCH; c++) {
 #pragma unroll
-    for (int e = 0; e < 8; e++) qop[c][e] = (_Float16)ldexpf(qf[c][e], kq);
+    for (int e = 0; e < 8; e++) {
+      // INT4: elements 2, 3, 6, 7 meet K pairs decoded times 16 (k_operand)
+      const int ke = FMT == FMT_INT4 && (e & 2) ? kq - 4 : kq;
+      qop[c][e] = (_Float16)ldexpf(qf[c][e], ke);
+    }
   }
   const float sm = p.sm_scale * kLog2e * ldexpf(1.0f, -kq) * (FMT == FMT_NVFP4 ? p.gs[0] : 1.0f);
 
@@ -485,23 +491,23 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
               pw[h][pp] = byte_perm(bb, a, sel == 0 ? 0x05040100u : 0x07060302u);
             }
           }
+          uint32_t pw8[2][2];  // the words shifted by 8 (nibble positions 2, 3 -> 0, 1)
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+#pragma unroll
+            for (int pp = 0; pp < 2; pp++) pw8[h][pp] = pw[h][pp] >> 8;
+          }
 #pragma unroll
           for (int k = 0; k < 4; k++) {
+            // odd tiles come out times 16, undone with the output scale
             const int t = 8 * d + 4 * sel + k;
             half2_t parts[4];
 #pragma unroll
             for (int h = 0; h < 2; h++) {
 #pragma unroll
               for (int pp = 0; pp < 2; pp++) {
-                const uint32_t word = pw[h][pp];
-                half2_t x;
-                switch (k) {
-                  case 0: x = int4x2_to_h2<0>(word); break;
-                  case 1: x = int4x2_to_h2<1>(word); break;
-                  case 2: x = int4x2_to_h2<2>(word); break;
-                  default: x = int4x2_to_h2<3>(word); break;
-                }
-                parts[2 * h + pp] = x;
+                const uint32_t word = k < 2 ? pw[h][pp] : pw8[h][pp];
+                parts[2 * h + pp] = (k & 1) ? int4x2_hi_to_h2_x16(word) : int4x2_to_h2<0>(word);
               }
             }
             const half8_t a = {parts[0][0], parts[0][1], parts[1][0], parts[1][1],
@@ -589,8 +595,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         float* row = dst + (4 * j + rr) * VT;
 #pragma unroll
         for (int t = 0; t < VT; t += 4) {
-          float4 x = make_float4(oacc[t][rr] * scale_o, oacc[t + 1][rr] * scale_o, oacc[t + 2][rr] * scale_o,
-                                 oacc[t + 3][rr] * scale_o);
+          // INT4: odd tiles were accumulated from values times 16
+          const float so = FMT == FMT_INT4 ? scale_o * 0.0625f : scale_o;
+          float4 x = make_float4(oacc[t][rr] * scale_o, oacc[t + 1][rr] * so, oacc[t + 2][rr] * scale_o,
+                                 oacc[t + 3][rr] * so);
           if (w > 0) {
             const float4 y = *(float4*)(row + t);
             x.x += y.x;

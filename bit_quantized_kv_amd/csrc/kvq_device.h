@@ -170,4 +170,15 @@ __device__ inline half2_t int4x2_to_h2(uint32_t w) {
   return u32_as_h2(t) - (half2_t){(_Float16)1032.0f, (_Float16)1032.0f};
 }
 
+// The same for the nibbles at positions 1 and 5 without a shift: left in
+// place they land 4 bits up in the mantissa of 1024 (the XOR with 0x0080
+// flips their sign bit), so the result is (16 q_1, 16 q_5), exact; the caller
+// undoes the factor 16 where it is cheap (the query, the output).  With the
+// word shifted right by 8 once, int4x2_to_h2<0> and this serve positions 2, 6
+// and 3, 7: one shift per word instead of three.
+__device__ inline half2_t int4x2_hi_to_h2_x16(uint32_t w) {
+  uint32_t t = (w & 0x00F000F0u) ^ 0x64806480u;
+  return u32_as_h2(t) - (half2_t){(_Float16)1152.0f, (_Float16)1152.0f};
+}
+
 }  // namespace kvq

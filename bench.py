@@ -206,7 +206,11 @@ def parse():
     ap.add_argument("--workload", default="ctx32k", choices=sorted(WORKLOADS))
     ap.add_argument("--secondary", default="ctx160k,ctx1m,int4_220k,fp8_32k,rot_32k",
                     help="comma-separated extra workloads to report ('' for none)")
-    ap.add_argument("--secondary-steps", type=int, default=5)
+    ap.add_argument("--cooldown", type=float, default=10.0,
+                    help="idle seconds before each secondary workload (measured: a workload run right after "
+                         "another ran up to 10 %% slower, the same workload after a 10 s pause did not)")
+    ap.add_argument("--secondary-steps", type=int, default=0,
+                    help="timed steps of each secondary workload (0 = --steps; warm-up = --warmup)")
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--num-splits", type=int, default=0, help="decode split count (0 = the library's plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -358,25 +362,20 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def step(timed_pairs=None):
+    def decode_only(lay):
+        if w.get("rotated"):
+            kvq.kvq_hadamard_rotate(lay.q, out=lay.q_rot)
+            kvq.kvq_decode_attention(lay.cache, lay.q_rot, lay.bt, lay.lens, L, out=lay.out_rot, workspace=ws,
+                                     num_splits=splits)
+            kvq.kvq_hadamard_rotate(lay.out_rot, out=lay.out)
+        else:
+            kvq.kvq_decode_attention(lay.cache, lay.q, lay.bt, lay.lens, L, out=lay.out, workspace=ws,
+                                     num_splits=splits)
+
+    def step():
         for lay in layers:
-            a, b_, c = (ev(), ev(), ev()) if timed_pairs is not None else (None, None, None)
-            if a is not None:
-                a.record(stream)
             kvq.kvq_quantize_store(lay.cache, lay.k_new, lay.v_new, lay.slots_new)
-            if a is not None:
-                b_.record(stream)
-            if w.get("rotated"):
-                kvq.kvq_hadamard_rotate(lay.q, out=lay.q_rot)
-                kvq.kvq_decode_attention(lay.cache, lay.q_rot, lay.bt, lay.lens, L, out=lay.out_rot, workspace=ws,
-                                         num_splits=splits)
-                kvq.kvq_hadamard_rotate(lay.out_rot, out=lay.out)
-            else:
-                kvq.kvq_decode_attention(lay.cache, lay.q, lay.bt, lay.lens, L, out=lay.out, workspace=ws,
-                                         num_splits=splits)
-            if a is not None:
-                c.record(stream)
-                timed_pairs.append((a, b_, c))
+            decode_only(lay)
 
     for _ in range(warmup):
         step()
@@ -389,21 +388,37 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
     t_end.record(stream)
     torch.cuda.synchronize()
     step_ms = t_start.elapsed_time(t_end) / steps
-    # per-call timing (events between launches on the same stream)
-    pairs = []
+    # per-call timing.  Decode: back to back over the layers, one event pair per
+    # pass (the host queues calls faster than the GPU runs them, so no launch
+    # wait lands inside the events).  Store (a few us, shorter than its launch
+    # on the host): an event pair around each store inside the normal step,
+    # where the decode calls keep the GPU busy while the host queues the next.
+    dec_marks = [(ev(), ev()) for _ in range(steps)]
+    for a, b_ in dec_marks:
+        a.record(stream)
+        for lay in layers:
+            decode_only(lay)
+        b_.record(stream)
+    st_marks = [(ev(), ev()) for _ in range(steps * len(layers))]
+    it = iter(st_marks)
     for _ in range(steps):
-        step(pairs)
+        for lay in layers:
+            a, b_ = next(it)
+            a.record(stream)
+            kvq.kvq_quantize_store(lay.cache, lay.k_new, lay.v_new, lay.slots_new)
+            b_.record(stream)
+            decode_only(lay)
     torch.cuda.synchronize()
-    store_ms = sum(a.elapsed_time(b) for a, b, _ in pairs) / len(pairs)
-    decode_ms = sum(b.elapsed_time(c) for _, b, c in pairs) / len(pairs)
-    decode_sorted = sorted(b.elapsed_time(c) for _, b, c in pairs)
-    decode_median_ms = decode_sorted[len(decode_sorted) // 2]
+    per = sorted(a.elapsed_time(b_) / len(layers) for a, b_ in dec_marks)
+    decode_ms, decode_median_ms = sum(per) / len(per), per[len(per) // 2]
+    store_ms = sum(a.elapsed_time(b_) for a, b_ in st_marks) / len(st_marks)
     kv_bytes_layer = B * L * HKV * token_head_bytes(fmt)
     res = {
         "workload": name, "desc": w["desc"], "format": {1: "nvfp4", 2: "int4_per_token_head", 3: "fp8_e4m3_per_tensor"}[fmt],
         "batch": B, "context": L, "page_size": P, "layers": n_layers, "num_splits": splits,
         "step_ms": step_ms, "decode_call_us": decode_ms * 1e3, "decode_call_us_median": decode_median_ms * 1e3,
-        "decode_call_calls_timed": len(decode_sorted), "store_call_us": store_ms * 1e3,
+        "decode_call_calls_timed": steps * len(layers), "decode_call_median_over": "passes over the layers",
+        "store_call_us": store_ms * 1e3,
         "kv_bytes_per_layer": kv_bytes_layer,
         "effective_kv_gbs": n_layers * kv_bytes_layer / (step_ms * 1e-3) / 1e9,
         "decode_call_gbs": kv_bytes_layer / (decode_ms * 1e-3) / 1e9,
@@ -613,12 +628,17 @@ def main():
                                   keep_for_cpu=not args.no_cpu_baseline, num_splits=args.num_splits)
     print(f"[bench] {args.workload}: step {main_res['step_ms']:.3f} ms, decode call {main_res['decode_call_us']:.1f} us "
           f"({main_res['decode_call_gbs']:.0f} GB/s), {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    time.sleep(args.cooldown)  # the ceiling from the same idle state as the headline
     ceiling = read_ceiling(torch, kvq, args.steps)
     print(f"[bench] plain streaming read: {ceiling['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     secondary = {}
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
         t1 = time.time()
-        r, _ = run_workload(torch, kvq, inputs, name, args.secondary_steps, 2, args.layers)
+        # same timing protocol as the headline, from the same idle GPU state
+        torch.cuda.synchronize()
+        time.sleep(args.cooldown)
+        r, _ = run_workload(torch, kvq, inputs, name, args.secondary_steps or args.steps, args.warmup, args.layers)
         secondary[name] = r
         print(f"[bench] {name}: step {r['step_ms']:.3f} ms, decode call {r['decode_call_us']:.1f} us "
               f"({r['decode_call_gbs']:.0f} GB/s), {time.time() - t1:.1f} s", file=sys.stderr, flush=True)

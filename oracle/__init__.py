@@ -26,6 +26,7 @@ import numpy as np
 NVFP4 = 1
 INT4 = 2
 FP8 = 3  # E4M3 with one FP32 scale per tensor: the comparator format
+K8V4 = 4  # FP8 (E4M3, per-tensor scale) keys with NVFP4 values
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
@@ -249,8 +250,8 @@ class Pool:
     def dequant_prefix(self, pages, prefix_len: int, out_token_stride: int | None = None):
         """Returns (k_out, v_out) as uint16 bf16 bit patterns [prefix_len][Hkv][D]
         (or [prefix_len][out_token_stride] when a wider stride is given)."""
-        if self.fmt == FP8:
-            raise ValueError("the FP8 comparator has no prefix dequantization")
+        if self.fmt in (FP8, K8V4):
+            raise ValueError("the FP8-keyed formats have no prefix dequantization")
         pages = _i32(pages)
         Hkv, D = self.num_kv_heads, self.head_dim
         stride = out_token_stride or Hkv * D
@@ -269,6 +270,13 @@ class Pool:
         if self.fmt == FP8:
             codes = slab[off * D:(off + 1) * D] if kv == 0 else slab[P * D + off::P][:D]
             return np.array([e4m3_value(int(c)) for c in codes]) * float(self.gs[kv])
+        if self.fmt == K8V4:
+            if kv == 0:
+                return np.array([e4m3_value(int(c)) for c in slab[off * D:(off + 1) * D]]) * float(self.gs[0])
+            vsec = slab[P * D:]
+            sc0 = P * (D // 2) + off * (D // 16)
+            return nvfp4_dequant_row(vsec[off * (D // 2):(off + 1) * (D // 2)], vsec[sc0:sc0 + D // 16],
+                                     float(self.gs[1]))
         half = slab[: self.slab // 2] if kv == 0 else slab[self.slab // 2:]
         codes = half[off * (D // 2):(off + 1) * (D // 2)]
         if self.fmt == NVFP4:

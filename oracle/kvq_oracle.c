@@ -41,6 +41,7 @@
 #define KVQO_NVFP4 1
 #define KVQO_INT4 2
 #define KVQO_FP8 3
+#define KVQO_K8V4 4
 
 /* ---------------------------------------------------------------------- */
 /* Element and scale formats                                               */
@@ -237,14 +238,26 @@ static size_t row_scale_bytes(int fmt, int D) { return fmt == KVQO_NVFP4 ? (size
  * [K: P rows x D bytes][V transposed: D rows (channels) x P bytes], so that a
  * channel's values for consecutive tokens are adjacent (the paged-attention
  * value layout). */
+/* FP8 keys with NVFP4 values (the split-precision variant: "SGLang's 4-bit KV
+ * cache ...", section "Against what this site already established": another
+ * engine's 4-bit cache keeps keys in FP8 and values in 4 bits, spending twice
+ * the bits on keys; which 4-bit value format it uses is not stated, and the
+ * reading here is the pages' own NVFP4).  Keys: E4M3 with the per-tensor
+ * scale gs[0], as the FP8 format; values: NVFP4 with global scale gs[1].
+ * Slab of one (page, head): [K: P rows x D bytes][V codes: P rows x D/2]
+ * [V scales: P rows x D/16]. */
+static size_t k8v4_k_bytes(int P, int D) { return (size_t)P * (size_t)D; }
+
 size_t kvqo_slab_bytes(int fmt, int P, int D) {
   if (fmt == KVQO_FP8) return 2 * (size_t)P * (size_t)D;
+  if (fmt == KVQO_K8V4) return k8v4_k_bytes(P, D) + (size_t)P * (row_code_bytes(D) + row_scale_bytes(KVQO_NVFP4, D));
   return 2 * (size_t)P * (row_code_bytes(D) + row_scale_bytes(fmt, D));
 }
 
 /* Bytes one token costs in one KV head (K and V, codes and scales). */
 size_t kvqo_token_head_bytes(int fmt, int D) {
   if (fmt == KVQO_FP8) return 2 * (size_t)D;
+  if (fmt == KVQO_K8V4) return (size_t)D + row_code_bytes(D) + row_scale_bytes(KVQO_NVFP4, D);
   return 2 * (row_code_bytes(D) + row_scale_bytes(fmt, D));
 }
 
@@ -330,6 +343,17 @@ void kvqo_quantize_store(int fmt, uint8_t* pool, int P, int Hkv, int D, const fl
           for (int c = 0; c < D; c++) base[fp8_offset(P, D, off, c, kv)] = (uint8_t)kvqo_fp8_encode(x[c], gs[kv]);
           continue;
         }
+        if (fmt == KVQO_K8V4) {
+          uint8_t* base = pool + ((size_t)page * Hkv + g) * kvqo_slab_bytes(fmt, P, D);
+          if (kv == 0) {
+            for (int c = 0; c < D; c++) base[(size_t)off * D + c] = (uint8_t)kvqo_fp8_encode(x[c], gs[0]);
+          } else {
+            uint8_t* vsec = base + k8v4_k_bytes(P, D);
+            kvqo_nvfp4_quantize_row(x, D, gs[1], vsec + (size_t)off * row_code_bytes(D),
+                                    vsec + (size_t)P * row_code_bytes(D) + (size_t)off * (D / 16));
+          }
+          continue;
+        }
         rowptr r = locate(pool, fmt, P, Hkv, D, page, g, off, kv);
         if (fmt == KVQO_NVFP4) {
           kvqo_nvfp4_quantize_row(x, D, gs[kv], r.codes, r.scales);
@@ -350,6 +374,18 @@ static void read_token(const uint8_t* pool, int fmt, int P, int Hkv, int D, cons
   if (fmt == KVQO_FP8) {
     const uint8_t* base = pool + ((size_t)pages[t / P] * Hkv + g) * kvqo_slab_bytes(fmt, P, D);
     for (int c = 0; c < D; c++) out[c] = kvqo_e4m3_value(base[fp8_offset(P, D, (int)(t % P), c, kv)]) * gs[kv];
+    return;
+  }
+  if (fmt == KVQO_K8V4) {
+    const uint8_t* base = pool + ((size_t)pages[t / P] * Hkv + g) * kvqo_slab_bytes(fmt, P, D);
+    const int off = (int)(t % P);
+    if (kv == 0) {
+      for (int c = 0; c < D; c++) out[c] = kvqo_e4m3_value(base[(size_t)off * D + c]) * gs[0];
+    } else {
+      const uint8_t* vsec = base + k8v4_k_bytes(P, D);
+      kvqo_nvfp4_dequant_row(vsec + (size_t)off * row_code_bytes(D),
+                             vsec + (size_t)P * row_code_bytes(D) + (size_t)off * (D / 16), D, gs[1], out);
+    }
     return;
   }
   rowptr r = locate((uint8_t*)pool, fmt, P, Hkv, D, pages[t / P], g, (int)(t % P), kv);
@@ -462,7 +498,7 @@ void kvqo_decode_attention(int fmt, const uint8_t* pool, int P, int Hkv, int D, 
 void kvqo_dequant_prefix(int fmt, const uint8_t* pool, int P, int Hkv, int D, const float* gs,
                          const int32_t* pages, int64_t prefix_len, uint16_t* k_out, uint16_t* v_out,
                          int64_t out_token_stride) {
-  if (fmt == KVQO_FP8) return; /* the FP8 comparator has no extend path */
+  if (fmt == KVQO_FP8 || fmt == KVQO_K8V4) return; /* no extend path for the FP8-keyed formats */
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < prefix_len; t++) {
     for (int g = 0; g < Hkv; g++) {

@@ -332,7 +332,8 @@ def _torch_attention(q, K, V, G, sm_scale):
 
 @pytest.mark.parametrize("fmt,P,G,Hkv,L", [(1, 16, 4, 1, 70), (1, 3, 6, 2, 40), (1, 1, 1, 2, 9),
                                             (2, 16, 6, 2, 45), (2, 4, 4, 1, 33),
-                                            (3, 16, 6, 2, 45), (3, 5, 4, 1, 33)])
+                                            (3, 16, 6, 2, 45), (3, 5, 4, 1, 33),
+                                            (4, 16, 6, 2, 45), (4, 3, 4, 1, 40)])
 def test_attention_matches_torch_fp64(oracle, fmt, P, G, Hkv, L):
     D, B = 64 if fmt != 2 else 32, 2
     Hq = G * Hkv
@@ -566,6 +567,39 @@ def test_fp8_layout_keys_by_row_values_by_channel(oracle):
     assert slab[9 * D + 5] == 0x40                  # K: row 9, byte 5
     assert slab[P * D + 7 * P + 9] == 0xB0          # V: channel 7's row, byte 9
     assert np.count_nonzero(pool.data) == 2
+
+
+# ------------------------------------------------- FP8 keys with NVFP4 values
+
+@pytest.mark.parametrize("D,rotate", [(64, False), (256, False), (256, True)])
+def test_k8v4_is_fp8_keys_and_nvfp4_values(oracle, D, rotate):
+    # the split-precision format composes the two pinned codecs: its K rows are
+    # byte for byte the FP8 format's K rows (per-tensor scale gs[0]) and its V
+    # rows and scales the NVFP4 format's (global scale gs[1]), for the same
+    # input rows and scales; 400 bytes per token and head at head dim 256
+    P, Hkv, n = 16, 2, 37
+    gs = (0.75, 0.25)
+    k, v = inputs.kv_outlier_channels(31, 0, n, Hkv, D)
+    slots = np.arange(n, dtype=np.int32) + 5
+    pages = -(-(n + 5) // P)
+    mixed = oracle.Pool(oracle.K8V4, pages, P, Hkv, D, global_scale=gs, rotated=rotate)
+    fp8 = oracle.Pool(oracle.FP8, pages, P, Hkv, D, global_scale=gs, rotated=rotate)
+    nv = oracle.Pool(oracle.NVFP4, pages, P, Hkv, D, global_scale=gs, rotated=rotate)
+    for pool in (mixed, fp8, nv):
+        pool.quantize_store(k, v, slots)
+    assert oracle.token_head_bytes(oracle.K8V4, D) == D + D // 2 + D // 16
+    if D == 256:
+        assert oracle.token_head_bytes(oracle.K8V4, 256) == 400
+    kb = P * D
+    vb = P * (D // 2 + D // 16)
+    assert mixed.slab == kb + vb
+    np.testing.assert_array_equal(mixed.data[:, :, :kb], fp8.data[:, :, :kb])
+    np.testing.assert_array_equal(mixed.data[:, :, kb:], nv.data[:, :, nv.slab // 2:])
+    # and the decoded rows are the two formats' decoded rows
+    for t in (0, 7, 36):
+        page, off = divmod(int(slots[t]), P)
+        np.testing.assert_array_equal(mixed.dequant_token(page, 1, off, 0), fp8.dequant_token(page, 1, off, 0))
+        np.testing.assert_array_equal(mixed.dequant_token(page, 1, off, 1), nv.dequant_token(page, 1, off, 1))
 
 
 # ----------------------------------------------------------------- Hadamard rotation

@@ -55,6 +55,9 @@ WORKLOADS = {
     "fp8_32k": dict(fmt=3, batch=32, ctx=32768, page=16, shuffled=False, kind="lognormal",
                     desc="comparator: the 32K headline shape with an FP8 E4M3 per-tensor cache (512 B per "
                          "token and head against NVFP4's 288 B)"),
+    "k8v4_32k": dict(fmt=4, batch=32, ctx=32768, page=16, shuffled=False, kind="lognormal",
+                     desc="split precision: the 32K headline shape with FP8 keys and NVFP4 values (400 B per "
+                          "token and head)"),
 }
 LAYERS, HKV, HQ, D = 16, 4, 24, 256
 
@@ -63,6 +66,8 @@ def token_head_bytes(fmt: int) -> int:
     # packed codes + scales of one token in one KV head, K and V
     if fmt == 3:
         return 2 * D  # FP8: one byte per value, per-tensor scales
+    if fmt == 4:
+        return D + D // 2 + D // 16  # FP8 keys, NVFP4 values
     return 2 * (D // 2 + (D // 16 if fmt == 1 else 4))
 
 
@@ -204,7 +209,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ctx32k", choices=sorted(WORKLOADS))
-    ap.add_argument("--secondary", default="ctx160k,ctx1m,int4_220k,fp8_32k,rot_32k",
+    ap.add_argument("--secondary", default="ctx160k,ctx1m,int4_220k,fp8_32k,k8v4_32k,rot_32k",
                     help="comma-separated extra workloads to report ('' for none)")
     ap.add_argument("--cooldown", type=float, default=10.0,
                     help="idle seconds before each secondary workload (measured: a workload run right after "
@@ -414,7 +419,8 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
     store_ms = sum(a.elapsed_time(b_) for a, b_ in st_marks) / len(st_marks)
     kv_bytes_layer = B * L * HKV * token_head_bytes(fmt)
     res = {
-        "workload": name, "desc": w["desc"], "format": {1: "nvfp4", 2: "int4_per_token_head", 3: "fp8_e4m3_per_tensor"}[fmt],
+        "workload": name, "desc": w["desc"], "format": {1: "nvfp4", 2: "int4_per_token_head", 3: "fp8_e4m3_per_tensor",
+                                                 4: "fp8_keys_nvfp4_values"}[fmt],
         "batch": B, "context": L, "page_size": P, "layers": n_layers, "num_splits": splits,
         "step_ms": step_ms, "decode_call_us": decode_ms * 1e3, "decode_call_us_median": decode_median_ms * 1e3,
         "decode_call_calls_timed": steps * len(layers), "decode_call_median_over": "passes over the layers",

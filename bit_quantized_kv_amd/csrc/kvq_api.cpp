@@ -23,7 +23,8 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 kvq_status check_cache(const kvq_cache* c) {
   if (c == nullptr || c->pool == nullptr) return KVQ_ERR_NULL;
-  if (c->fmt != KVQ_FMT_NVFP4 && c->fmt != KVQ_FMT_INT4_TOKHEAD && c->fmt != KVQ_FMT_FP8_E4M3)
+  if (c->fmt != KVQ_FMT_NVFP4 && c->fmt != KVQ_FMT_INT4_TOKHEAD && c->fmt != KVQ_FMT_FP8_E4M3 &&
+      c->fmt != KVQ_FMT_K8V4)
     return KVQ_ERR_UNSUPPORTED;
   if (c->fmt != KVQ_FMT_INT4_TOKHEAD && c->global_scale == nullptr) return KVQ_ERR_NULL;
   if (c->num_pages <= 0 || c->num_kv_heads <= 0 || c->page_size <= 0) return KVQ_ERR_SHAPE;
@@ -99,7 +100,8 @@ size_t workspace_bytes(const kvq_cache* c, int32_t batch, int32_t num_q_heads, i
 extern "C" {
 
 size_t kvq_slab_bytes(int32_t fmt, int32_t page_size, int32_t head_dim) {
-  if ((fmt != KVQ_FMT_NVFP4 && fmt != KVQ_FMT_INT4_TOKHEAD && fmt != KVQ_FMT_FP8_E4M3) || page_size <= 0 ||
+  if ((fmt != KVQ_FMT_NVFP4 && fmt != KVQ_FMT_INT4_TOKHEAD && fmt != KVQ_FMT_FP8_E4M3 && fmt != KVQ_FMT_K8V4) ||
+      page_size <= 0 ||
       head_dim <= 0 || head_dim % 16)
     return 0;
   return (size_t)kvq::slab_layout(fmt, page_size, head_dim).slab;
@@ -209,7 +211,7 @@ kvq_status kvq_dequant_prefix(const kvq_cache* cache, const int32_t* block_table
                               void* k_out, void* v_out, int64_t out_token_stride, void* stream) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
-  if (cache->fmt == KVQ_FMT_FP8_E4M3) return KVQ_ERR_UNSUPPORTED;
+  if (cache->fmt == KVQ_FMT_FP8_E4M3 || cache->fmt == KVQ_FMT_K8V4) return KVQ_ERR_UNSUPPORTED;
   if (prefix_len < 0) return KVQ_ERR_SHAPE;
   if (prefix_len == 0) return KVQ_OK;
   if (block_table_row == nullptr || k_out == nullptr || v_out == nullptr) return KVQ_ERR_NULL;
@@ -314,7 +316,7 @@ kvq_status kvq_extend_attention_paged(const kvq_cache* cache, const int32_t* blo
                                       float* lse_out, void* stream) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
-  if (cache->fmt == KVQ_FMT_FP8_E4M3) return KVQ_ERR_UNSUPPORTED;
+  if (cache->fmt == KVQ_FMT_FP8_E4M3 || cache->fmt == KVQ_FMT_K8V4) return KVQ_ERR_UNSUPPORTED;
   const int32_t Hkv = cache->num_kv_heads, D = cache->head_dim;
   if (prefix_len < 0 || chunk_len < 0 || num_q_heads <= 0 || num_q_heads % Hkv != 0) return KVQ_ERR_SHAPE;
   if (out_dtype != KVQ_DT_F32 && out_dtype != KVQ_DT_BF16) return KVQ_ERR_UNSUPPORTED;

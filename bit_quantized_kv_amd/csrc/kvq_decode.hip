@@ -49,9 +49,10 @@ static constexpr int kWaves = kDecodeWaves;   // wavefronts per decode workgroup
 
 template <int D, int FMT>
 struct ChunkRegs {
-  static constexpr int VEC = D / 128;  // 16-byte K vectors per lane and token
+  static constexpr int VEC = D / 128;  // 16-byte 4-bit K vectors per lane and token
+  static constexpr int KVEC = FMT == FMT_K8V4 ? D / 64 : VEC;  // K8V4: FP8 keys, twice the bytes
   static constexpr int VW = D / 128;   // V dwords per lane and token (D/32 bytes)
-  u32x4_t kw[2][VEC];
+  u32x4_t kw[2][KVEC];
   uint32_t ks[2][VEC];  // NVFP4: dword holding the lane's two E4M3 block scales
   uint32_t ksc[2];      // INT4: K scale (fp32 bits) of token 4j + r%4 (quad-broadcast later)
   uint32_t vw[2][4][VW];
@@ -133,6 +134,9 @@ struct Decoder : PageWalk {
   static constexpr int VW = D / 128;
   static constexpr int KCH = D / 32;  // QK MFMAs per half
   static constexpr int VT = D / 16;   // PV MFMAs (16-channel tiles)
+  static constexpr int KVEC = ChunkRegs<D, FMT>::KVEC;
+  static constexpr bool K8 = FMT == FMT_K8V4;   // FP8 keys (by token, per-tensor scale)
+  static constexpr bool VNV = FMT != FMT_INT4;  // NVFP4 values
   using Regs = ChunkRegs<D, FMT>;
 
   const int lane, j, r;
@@ -141,7 +145,7 @@ struct Decoder : PageWalk {
   __device__ Decoder(const DecodeParams& p_, int lane_, int b_, int g_, int L_)
       : PageWalk(p_, b_, g_, L_), lane(lane_), j(lane_ >> 4), r(lane_ & 15) {
     // (the _h offsets include the K half, i.e. they address the V half)
-    vo_k = r * (D / 2) + 16 * j;                                            // K code row r
+    vo_k = r * (K8 ? D : D / 2) + 16 * j;                                   // K code row r
     vo_ks = r * (D / 16) + 4 * (j >> 1);                                    // K scale row r
     vo_vs_h = (int)p.half + (4 * j + (r & 3)) * (D / 16) + 4 * (((r >> 2) * D) / 256);
     vo_sc = (4 * j + (r & 3)) * 4;                                          // INT4 scale of row 4j + r%4
@@ -159,16 +163,19 @@ struct Decoder : PageWalk {
     for (int h = 0; h < 2; h++) {
       const __amdgpu_buffer_rsrc_t rs = slab_rsrc(__builtin_amdgcn_readfirstlane(h == 0 ? pg.x : pg.y));
       const int off = __builtin_amdgcn_readfirstlane(h == 0 ? ref.row0 : ref.row1);
-      const int ko = off * (D / 2);
-      const int so = (int)p.scales_off + off * (FMT == FMT_NVFP4 ? D / 16 : 4);
+      const int ko = off * (K8 ? D : D / 2);  // K rows
+      const int vko = off * (D / 2);          // V code rows
+      const int so = (int)p.scales_off + off * (FMT == FMT_INT4 ? 4 : D / 16);
       // K codes: row off + r, bytes 64v + 16j
 #pragma unroll
-      for (int v = 0; v < VEC; v++)
+      for (int v = 0; v < KVEC; v++)
         R.kw[h][v] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo_k + 64 * v, ko, kLoadStream);
       if (FMT == FMT_NVFP4) {
 #pragma unroll
         for (int v = 0; v < VEC; v++)
           R.ks[h][v] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_ks + 8 * v, so, kLoadStream);
+      }
+      if (VNV) {
         // Lane (j, r) with quad Q = r / 4 loads the dword of V-scale row 4j + r%4
         // that holds block (r * D / 256), the block every lane of quad Q needs;
         // compute() broadcasts row i of the quad with a DPP quad_perm.
@@ -181,11 +188,11 @@ struct Decoder : PageWalk {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         if (VW == 2) {
-          const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo_v_h + i * (D / 2), ko, kLoadStream);
+          const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo_v_h + i * (D / 2), vko, kLoadStream);
           R.vw[h][i][0] = w.x;
           R.vw[h][i][VW - 1] = w.y;
         } else {
-          R.vw[h][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_v_h + i * (D / 2), ko, kLoadStream);
+          R.vw[h][i][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_v_h + i * (D / 2), vko, kLoadStream);
         }
       }
     }
@@ -193,8 +200,20 @@ struct Decoder : PageWalk {
 
   // One QK MFMA operand: 8 fp16 K values of chunk (v, w) for this lane's token.
   __device__ inline half8_t k_operand(const Regs& R, int h, int v, int w, half2_t s2) const {
-    const uint32_t word = w == 0 ? R.kw[h][v].x : w == 1 ? R.kw[h][v].y : w == 2 ? R.kw[h][v].z : R.kw[h][v].w;
     half2_t a0, a1, a2, a3;
+    if (K8) {
+      // FP8 keys: MFMA m = 4v + w takes 8 bytes (dwords 0-1 or 2-3 of vector
+      // m / 2); E4M3 -> fp16 exactly at unit scale
+      const int m = 4 * v + w;
+      const u32x4_t kv4 = R.kw[h][m / 2];
+      const uint32_t d0 = (m % 2) ? kv4.z : kv4.x, d1 = (m % 2) ? kv4.w : kv4.y;
+      a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
+      a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
+      a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
+      a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
+      return (half8_t){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+    }
+    const uint32_t word = w == 0 ? R.kw[h][v].x : w == 1 ? R.kw[h][v].y : w == 2 ? R.kw[h][v].z : R.kw[h][v].w;
     if (FMT == FMT_NVFP4) {
       // (e2m1 * 2^8) * (scale * 2^-8): pairs of channels (2k, 2k + 1)
       a0 = e2m1x2_to_h2_x256<0>(word) * s2;
@@ -212,9 +231,20 @@ struct Decoder : PageWalk {
     return (half8_t){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
   }
 
+  // First channel of the 8 channels of QK chunk (v, w) for lane group jj
+  // (k_channel - k_base is in 0..7).
+  __device__ static inline int k_base(int v, int w, int jj) {
+    if (K8) {
+      const int m = 4 * v + w;
+      return 64 * (m / 2) + 16 * jj + 8 * (m % 2);
+    }
+    return 128 * v + 32 * jj + 8 * w;
+  }
+
   // Channel of element e of QK chunk (v, w) for lane group j (must match
   // k_operand's element order).
   __device__ static inline int k_channel(int v, int w, int jj, int e) {
+    if (K8) return k_base(v, w, jj) + e;
     if (FMT == FMT_NVFP4) return 128 * v + 32 * jj + 8 * w + e;
     return 128 * v + 32 * jj + 8 * w + (e >> 1) + 4 * (e & 1);
   }
@@ -271,7 +301,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     for (int v = 0; v < VEC; v++) {
 #pragma unroll
       for (int w = 0; w < 4; w++) {
-        const uint4 raw = *(const uint4*)(qrow + 128 * v + 32 * j + 8 * w);
+        const uint4 raw = *(const uint4*)(qrow + Dec::k_base(v, w, j));
         const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
         float nat[8];
 #pragma unroll
@@ -281,7 +311,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         }
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-          const int ch = Dec::k_channel(v, w, j, e) - (128 * v + 32 * j + 8 * w);
+          const int ch = Dec::k_channel(v, w, j, e) - Dec::k_base(v, w, j);
           float x = qn < G ? nat[ch] : 0.0f;
           qf[4 * v + w][e] = x;
           qmax = fmaxf(qmax, __builtin_fabsf(x));
@@ -304,7 +334,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       qop[c][e] = (_Float16)ldexpf(qf[c][e], ke);
     }
   }
-  const float sm = p.sm_scale * kLog2e * ldexpf(1.0f, -kq) * (FMT == FMT_NVFP4 ? p.gs[0] : 1.0f);
+  const float sm = p.sm_scale * kLog2e * ldexpf(1.0f, -kq) * (FMT != FMT_INT4 ? p.gs[0] : 1.0f);
 
   const float lo_sel = n < 8 ? 0.0f : 1.0f;  // DUP: lanes n >= 8 carry the low fp16 part of p
   // byte of block (n * D / 256) within its scale dword, from two dwords -> bytes 0, 1
@@ -414,7 +444,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     }
     // ---------------- V scales of the token pairs (2pp, 2pp + 1) of each half
     half2_t vsc2[2][2];
-    if (FMT == FMT_NVFP4) {
+    if (Dec::VNV) {
 #pragma unroll
       for (int h = 0; h < 2; h++) {
 #pragma unroll
@@ -432,7 +462,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     // ---------------- PV.  The A operand of tile t holds channel t of the
     // lane's 16-channel segment for the 8 tokens 4j..4j+3 of each half, as
     // fp16 pairs (token 2i, token 2i + 1).
-    if (FMT == FMT_NVFP4) {
+    if (Dec::VNV) {
       // token pairs (2i, 2i+1) nibble-interleaved so one conversion yields
       // (token a, token b) of a single channel; groups of 4 tiles share the
       // interleaved word of each pair (sel 0: even channels, 1: odd)
@@ -583,7 +613,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     float M = -__builtin_inff();
 #pragma unroll
     for (int w = 0; w < kWaves; w++) M = fmaxf(M, sm_ml[(w * G + n) * 2]);
-    scale_o = m_run == -__builtin_inff() ? 0.0f : exp2f(m_run - M) * (FMT == FMT_NVFP4 ? p.gs[1] : 1.0f);
+    scale_o = m_run == -__builtin_inff() ? 0.0f : exp2f(m_run - M) * (FMT != FMT_INT4 ? p.gs[1] : 1.0f);
   }
 #pragma unroll
   for (int w = 0; w < kWaves; w++) {
@@ -1028,9 +1058,11 @@ hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream
     }
   } else if (head_dim == 256) {
     if (fmt == FMT_NVFP4) KVQ_DECODE(256, FMT_NVFP4);
+    else if (fmt == FMT_K8V4) KVQ_DECODE(256, FMT_K8V4);
     else KVQ_DECODE(256, FMT_INT4);
   } else {
     if (fmt == FMT_NVFP4) KVQ_DECODE(128, FMT_NVFP4);
+    else if (fmt == FMT_K8V4) KVQ_DECODE(128, FMT_K8V4);
     else KVQ_DECODE(128, FMT_INT4);
   }
   if (head_dim == 256) {

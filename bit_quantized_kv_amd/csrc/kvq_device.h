@@ -4,7 +4,8 @@
 // 16 head-dim elements of a token row, FP32 per-layer global scale; INT4 =
 // symmetric -7..7 two's-complement nibbles with one FP32 scale per token and
 // head.  Even element in the low nibble.  FP8 (the comparator) = one OCP E4M3
-// byte per value with one FP32 scale per tensor, V stored by channel.
+// byte per value with one FP32 scale per tensor, V stored by channel.  K8V4 =
+// FP8 keys (by token, per-tensor scale) with NVFP4 values.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,7 +22,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-enum { FMT_NVFP4 = 1, FMT_INT4 = 2, FMT_FP8 = 3 };
+enum { FMT_NVFP4 = 1, FMT_INT4 = 2, FMT_FP8 = 3, FMT_K8V4 = 4 };
 
 // Byte layout of one slab (one page of one KV head).
 struct SlabLayout {
@@ -34,6 +35,15 @@ struct SlabLayout {
 
 __host__ __device__ inline SlabLayout slab_layout(int fmt, int page_size, int head_dim) {
   SlabLayout s;
+  if (fmt == FMT_K8V4) {
+    // [K: page_size rows x head_dim bytes][V codes: page_size x head_dim/2][V scales]
+    s.code_row = head_dim / 2;  // of the V section
+    s.scale_row = head_dim / 16;
+    s.half = (int64_t)page_size * head_dim;             // offset of the V section
+    s.scales_off = (int64_t)page_size * s.code_row;     // within the V section
+    s.slab = s.half + (int64_t)page_size * (s.code_row + s.scale_row);
+    return s;
+  }
   if (fmt == FMT_FP8) {
     // [K: page_size rows x head_dim bytes][V: head_dim rows x page_size bytes]
     s.code_row = head_dim;

@@ -128,6 +128,45 @@ __device__ inline uint32_t e2m1_pack8(const float* y) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
 }
 
+// NVFP4 of one 16-element block under the global scale gs: the E4M3 block
+// scale code and the two words of E2M1 codes (element 0 in the low nibble).
+__device__ inline void nvfp4_block(const float x[16], float gs, uint32_t& w0, uint32_t& w1, uint32_t& cs) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; e++) amax = fmaxf(amax, __builtin_fabsf(x[e]));
+  const float den = 6.0f * gs;
+  const float s_raw = amax / den;
+  cs = e4m3_encode(s_raw);
+  const float S = e4m3_decode(cs) * gs;
+
+  float y[16];
+  if (S != 0.0f && s_raw <= 448.0f && fma_quotient_exact(gs)) {
+    const float r = 1.0f / S;
+#pragma unroll
+    for (int e = 0; e < 16; e++) y[e] = fma_quotient(x[e], S, r);
+  } else {
+    // general global scale, a saturated block scale, or S = 0 (codes 0 below)
+#pragma unroll
+    for (int e = 0; e < 16; e++) y[e] = x[e] / S;
+  }
+  w0 = e2m1_pack8(y);
+  w1 = e2m1_pack8(y + 8);
+  if (S == 0.0f) w0 = w1 = 0u;
+}
+
+// FP8 E4M3 of 16 values with a per-tensor scale s: code = E4M3(fp32(x / s))
+// with the sign kept, saturating at 448; four words, element 0 in the low byte.
+__device__ inline void fp8_block(const float x[16], float s, uint32_t w[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; e++) w[e] = 0u;
+#pragma unroll
+  for (int e = 0; e < 16; e++) {
+    const float y = x[e] / s;
+    const uint32_t code = e4m3_encode(__builtin_fabsf(y)) | ((as_u32(y) >> 24) & 0x80u);
+    w[e / 4] |= code << (8 * (e % 4));
+  }
+}
+
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void nvfp4_store_kernel(StoreParams p) {
   constexpr int NB = D / 16;
@@ -143,28 +182,8 @@ __global__ __launch_bounds__(256) void nvfp4_store_kernel(StoreParams p) {
   Row16<TIn>::load(src, x);
   if (p.rotate) hadamard_row<D>(x, b, p.rot_scale);
   const int32_t slot = p.slots[i];
-
-  float amax = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 16; e++) amax = fmaxf(amax, __builtin_fabsf(x[e]));
-  const float gs = p.gs[kv];
-  const float den = 6.0f * gs;
-  const float s_raw = amax / den;
-  const uint32_t cs = e4m3_encode(s_raw);
-  const float S = e4m3_decode(cs) * gs;
-
-  float y[16];
-  if (S != 0.0f && s_raw <= 448.0f && fma_quotient_exact(gs)) {
-    const float r = 1.0f / S;
-#pragma unroll
-    for (int e = 0; e < 16; e++) y[e] = fma_quotient(x[e], S, r);
-  } else {
-    // general global scale, a saturated block scale, or S = 0 (codes 0 below)
-#pragma unroll
-    for (int e = 0; e < 16; e++) y[e] = x[e] / S;
-  }
-  uint32_t w0 = e2m1_pack8(y), w1 = e2m1_pack8(y + 8);
-  if (S == 0.0f) w0 = w1 = 0u;
+  uint32_t w0, w1, cs;
+  nvfp4_block(x, p.gs[kv], w0, w1, cs);
   if (slot < 0) return;
 
   const int64_t page = slot / p.page_size;
@@ -190,14 +209,8 @@ __global__ __launch_bounds__(256) void fp8_store_kernel(StoreParams p) {
   Row16<TIn>::load((const TIn*)(kv ? p.v : p.k) + i * p.in_stride + (int64_t)g * D + 16 * b, x);
   if (p.rotate) hadamard_row<D>(x, b, p.rot_scale);
   const int32_t slot = p.slots[i];
-  const float s = p.gs[kv];
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 16; e++) {
-    const float y = x[e] / s;
-    const uint32_t code = e4m3_encode(__builtin_fabsf(y)) | ((as_u32(y) >> 24) & 0x80u);
-    w[e / 4] |= code << (8 * (e % 4));
-  }
+  uint32_t w[4];
+  fp8_block(x, p.gs[kv], w);
   if (slot < 0) return;
   const int64_t page = slot / p.page_size;
   const int off = slot % p.page_size;
@@ -208,6 +221,37 @@ __global__ __launch_bounds__(256) void fp8_store_kernel(StoreParams p) {
     uint8_t* col = base + (int64_t)p.page_size * D + (int64_t)(16 * b) * p.page_size + off;
 #pragma unroll
     for (int e = 0; e < 16; e++) col[(int64_t)e * p.page_size] = (uint8_t)(w[e / 4] >> (8 * (e % 4)));
+  }
+}
+
+// FP8 keys with NVFP4 values: K rows as in the FP8 format (by token, D bytes,
+// per-tensor scale gs[0]), V rows as in NVFP4 (global scale gs[1]) in the
+// slab's V section.  The K|V choice is per workgroup (grid y).
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void k8v4_store_kernel(StoreParams p) {
+  constexpr int NB = D / 16;
+  const int kv = (int)blockIdx.y >= p.num_kv_heads ? 1 : 0;
+  const int g = (int)blockIdx.y - kv * p.num_kv_heads;
+  const int b = threadIdx.x % NB;
+  const int64_t i = store_token<D>(threadIdx.x);
+  if (i >= p.num_tokens) return;
+  float x[16];
+  Row16<TIn>::load((const TIn*)(kv ? p.v : p.k) + i * p.in_stride + (int64_t)g * D + 16 * b, x);
+  if (p.rotate) hadamard_row<D>(x, b, p.rot_scale);
+  const int32_t slot = p.slots[i];
+  uint32_t w[4], cs = 0u;
+  if (kv == 0) fp8_block(x, p.gs[0], w);
+  else nvfp4_block(x, p.gs[1], w[0], w[1], cs);
+  if (slot < 0) return;
+  const int64_t page = slot / p.page_size;
+  const int64_t off = slot % p.page_size;
+  uint8_t* base = p.pool + (page * p.num_kv_heads + g) * p.slab;
+  if (kv == 0) {
+    *(uint4*)(base + off * D + 16 * b) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    uint8_t* vsec = base + p.half;
+    *(uint2*)(vsec + off * (D / 2) + 8 * b) = make_uint2(w[0], w[1]);
+    vsec[p.scales_off + off * NB + b] = (uint8_t)cs;
   }
 }
 
@@ -501,6 +545,8 @@ hipError_t launch_quantize_store(const StoreParams& p, int fmt, int head_dim, in
       hipLaunchKernelGGL((nvfp4_store_kernel<D, T>), grid, block, 0, stream, p);   \
     else if (fmt == FMT_INT4)                                                      \
       hipLaunchKernelGGL((int4_store_kernel<D, T>), grid, block, 0, stream, p);    \
+    else if (fmt == FMT_K8V4)                                                      \
+      hipLaunchKernelGGL((k8v4_store_kernel<D, T>), grid, block, 0, stream, p);    \
     else                                                                           \
       hipLaunchKernelGGL((fp8_store_kernel<D, T>), grid, block, 0, stream, p);     \
   } while (0)

@@ -15,6 +15,7 @@ import torch
 NVFP4 = 1
 INT4_TOKHEAD = 2
 FP8_E4M3 = 3  # the per-tensor FP8 comparator format
+K8V4 = 4  # FP8 keys (per-tensor scale) with NVFP4 values
 DT_F32 = 0
 DT_BF16 = 1
 

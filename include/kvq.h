@@ -28,6 +28,15 @@
  *     section "The 56% survives its own scale, and names the block size").
  *     code = E4M3(fp32(x / s)) with the sign kept, saturating at 448.  Store
  *     and decode only (kvq_dequant_prefix and calibration: UNSUPPORTED).
+ *   KVQ_FMT_K8V4: FP8 keys with NVFP4 values -- the split-precision 4-bit
+ *     cache ("SGLang's 4-bit KV cache ...", section "Against what this site
+ *     already established": another engine keeps keys in FP8 and values in 4
+ *     bits, twice the bits on keys; its 4-bit value format is not stated and
+ *     NVFP4 is taken).  Keys as KVQ_FMT_FP8_E4M3's (by token, per-tensor
+ *     scale global_scale[0]); values as KVQ_FMT_NVFP4's (global scale
+ *     global_scale[1]); 400 bytes per token and head at head dim 256.  Store
+ *     and decode only.  With KVQ_FLAG_HADAMARD it is that engine's rotated
+ *     design.
  *   Quantization rules (4-bit formats): block/row amax; NVFP4 scale
  *   E4M3(fp32(amax / fp32(6 * gs))), elements rounded to nearest-even under the
  *   stored scale fp32(E4M3 * gs), |x| >= 6 saturating; INT4 scale
@@ -41,7 +50,9 @@
  * Scales are page_size rows of head_dim/16 E4M3 bytes (NVFP4) or page_size
  * fp32 values (INT4).  FP8 slabs are [K: page_size rows of head_dim bytes]
  * [V: head_dim rows (channels) of page_size bytes], values stored by channel
- * as in paged-attention value caches.  Cache token t of a sequence lives in page
+ * as in paged-attention value caches.  K8V4 slabs are [K: page_size rows of
+ * head_dim bytes][V codes: page_size rows of head_dim/2 bytes][V scales:
+ * page_size rows of head_dim/16 bytes].  Cache token t of a sequence lives in page
  * block_table[t / page_size] at row t % page_size; a write slot is
  * page * page_size + row.
  *
@@ -82,7 +93,7 @@ typedef enum {
   KVQ_ERR_HIP = -6          /* a HIP launch failed; see kvq_last_hip_error() */
 } kvq_status;
 
-typedef enum { KVQ_FMT_NVFP4 = 1, KVQ_FMT_INT4_TOKHEAD = 2, KVQ_FMT_FP8_E4M3 = 3 } kvq_format;
+typedef enum { KVQ_FMT_NVFP4 = 1, KVQ_FMT_INT4_TOKHEAD = 2, KVQ_FMT_FP8_E4M3 = 3, KVQ_FMT_K8V4 = 4 } kvq_format;
 
 typedef enum { KVQ_DT_F32 = 0, KVQ_DT_BF16 = 1 } kvq_dtype;
 
@@ -96,7 +107,8 @@ typedef struct {
   void* pool;                 /* device, uint8 [num_pages][num_kv_heads][slab] */
   const float* global_scale;  /* device float[2] = {gs_K, gs_V}, positive and
                                  finite; NVFP4 global scales, FP8 per-tensor
-                                 scales (ignored for INT4) */
+                                 scales, K8V4 {FP8 key scale, NVFP4 value
+                                 global scale} (ignored for INT4) */
   int32_t flags;              /* 0, or KVQ_FLAG_HADAMARD */
 } kvq_cache;
 
@@ -118,7 +130,8 @@ typedef struct {
  * NVFP4: 2 * page_size * (head_dim/2 + head_dim/16); INT4: 2 * page_size *
  * (head_dim/2 + 4), i.e. 422,400 bytes for a 1,600-token page at head dim
  * 256, the page size "KV cache in 4 bits ..." ("What we changed") prints;
- * FP8: 2 * page_size * head_dim. */
+ * FP8: 2 * page_size * head_dim; K8V4: page_size * (head_dim + head_dim/2 +
+ * head_dim/16). */
 size_t kvq_slab_bytes(int32_t fmt, int32_t page_size, int32_t head_dim);
 
 /* Quantize-on-write ("SGLang's 4-bit KV cache ...", Figure 2 caption: prefill

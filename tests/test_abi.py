@@ -187,6 +187,20 @@ def test_fp8_comparator_format(lib, oracle):
     assert q_store(lib, c, n=0) == OK
 
 
+def test_k8v4_format(lib, oracle):
+    for P in (16, 48, 1600):
+        for D in (128, 256):
+            assert kvq.kvq_slab_bytes(4, P, D) == oracle.slab_bytes(4, P, D) == P * (D + D // 2 + D // 16)
+    c = cache(fmt=4)
+    assert lib.kvq_dequant_prefix(ctypes.byref(c), FAKE, 16, FAKE, FAKE, 1024, None) == ERR_UNSUPPORTED
+    assert lib.kvq_calibrate_amax(ctypes.byref(c), FAKE, FAKE, 1, 1024, 4, FAKE, None) == ERR_UNSUPPORTED
+    assert lib.kvq_extend_attention_paged(ctypes.byref(c), FAKE, 100, FAKE, 24 * 256, 24, FAKE, FAKE, 4 * 256, 8,
+                                          0.0, FAKE, 1, 24 * 256, None, None) == ERR_UNSUPPORTED
+    c0 = cache(fmt=4, gs=0)
+    assert q_store(lib, c0) == ERR_NULL                      # the key and value scales are required
+    assert q_store(lib, c, n=0) == OK
+
+
 def test_rotation_flag_and_rotate_validation(lib):
     c = cache()
     c.flags = 2                                                   # unknown flag bit

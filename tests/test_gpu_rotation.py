@@ -46,6 +46,7 @@ def test_rotation_kernel_bitexact(D):
     (1, 4, [129], "lognormal", torch.float32, (0.37, 2.5)),
     (2, 6, [300, 47, 1], "outliers", torch.bfloat16, (1.0, 1.0)),
     (3, 6, [200, 33], "lognormal", torch.bfloat16, (0.05, 0.04)),
+    (4, 6, [300, 47, 1], "outliers", torch.bfloat16, (0.05, 1.0)),  # FP8 keys, NVFP4 values, rotated
 ])
 def test_rotated_cache_store_and_decode(fmt, G, lens, kind, dtype, gs):
     print(f"case: rotated cache fmt {fmt} G {G} lens {lens} {kind} {dtype}", flush=True)

@@ -142,7 +142,8 @@ size_t kvq_slab_bytes(int32_t fmt, int32_t page_size, int32_t head_dim);
  *   in_token_stride elements between tokens, >= num_kv_heads * head_dim
  *   slot_mapping    device int32 [num_tokens]; slot < 0 skips the token
  * Writes each (token, head) K row and V row -- codes and scales -- into its
- * slot.  NVFP4 reads cache->global_scale.  num_tokens == 0 is a no-op. */
+ * slot.  NVFP4, FP8 and K8V4 read cache->global_scale.  num_tokens == 0 is a
+ * no-op. */
 kvq_status kvq_quantize_store(const kvq_cache* cache, const void* k, const void* v, int32_t in_dtype,
                               int64_t in_token_stride, const int32_t* slot_mapping, int32_t num_tokens,
                               void* stream);
@@ -151,7 +152,7 @@ kvq_status kvq_quantize_store(const kvq_cache* cache, const void* k, const void*
  * (sequence, KV head) is cut into that many token ranges of whole 32-token
  * chunks, sized from (format, batch, num_kv_heads, max_seq_len) and the
  * current device's compute-unit count (256 when no device is visible) so the
- * grid holds about one workgroup per CU (NVFP4) or two (INT4). */
+ * grid holds about one workgroup per CU (NVFP4, FP8, K8V4) or two (INT4). */
 kvq_status kvq_decode_num_splits(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
                                  int32_t max_seq_len, int32_t* num_splits);
 
@@ -199,7 +200,8 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
  *   k_out, v_out     device bf16; head g of token t at element
  *                    t * out_token_stride + g * head_dim
  *   out_token_stride elements, >= num_kv_heads * head_dim
- * prefix_len == 0 is a no-op. */
+ * prefix_len == 0 is a no-op.  NVFP4 and INT4 caches (FP8, K8V4:
+ * KVQ_ERR_UNSUPPORTED). */
 kvq_status kvq_dequant_prefix(const kvq_cache* cache, const int32_t* block_table_row, int32_t prefix_len,
                               void* k_out, void* v_out, int64_t out_token_stride, void* stream);
 
@@ -231,7 +233,7 @@ kvq_status kvq_extend_attention(const void* q, int64_t q_token_stride, int32_t n
  * "The 1.78x is arithmetic ...": the 1M run handed 15 % of the GPU back for
  * prefill workspace).  The chunk's own K/V come as bf16 rows k_chunk, v_chunk
  * [chunk_len][chunk_token_stride] (head g at g * head_dim).  NVFP4 and INT4
- * caches (FP8: KVQ_ERR_UNSUPPORTED); for a rotated cache the caller passes
+ * caches (FP8, K8V4: KVQ_ERR_UNSUPPORTED); for a rotated cache the caller passes
  * rotated q and chunk rows and rotates the output back. */
 kvq_status kvq_extend_attention_paged(const kvq_cache* cache, const int32_t* block_table_row, int32_t prefix_len,
                                       const void* q, int64_t q_token_stride, int32_t num_q_heads, const void* k_chunk,

@@ -195,6 +195,26 @@ def test_full_32k_fp8_comparator_batch32():
     lay.check_decode(pool, seqs=[0, 31], heads_per_group=1)
 
 
+def test_full_32k_k8v4_batch32():
+    # FP8 keys with NVFP4 values at the headline shape, 32 sequences x 32,768 tokens
+    print("case: full 32K FP8-key / NVFP4-value layer", flush=True)
+    lay = FullLayer(9, 4, 32, 32768, 16, False, "lognormal")
+    pool = lay.cache.pool.cpu().numpy()
+    P = 16
+    for b, t, krow, vrow in lay.samples:
+        page, row = int(lay.bt[b, t // P]), t % P
+        for g in range(HKV):
+            sl = pool[page, g]
+            kc = np.array([oracle.fp8_encode(x, 1.0) for x in krow[g]], np.uint8)
+            assert np.array_equal(sl[row * D:(row + 1) * D], kc), (b, t, g)
+            vsec = sl[P * D:]
+            rc, rs = oracle.nvfp4_quantize_row(vrow[g], 1.0)
+            assert np.array_equal(vsec[row * (D // 2):(row + 1) * (D // 2)], rc), (b, t, g)
+            sc0 = P * (D // 2) + row * (D // 16)
+            assert np.array_equal(vsec[sc0:sc0 + D // 16], rs), (b, t, g)
+    lay.check_decode(pool, seqs=[0, 31], heads_per_group=1)
+
+
 def test_full_extend_4096_over_32k_prefix():
     # extend attention of a 4,096-token chunk over a 32K prefix workspace (the
     # bench's shape), sampled query rows against the oracle run row by row

@@ -60,7 +60,9 @@
  *   - The caller owns all memory.  The library allocates and frees nothing and
  *     keeps no state between calls.
  *   - All work is enqueued on the caller's HIP stream (`stream`, a
- *     hipStream_t; NULL = the default stream) and is asynchronous.
+ *     hipStream_t; NULL = the default stream) and is asynchronous.  The calls
+ *     record nothing but kernel launches (no allocation, copy or memset), so
+ *     they can be captured into a HIP graph and replayed.
  *   - Every host-checkable condition is validated before any launch; a
  *     failing call returns a negative kvq_status and launches nothing.  A
  *     failed launch returns KVQ_ERR_HIP; kvq_last_hip_error() then gives the

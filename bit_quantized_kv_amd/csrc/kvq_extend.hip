@@ -41,39 +41,25 @@ static constexpr float kExtLn2 = 0.6931471805599453f;
 static constexpr float kExtSlack = 8.0f;
 
 // LDS layout, chosen from measured bank-conflict counts of each access
-// pattern on gfx950 (16-byte reads of the MFMA operand layout, lane (j, n)
-// reading column j of row n, run conflict-free when the row stride is 8 mod 16
-// dwords, or with a 16-dword stride when column j is XOR-swizzled by
-// (n / 2) mod 4):
-//  - K rows (tokens) D/2 + 8 dwords apart; the staging writes are 16-byte
-//    stores of consecutive segments of a row (a half-wavefront per row at head
-//    dim 256), as fast as a linear store;
-//  - V^T in 16-channel tiles of 272 dwords (16 rows of 16 dwords + 16 pad);
-//    row n holds the step's 32 tokens as 16 bf16 pairs in the PV operand's k
-//    order (tokens 4j..4j+3 then 16+4j..16+4j+3 in 16-byte column j), with
-//    column j stored at column j ^ ((n / 2) mod 4); the staging writes are
-//    single dwords, 16 token pairs of 4 tiles per wavefront, conflict-free.
+// pattern on gfx950: K and V are both staged by token row, D/2 + 8 dwords
+// apart.  With that stride the QK operand reads (16-byte, lane (j, n) reading
+// column j of row n) and the PV operand reads -- transposing 8-byte reads
+// (ds_read_b64_tr_b16), where the 16 lanes of a group each name 4 channels of
+// one token row and every lane receives one channel of 4 tokens -- are
+// conflict-free, and the staging writes (16-byte segments, whole rows per
+// half-wavefront) run as fast as a linear store.  No transposition in
+// registers: V rows are copied like K rows.
 template <int D>
 struct ExtLds {
-  static constexpr int KPD = D / 2 + 8;  // dwords per staged K row
+  static constexpr int KPD = D / 2 + 8;  // dwords per staged K or V row
   static constexpr int KB = kExtStep * KPD * 4;
-  static constexpr int VTD = 16 * 16 + 16;  // dwords per 16-channel V^T tile
-  static constexpr int VB = (D / 16) * VTD * 4;
+  static constexpr int VB = KB;
   static constexpr int BUF = KB + VB + 2 * kExtStep * 4;  // + per-token K and V factors
   static constexpr int TOTAL = 2 * BUF;
-  // dword offset of 16-byte column j of V^T row c
-  __device__ static int vcol(int c, int j) {
-    const int n = c & 15;
-    return (c >> 4) * VTD + 16 * n + 4 * (j ^ ((n >> 1) & 3));
-  }
 };
 
-// 16-byte column and dword inside it of the token pair (2 vp, 2 vp + 1) in a
-// staged V^T row: pair groups of 4 tokens interleaved as 0, 4, 1, 5, 2, 6, 3, 7
-__device__ inline int ext_vslot(int vp) {
-  const int g4 = vp >> 1;
-  return 2 * (g4 < 4 ? 2 * g4 : 2 * (g4 - 4) + 1) + (vp & 1);
-}
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
 
 constexpr int kExtWorkspace = 0;  // SRC: every key from the bf16 workspace (else the cache format)
 
@@ -83,7 +69,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   constexpr bool PAGED = SRC != kExtWorkspace;
   constexpr int KCH = D / 32, VT = D / 16;
   constexpr int KV16 = D / 64;       // 16-byte K vectors per thread and step
-  constexpr int CPT = D / 16;        // V channels per thread and step (two tokens each)
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -138,27 +123,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   // fast as a linear store).  K, paged variant: thread t takes the D/8
   // elements from kseg * D/8 of one row, krow0 (one page lookup and one code
   // load per row and step; at head dim 256 a quarter-wavefront covers 4 rows x
-  // 4 segments).  V: tokens 2(t%16), 2(t%16)+1, channels (t/16)*CPT ...
+  // 4 segments).  V rows are staged exactly like K rows.
   constexpr int KSEG = PAGED ? 8 : D / 8, KRP = 256 / KSEG;
   const int krow0 = PAGED ? (D == 256 ? ((tid >> 2) & 3) + 4 * (tid >> 5) : tid >> 3) : tid / KSEG;
   const int kseg = PAGED ? (D == 256 ? (tid & 3) + 4 * ((tid >> 4) & 1) : tid & 7) : tid % KSEG;
   // row and first element of pass v
   auto krow_of = [&](int v) { return PAGED ? krow0 : krow0 + v * KRP; };
   auto kel_of = [&](int v) { return PAGED ? kseg * (D / 8) + 8 * v : 8 * kseg; };
-  const int vpair = tid & 15, vcb = tid >> 4, vslot = ext_vslot(vpair);
-  const int vsj = vslot >> 2, vsw = vslot & 3;
   const int64_t Lp = p.prefix_len;
   // bf16 rows: the workspace holds every token; the paged variant's rows are the chunk's
   const int64_t row_base = PAGED ? Lp : 0;
-  // staged rows in flight: bf16 values, or for a paged prefix token its raw
-  // code word(s) and scale word in the same registers (.x, .y: codes; K .y /
-  // V .z: scale), expanded to bf16 in lstore
-  u32x4_t kreg[KV16], va[CPT / 8], vb[CPT / 8];
+  // staged rows in flight: bf16 values, or for a paged prefix row its raw
+  // code words (reg[0]) and scale word (reg[1].x), expanded to bf16 in lstore
+  u32x4_t kreg[KV16], vreg[KV16];
   // bf16 rows through buffer descriptors rebased per step (uniform, scalar
   // math); the record count ends at row Lk, so rows past the end read zeros,
   // and the lane parts of the offsets are loop-invariant
   const int kvo = (krow0 * (int)p.kv_stride + g * D + kel_of(0)) * 2;
-  const int vvo = (2 * vpair * (int)p.kv_stride + g * D + vcb * CPT) * 2;
   const int rowb = (int)p.kv_stride * 2;
   auto rows_rsrc = [&](const uint16_t* rows, int64_t t0) {
     const int64_t bytes = min((Lk - t0) * p.kv_stride * 2, (int64_t)0x7FFFFFF0);
@@ -167,10 +148,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   };
   auto gload = [&](int step) {
     const int64_t t0 = (int64_t)step * kExtStep;
-    const __amdgpu_buffer_rsrc_t krs = rows_rsrc(p.k, t0), vrs = rows_rsrc(p.v, t0);
     // paged prefix: the step's first token t0 sits in page pi0 at row off0; a
-    // page holds at least 16 rows, so the step's 32 tokens span at most the
-    // pages pi0 .. pi0 + 2, whose slabs are looked up once (uniform values)
+    // page holds at least 16 rows, so a token of the step is at most two pages
+    // further
     int off0 = 0;
     int pi0 = 0;
     if (PAGED && t0 < Lp) {
@@ -185,56 +165,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       off = o;
       return p.pool + ((int64_t)p.pages[pi] * p.num_kv_heads + g) * p.slab;
     };
-    if (PAGED && t0 + krow0 < Lp) {
-      // the row's D/8 elements from kseg * D/8: D/16 code bytes, and D/128 E4M3
-      // block scales (NVFP4) or the fp32 row scale (INT4), kept raw in kreg
-      int off;
-      const uint8_t* sl = locate(krow0, off);
-      const uint8_t* cp = sl + (int64_t)off * (D / 2) + kseg * (D / 16);
-      if (D == 256) {
-        kreg[0] = ld_global<u32x4_t>(cp);
-      } else {
-        const u32x2_t w = ld_global<u32x2_t>(cp);
-        kreg[0].x = w.x;
-        kreg[0].y = w.y;
-      }
-      const uint8_t* sc = sl + p.scales_off;
-      if (SRC == FMT_NVFP4)
-        kreg[1].x = D == 256 ? (uint32_t)ld_global<uint16_t>(sc + (int64_t)off * (D / 16) + 2 * kseg)
-                             : (uint32_t)ld_global<uint8_t>(sc + (int64_t)off * (D / 16) + kseg);
-      else
-        kreg[1].x = ld_global<uint32_t>(sc + (int64_t)off * 4);
-    } else {
-#pragma unroll
-      for (int v = 0; v < KV16; v++)
-        kreg[v] = __builtin_amdgcn_raw_buffer_load_b128(krs, kvo + (PAGED ? 16 * v : v * KRP * rowb), 0, 0);
-    }
-    auto vload = [&](u32x4_t(&vr)[CPT / 8], int half) {
-      const int r = 2 * vpair + half;
-      if (PAGED && t0 + r < Lp) {
+    // one row's staging registers: K (kv 0) or V (kv 1)
+    auto rows = [&](u32x4_t(&reg)[KV16], int kv) {
+      if (PAGED && t0 + krow0 < Lp) {
+        // the row's D/8 elements from kseg * D/8: D/16 code bytes, and D/128
+        // E4M3 block scales (NVFP4) or the fp32 row scale (INT4), kept raw
         int off;
-        const uint8_t* sl = locate(r, off) + p.half;
-        // CPT channels from vcb * CPT: CPT/2 code bytes, one NVFP4 block scale (CPT == 16) or the row scale
-        const uint8_t* cp = sl + (int64_t)off * (D / 2) + vcb * (CPT / 2);
-        if (CPT == 16) {
-          const u32x2_t w = ld_global<u32x2_t>(cp);
-          vr[0].x = w.x;
-          vr[0].y = w.y;
+        const uint8_t* sl = locate(krow0, off) + kv * p.half;
+        const uint8_t* cp = sl + (int64_t)off * (D / 2) + kseg * (D / 16);
+        if (D == 256) {
+          reg[0] = ld_global<u32x4_t>(cp);
         } else {
-          vr[0].x = ld_global<uint32_t>(cp);
+          const u32x2_t w = ld_global<u32x2_t>(cp);
+          reg[0].x = w.x;
+          reg[0].y = w.y;
         }
+        const uint8_t* sc = sl + p.scales_off;
         if (SRC == FMT_NVFP4)
-          vr[0].z = ld_global<uint8_t>(sl + p.scales_off + (int64_t)off * (D / 16) + vcb * CPT / 16);
+          reg[1].x = D == 256 ? (uint32_t)ld_global<uint16_t>(sc + (int64_t)off * (D / 16) + 2 * kseg)
+                              : (uint32_t)ld_global<uint8_t>(sc + (int64_t)off * (D / 16) + kseg);
         else
-          vr[0].z = ld_global<uint32_t>(sl + p.scales_off + (int64_t)off * 4);
+          reg[1].x = ld_global<uint32_t>(sc + (int64_t)off * 4);
       } else {
+        const __amdgpu_buffer_rsrc_t rs = rows_rsrc(kv ? p.v : p.k, t0);
 #pragma unroll
-        for (int v = 0; v < CPT / 8; v++)
-          vr[v] = __builtin_amdgcn_raw_buffer_load_b128(vrs, vvo + half * rowb + 16 * v, 0, 0);
+        for (int v = 0; v < KV16; v++)
+          reg[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, kvo + (PAGED ? 16 * v : v * KRP * rowb), 0, 0);
       }
     };
-    vload(va, 0);
-    vload(vb, 1);
+    rows(kreg, 0);
+    rows(vreg, 1);
   };
   // bf16 pairs of 8 codes (element 0 low): NVFP4 e2m1 * block scale, exact;
   // INT4 the integers q, exact
@@ -260,59 +220,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   };
   auto lstore = [&](int buf, int64_t t0) {
     uint8_t* base = lds + buf * Lds::BUF;
-    float* kfac = (float*)(base + Lds::KB + Lds::VB);
-    float* vfac = kfac + kExtStep;
-    if (PAGED) {
-      const bool pg = t0 + krow0 < Lp;
-      const u32x4_t raw = kreg[0];
-      const uint32_t ksw = kreg[1].x;  // read before the expansion overwrites them
-      if (pg) {
-        const uint32_t cw[4] = {raw.x, raw.y, raw.z, raw.w};
+    float* fac = (float*)(base + Lds::KB + Lds::VB);  // [K factors][V factors], one per token
+    auto stage = [&](u32x4_t(&reg)[KV16], int kv) {
+      if (PAGED) {
+        const bool pg = t0 + krow0 < Lp;
+        const u32x4_t raw = reg[0];
+        const uint32_t sw = reg[1].x;  // read before the expansion overwrites them
+        if (pg) {
+          const uint32_t cw[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-        for (int v = 0; v < KV16; v++) {
-          uint32_t o[4];
-          expand8(cw[v], SRC == FMT_NVFP4 ? e4m3_decode((ksw >> (8 * (v / 2))) & 0xFFu) : 1.0f, o);
-          kreg[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
+          for (int v = 0; v < KV16; v++) {
+            uint32_t o[4];
+            expand8(cw[v], SRC == FMT_NVFP4 ? e4m3_decode((sw >> (8 * (v / 2))) & 0xFFu) : 1.0f, o);
+            reg[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
+          }
         }
+        if (kseg == 0) fac[kv * kExtStep + krow0] = pg ? (SRC == FMT_NVFP4 ? p.gs[kv] : as_f32(sw)) : 1.0f;
       }
-      if (kseg == 0) kfac[krow0] = pg ? (SRC == FMT_NVFP4 ? p.gs[0] : as_f32(ksw)) : 1.0f;
-    }
+      uint8_t* rbase = base + kv * Lds::KB;
 #pragma unroll
-    for (int v = 0; v < KV16; v++)
-      *(u32x4_t*)(base + (krow_of(v) * Lds::KPD + kel_of(v) / 2) * 4) = kreg[v];
-    if (PAGED) {
-      const bool vapaged = t0 + 2 * vpair < Lp, vbpaged = t0 + 2 * vpair + 1 < Lp;
-      const uint32_t vsa = va[0].z, vsb = vb[0].z;  // scale words (read before the expansion overwrites them)
-      auto vexpand = [&](u32x4_t(&vr)[CPT / 8], uint32_t sw) {
-        const uint32_t codes[2] = {vr[0].x, vr[0].y};
-        const float sc = SRC == FMT_NVFP4 ? e4m3_decode(sw & 0xFFu) : 1.0f;
-#pragma unroll
-        for (int v = 0; v < CPT / 8; v++) {
-          uint32_t o[4];
-          expand8(codes[v], sc, o);
-          vr[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
-        }
-      };
-      if (vapaged) vexpand(va, vsa);
-      if (vbpaged) vexpand(vb, vsb);
-      if (vcb == 0) {
-        vfac[2 * vpair] = vapaged ? (SRC == FMT_NVFP4 ? p.gs[1] : as_f32(vsa)) : 1.0f;
-        vfac[2 * vpair + 1] = vbpaged ? (SRC == FMT_NVFP4 ? p.gs[1] : as_f32(vsb)) : 1.0f;
-      }
-    }
-    uint32_t* vt = (uint32_t*)(base + Lds::KB) + vsw;
-#pragma unroll
-    for (int v = 0; v < CPT / 8; v++) {
-      const uint32_t a4[4] = {va[v].x, va[v].y, va[v].z, va[v].w};
-      const uint32_t b4[4] = {vb[v].x, vb[v].y, vb[v].z, vb[v].w};
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int c = vcb * CPT + 8 * v + 2 * e;
-        // (token a, token b) of channel c, then of channel c + 1
-        vt[Lds::vcol(c, vsj)] = byte_perm(b4[e], a4[e], 0x05040100u);
-        vt[Lds::vcol(c + 1, vsj)] = byte_perm(b4[e], a4[e], 0x07060302u);
-      }
-    }
+      for (int v = 0; v < KV16; v++)
+        *(u32x4_t*)(rbase + (krow_of(v) * Lds::KPD + kel_of(v) / 2) * 4) = reg[v];
+    };
+    stage(kreg, 0);
+    stage(vreg, 1);
   };
 
   float4_t oacc[VT];
@@ -322,7 +253,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 
   auto compute = [&](int buf, int64_t t0) {
     const uint8_t* kb = lds + buf * Lds::BUF;
-    const uint32_t* vt = (const uint32_t*)(kb + Lds::KB);
+    const uint8_t* vrows = kb + Lds::KB;
     float4_t sacc[2];
 #pragma unroll
     for (int hh = 0; hh < 2; hh++) {
@@ -378,10 +309,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     }
     const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, (u32x4_t){hi[0], hi[1], hi[2], hi[3]});
     const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, (u32x4_t){lo[0], lo[1], lo[2], lo[3]});
+    // PV operand of tile t for lane (j, n): channel 16t + n of tokens 4j..4j+3
+    // and 16+4j..16+4j+3 (the order of P's k index), by two transposing reads:
+    // lane (j, n) names channels 16t + 4(n%4) .. +3 of token row 4j + n/4
+    // (then 16 + 4j + n/4) and receives channel 16t + n of the group's 4 rows
+    const uint8_t* vop = vrows + ((4 * j + (n >> 2)) * Lds::KPD + 2 * (n & 3)) * 4;
 #pragma unroll
     for (int t = 0; t < VT; t++) {
-      // channel 16t + n, tokens 4j..4j+3 and 16+4j..16+4j+3 (the order of P's k index)
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(vt + Lds::vcol(16 * t + n, j)));
+      const v4i16_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vop + 32 * t));
+      const v4i16_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vop + 32 * t + 16 * Lds::KPD * 4));
+      const bf16x8_t a = __builtin_bit_cast(
+          bf16x8_t, (u32x4_t){__builtin_bit_cast(u32x2_t, lo4).x, __builtin_bit_cast(u32x2_t, lo4).y,
+                              __builtin_bit_cast(u32x2_t, hi4).x, __builtin_bit_cast(u32x2_t, hi4).y});
       oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, oacc[t], 0, 0, 0);
       oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, oacc[t], 0, 0, 0);
     }

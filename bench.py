@@ -55,6 +55,9 @@ WORKLOADS = {
     "fp8_32k": dict(fmt=3, batch=32, ctx=32768, page=16, shuffled=False, kind="lognormal",
                     desc="comparator: the 32K headline shape with an FP8 E4M3 per-tensor cache (512 B per "
                          "token and head against NVFP4's 288 B)"),
+    "ext32k": dict(fmt=1, batch=1, ctx=32768, page=16, shuffled=False, kind="lognormal", prefix=True,
+                   desc="extend only (profiling): NVFP4, batch 1, a 32,768-token cached prefix, prefix dequant, "
+                        "then a 4,096-token chunk through the workspace and the fused extend"),
     "k8v4_32k": dict(fmt=4, batch=32, ctx=32768, page=16, shuffled=False, kind="lognormal",
                      desc="split precision: the 32K headline shape with FP8 keys and NVFP4 values (400 B per "
                           "token and head)"),
@@ -175,6 +178,29 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> str:
     return "\n".join(lines)
 
 
+def summarize_counters(dirs: list[str], kernel: str) -> str:
+    """Markdown table: per kernel (name and grid) matching `kernel`, the
+    per-dispatch average of every counter found in the rocprofv3 --pmc csv
+    output directories `dirs` (one directory per counter pass)."""
+    agg = {}
+    counters = []
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            name = r["Kernel_Name"].split("(")[0]
+            key = (name, r["Grid_Size"])
+            c = r["Counter_Name"]
+            if c not in counters:
+                counters.append(c)
+            agg.setdefault(key, {}).setdefault(c, []).append(float(r["Counter_Value"]))
+    lines = ["| kernel | grid | " + " | ".join(counters) + " |", "|---|---|" + "---|" * len(counters)]
+    for (name, grid), cs in sorted(agg.items()):
+        vals = [f"{sum(cs[c]) / len(cs[c]):,.0f}" if c in cs else "" for c in counters]
+        lines.append(f"| `{name}` | {grid} | " + " | ".join(vals) + " |")
+    return "\n".join(lines) + "\n"
+
+
 def summarize_trace(trace_dir: str, bench_json: str | None) -> str:
     """Markdown table of kernel durations (rocprofv3 --kernel-trace, csv output) per
     kernel and launch grid, plus the bench's own live figures for comparison."""
@@ -228,6 +254,9 @@ def parse():
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print a kernel-duration table of a rocprofv3 --kernel-trace csv run (no GPU use)")
     ap.add_argument("--bench-json", help="with --summarize-trace: the JSON line printed by the traced run")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="print per-dispatch counter averages of the kernels named by --kernel")
+    ap.add_argument("--kernel", default="extend_kernel", help="with --summarize-counters: kernel name filter")
     return ap.parse_args()
 
 
@@ -618,6 +647,9 @@ def main():
         return
     if args.summarize_trace:
         sys.stdout.write(summarize_trace(args.summarize_trace, args.bench_json))
+        return
+    if args.summarize_counters:
+        sys.stdout.write(summarize_counters(args.summarize_counters, args.kernel))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the split-context path is "

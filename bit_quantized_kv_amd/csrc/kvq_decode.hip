@@ -337,9 +337,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   const float sm = p.sm_scale * kLog2e * ldexpf(1.0f, -kq) * (FMT != FMT_INT4 ? p.gs[0] : 1.0f);
 
   const float lo_sel = n < 8 ? 0.0f : 1.0f;  // DUP: lanes n >= 8 carry the low fp16 part of p
-  // byte of block (n * D / 256) within its scale dword, from two dwords -> bytes 0, 1
+  // byte of block (n * D / 256) within its scale dword, from two dwords -> bytes 0, 2
   const uint32_t vb_byte = ((n * D) / 256) & 3;
-  const uint32_t vsel = vb_byte | ((4 + vb_byte) << 8) | 0x0C0C0000u;
+  const uint32_t vsel = vb_byte | ((4 + vb_byte) << 16) | 0x0C000C00u;
+  // the lane's two K block scales, bytes 2 (j & 1) and 2 (j & 1) + 1 of its
+  // scale dword -> bytes 0, 2
+  const uint32_t ksel = (2 * (j & 1)) | ((2 * (j & 1) + 1) << 16) | 0x0C000C00u;
 
   float4_t oacc[VT];
 #pragma unroll
@@ -360,10 +363,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       for (int v = 0; v < VEC; v++) {
         half2_t s_lo = {}, s_hi = {};
         if (FMT == FMT_NVFP4) {
-          // the lane's two block scales (bytes 0, 1), each as scale * 2^-8 in both halves
-          const uint32_t sb = R.ks[h][v] >> (16 * (j & 1));
-          s_lo = u32_as_h2(e4m3_to_h_x2m8(sb) * 0x00010001u);
-          s_hi = u32_as_h2(e4m3_to_h_x2m8(sb >> 8) * 0x00010001u);
+          // the lane's two block scales as (scale_0, scale_1) * 2^-8 (the
+          // e4m3_to_h_x2m8 move on both halves at once), each broadcast to a pair
+          const half2_t s2 = u32_as_h2(e4m3_to_h_x2m8_pair(byte_perm(0u, R.ks[h][v], ksel)));
+          s_lo = (half2_t){s2[0], s2[0]};
+          s_hi = (half2_t){s2[1], s2[1]};
         }
 #pragma unroll
         for (int w = 0; w < 4; w++) {
@@ -391,17 +395,37 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       }
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        const bool valid = FULL || T + 16 * h + 4 * j + q < L;
         float x = sacc[h][q] * sm;
         if (FMT == FMT_INT4) x *= ksc[q];
-        s[h][q] = valid ? x : -__builtin_inff();
+        s[h][q] = x;
         if (FMT == FMT_INT4) {
-          sv[h][q] = valid ? vsc[q] : 0.0f;
-          const float lv = fmaxf(log2f(sv[h][q]), -64.0f);
-          cand[h][q] = valid ? x + lv : -__builtin_inff();
-        } else {
-          cand[h][q] = s[h][q];
+          sv[h][q] = vsc[q];
+          cand[h][q] = x + fmaxf(log2f(vsc[q]), -64.0f);
         }
+      }
+    }
+    // only the chunk holding the sequence's end has tokens past it (a
+    // workgroup-uniform test, so other chunks skip the masking)
+    if (!FULL && T + 32 > L) {
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          if (T + 16 * h + 4 * j + q >= L) {
+            s[h][q] = -__builtin_inff();
+            if (FMT == FMT_INT4) {
+              sv[h][q] = 0.0f;
+              cand[h][q] = -__builtin_inff();
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        if (FMT != FMT_INT4) cand[h][q] = s[h][q];
         cmax = fmaxf(cmax, cand[h][q]);
       }
     }
@@ -454,8 +478,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
           // bytes are arbitrary but decode finite, and p is exactly 0 there.
           const uint32_t d0 = pp == 0 ? quad_bcast<0>(R.vs[h]) : quad_bcast<2>(R.vs[h]);
           const uint32_t d1 = pp == 0 ? quad_bcast<1>(R.vs[h]) : quad_bcast<3>(R.vs[h]);
-          const uint32_t ab = byte_perm(d1, d0, vsel);  // bytes [s_a, s_b, 0, 0]
-          vsc2[h][pp] = u32_as_h2(e4m3_to_h_x2m8(ab) | (e4m3_to_h_x2m8(ab >> 8) << 16));
+          const uint32_t ab = byte_perm(d1, d0, vsel);  // bytes [s_a, 0, s_b, 0]
+          vsc2[h][pp] = u32_as_h2(e4m3_to_h_x2m8_pair(ab));
         }
       }
     }

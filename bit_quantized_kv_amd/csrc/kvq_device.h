@@ -158,6 +158,10 @@ __device__ inline float e4m3_decode(uint32_t code) {
 // is dropped so even corrupt bytes give finite values.
 __device__ inline uint32_t e4m3_to_h_x2m8(uint32_t b) { return (b & 0x7Fu) << 7; }
 
+// The same for two code bytes at bytes 0 and 2 of x (bytes 1 and 3 zero):
+// both fp16 halves in one shift and one mask.
+__device__ inline uint32_t e4m3_to_h_x2m8_pair(uint32_t x) { return (x << 7) & 0x3F803F80u; }
+
 // Two E2M1 nibbles (byte `sel` of w: low nibble -> element 0, high -> element
 // 1) as exact fp16 values times 2^8 (v_cvt_scalef32_pk_f16_fp4; that
 // instruction applies only the exponent of its scale operand, so the 2^8 is

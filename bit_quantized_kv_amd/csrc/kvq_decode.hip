@@ -65,12 +65,13 @@ struct ChunkRegs {
 struct PageWalk {
   const DecodeParams& p;
   const int L;
-  const uint8_t* head_base;  // pool + g * slab
-  const int32_t* pages;      // block_table row of sequence b
+  const uint8_t* head_base;      // pool + g * slab
+  __amdgpu_buffer_rsrc_t pages;  // block_table row of sequence b
 
   __device__ PageWalk(const DecodeParams& p_, int b, int g, int L_) : p(p_), L(L_) {
     head_base = p.pool + (int64_t)g * p.slab;
-    pages = p.block_table + (int64_t)b * p.max_pages;
+    pages = __builtin_amdgcn_make_buffer_rsrc((void*)(p.block_table + (int64_t)b * p.max_pages), (short)0,
+                                              p.max_pages * 4, 0x00020000);
   }
 
   // Position of a chunk in the page table, advanced without division: the
@@ -97,9 +98,10 @@ struct PageWalk {
     }
   }
 
-  // Where a chunk's two 16-token halves live: page ids (read with a vector
-  // load, kept out of the scalar counter, well before use) and rows.  A half
-  // past the end of the sequence repeats the first half.
+  // Where a chunk's two 16-token halves live: page ids (read with vector
+  // loads whose table offsets are scalar, so the walk itself stays on the
+  // scalar unit and the wait stays off the scalar counter; issued well before
+  // use) and rows.  A half past the end of the sequence repeats the first half.
   struct ChunkRef {
     int2 pg;
     int row0, row1;
@@ -114,8 +116,9 @@ struct PageWalk {
         i1 += 1;
       }
     }
-    asm volatile("" : "+v"(i0), "+v"(i1));
-    return ChunkRef{make_int2(ld_global<int32_t>(pages + i0), ld_global<int32_t>(pages + i1)), k.row, row1};
+    return ChunkRef{make_int2(__builtin_amdgcn_raw_buffer_load_b32(pages, 0, 4 * i0, 0),
+                              __builtin_amdgcn_raw_buffer_load_b32(pages, 0, 4 * i1, 0)),
+                    k.row, row1};
   }
 
   // Buffer descriptor of one slab: base address in SGPRs, range-checked to
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   extern __shared__ float smem[];  // [G][D] partial o, then [kWaves][G] (m, l)
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: the page walk stays scalar
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int L = p.seq_lens[b];
   const int G = p.group;
@@ -714,7 +717,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   extern __shared__ float smem[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: the page walk stays scalar
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int L = p.seq_lens[b];
   const int G = p.group;

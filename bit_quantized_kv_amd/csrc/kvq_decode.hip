@@ -379,6 +379,47 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         }
       }
     }
+    // (value-side preparation first: it does not depend on the scores and
+    // fills the wait for the QK products)
+    // ---------------- V scales of the token pairs (2pp, 2pp + 1) of each half
+    half2_t vsc2[2][2];
+    if (Dec::VNV) {
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+#pragma unroll
+        for (int pp = 0; pp < 2; pp++) {
+          // dwords of scale rows 4j + 2pp and 4j + 2pp + 1 (quad lanes 2pp, 2pp+1);
+          // (s_a, s_b) * 2^-8 as an fp16 pair.  Past the end of the sequence the
+          // bytes are arbitrary but decode finite, and p is exactly 0 there.
+          const uint32_t d0 = pp == 0 ? quad_bcast<0>(R.vs[h]) : quad_bcast<2>(R.vs[h]);
+          const uint32_t d1 = pp == 0 ? quad_bcast<1>(R.vs[h]) : quad_bcast<3>(R.vs[h]);
+          const uint32_t ab = byte_perm(d1, d0, vsel);  // bytes [s_a, 0, s_b, 0]
+          vsc2[h][pp] = u32_as_h2(e4m3_to_h_x2m8_pair(ab));
+        }
+      }
+    }
+    // token pairs (2i, 2i+1) of the value codes nibble-interleaved so one
+    // conversion yields (token a, token b) of a single channel; groups of 4
+    // tiles share the interleaved word of each pair (sel 0: even channels, 1: odd)
+    uint32_t vpw[VW][2][2][2];
+    if (Dec::VNV) {
+#pragma unroll
+      for (int d = 0; d < VW; d++) {
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+#pragma unroll
+          for (int pp = 0; pp < 2; pp++) {
+            const uint32_t a = R.vw[h][2 * pp][d], bb = R.vw[h][2 * pp + 1][d];
+            vpw[d][0][h][pp] = bitfield_insert(0x0F0F0F0Fu, a, bb << 4);
+            vpw[d][1][h][pp] = bitfield_insert(0x0F0F0F0Fu, a >> 4, bb);
+            // computed here, not sunk past the softmax's branches to the PV loop
+            asm volatile("" : "+v"(vpw[d][0][h][pp]), "+v"(vpw[d][1][h][pp]));
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; h++) asm volatile("" : "+v"(vsc2[h][0]), "+v"(vsc2[h][1]));
+    }
     // ---------------- scores (log2 units) and chunk max
     float s[2][4], cand[2][4], sv[2][4];
     float cmax = -__builtin_inff();
@@ -469,43 +510,15 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         }
       }
     }
-    // ---------------- V scales of the token pairs (2pp, 2pp + 1) of each half
-    half2_t vsc2[2][2];
-    if (Dec::VNV) {
-#pragma unroll
-      for (int h = 0; h < 2; h++) {
-#pragma unroll
-        for (int pp = 0; pp < 2; pp++) {
-          // dwords of scale rows 4j + 2pp and 4j + 2pp + 1 (quad lanes 2pp, 2pp+1);
-          // (s_a, s_b) * 2^-8 as an fp16 pair.  Past the end of the sequence the
-          // bytes are arbitrary but decode finite, and p is exactly 0 there.
-          const uint32_t d0 = pp == 0 ? quad_bcast<0>(R.vs[h]) : quad_bcast<2>(R.vs[h]);
-          const uint32_t d1 = pp == 0 ? quad_bcast<1>(R.vs[h]) : quad_bcast<3>(R.vs[h]);
-          const uint32_t ab = byte_perm(d1, d0, vsel);  // bytes [s_a, 0, s_b, 0]
-          vsc2[h][pp] = u32_as_h2(e4m3_to_h_x2m8_pair(ab));
-        }
-      }
-    }
     // ---------------- PV.  The A operand of tile t holds channel t of the
     // lane's 16-channel segment for the 8 tokens 4j..4j+3 of each half, as
     // fp16 pairs (token 2i, token 2i + 1).
     if (Dec::VNV) {
-      // token pairs (2i, 2i+1) nibble-interleaved so one conversion yields
-      // (token a, token b) of a single channel; groups of 4 tiles share the
-      // interleaved word of each pair (sel 0: even channels, 1: odd)
 #pragma unroll
       for (int d = 0; d < VW; d++) {
 #pragma unroll
         for (int sel = 0; sel < 2; sel++) {
-          uint32_t pw[2][2];
-#pragma unroll
-          for (int h = 0; h < 2; h++) {
-#pragma unroll
-            for (int pp = 0; pp < 2; pp++) {
-              const uint32_t a = R.vw[h][2 * pp][d], bb = R.vw[h][2 * pp + 1][d];
-              pw[h][pp] = sel == 0 ? bitfield_insert(0x0F0F0F0Fu, a, bb << 4) : bitfield_insert(0x0F0F0F0Fu, a >> 4, bb);
-            }
-          }
+          const uint32_t(&pw)[2][2] = vpw[d][sel];
 #pragma unroll
           for (int k = 0; k < 4; k++) {
             const int t = 8 * d + 2 * k + sel;

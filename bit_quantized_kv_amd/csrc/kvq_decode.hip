@@ -420,6 +420,27 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
       for (int h = 0; h < 2; h++) asm volatile("" : "+v"(vsc2[h][0]), "+v"(vsc2[h][1]));
     }
+    // INT4: nibbles of tokens a, b interleaved 16 bits apart (and the words
+    // shifted by 8: nibble positions 2, 3 -> 0, 1), pinned here likewise
+    uint32_t vpw8[VW][2][2][2];
+    if (!Dec::VNV) {
+#pragma unroll
+      for (int d = 0; d < VW; d++) {
+#pragma unroll
+        for (int sel = 0; sel < 2; sel++) {
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+#pragma unroll
+            for (int pp = 0; pp < 2; pp++) {
+              const uint32_t a = R.vw[h][2 * pp][d], bb = R.vw[h][2 * pp + 1][d];
+              vpw[d][sel][h][pp] = byte_perm(bb, a, sel == 0 ? 0x05040100u : 0x07060302u);
+              vpw8[d][sel][h][pp] = vpw[d][sel][h][pp] >> 8;
+              asm volatile("" : "+v"(vpw[d][sel][h][pp]), "+v"(vpw8[d][sel][h][pp]));
+            }
+          }
+        }
+      }
+    }
     // ---------------- scores (log2 units) and chunk max
     float s[2][4], cand[2][4], sv[2][4];
     float cmax = -__builtin_inff();
@@ -444,7 +465,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         s[h][q] = x;
         if (FMT == FMT_INT4) {
           sv[h][q] = vsc[q];
-          cand[h][q] = x + fmaxf(log2f(vsc[q]), -64.0f);
+          // the running max also bounds p * (value scale): the scale's binary
+          // exponent (frexp: scale < 2^e) is an upper bound of its log2 that
+          // keeps p * scale below 2^slack; clamped so tiny scales cannot push
+          // exp2(s - max) out of fp32 range
+          cand[h][q] = x + (float)max(__builtin_amdgcn_frexp_exp(vsc[q]), -64);
         }
       }
     }
@@ -552,21 +577,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       for (int d = 0; d < VW; d++) {
 #pragma unroll
         for (int sel = 0; sel < 2; sel++) {
-          uint32_t pw[2][2];
-#pragma unroll
-          for (int h = 0; h < 2; h++) {
-#pragma unroll
-            for (int pp = 0; pp < 2; pp++) {
-              const uint32_t a = R.vw[h][2 * pp][d], bb = R.vw[h][2 * pp + 1][d];
-              pw[h][pp] = byte_perm(bb, a, sel == 0 ? 0x05040100u : 0x07060302u);
-            }
-          }
-          uint32_t pw8[2][2];  // the words shifted by 8 (nibble positions 2, 3 -> 0, 1)
-#pragma unroll
-          for (int h = 0; h < 2; h++) {
-#pragma unroll
-            for (int pp = 0; pp < 2; pp++) pw8[h][pp] = pw[h][pp] >> 8;
-          }
+          const uint32_t(&pw)[2][2] = vpw[d][sel];
+          const uint32_t(&pw8)[2][2] = vpw8[d][sel];
 #pragma unroll
           for (int k = 0; k < 4; k++) {
             // odd tiles come out times 16, undone with the output scale

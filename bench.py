@@ -100,7 +100,7 @@ def decode_source_digest() -> str:
 
 
 def counters_path(workload: str) -> str:
-    fmt = "nvfp4" if WORKLOADS[workload]["fmt"] == 1 else "int4"
+    fmt = {1: "nvfp4", 2: "int4", 3: "fp8", 4: "k8v4"}[WORKLOADS[workload]["fmt"]]
     return os.path.join(REPO, "profiles", f"decode_{fmt}_{workload}_counters.md")
 
 
@@ -677,6 +677,10 @@ def main():
         torch.cuda.synchronize()
         time.sleep(args.cooldown)
         r, _ = run_workload(torch, kvq, inputs, name, args.secondary_steps or args.steps, args.warmup, args.layers)
+        rec, _ = load_counter_summary(name)
+        if rec is not None:  # HBM bytes per decode call from this workload's own counter passes
+            r["hbm_traffic_bytes_per_call"] = rec["traffic_bytes_per_call"]
+            r["hbm_traffic_over_algorithmic"] = rec["traffic_bytes_per_call"] / rec["algorithmic_bytes_per_call"]
         secondary[name] = r
         print(f"[bench] {name}: step {r['step_ms']:.3f} ms, decode call {r['decode_call_us']:.1f} us "
               f"({r['decode_call_gbs']:.0f} GB/s), {time.time() - t1:.1f} s", file=sys.stderr, flush=True)

@@ -176,7 +176,9 @@ kvq_status kvq_decode_workspace_size(const kvq_cache* cache, int32_t batch, int3
  * fixed order, so results are bitwise reproducible for a fixed split count.
  *   q            device bf16 [batch][num_q_heads][head_dim]
  *   block_table  device int32 [batch][max_pages]; only the first
- *                ceil(seq_lens[b] / page_size) entries of a row are read
+ *                ceil(seq_lens[b] / page_size) entries of a row are read (the
+ *                reads are bounded by max_pages: an index past the row, from a
+ *                seq_lens value above max_pages * page_size, reads page 0)
  *   seq_lens     device int32 [batch], each in [0, max_seq_len]; 0 gives o = 0
  *                and lse = -inf
  *   max_seq_len  host upper bound of seq_lens, fixes the split plan

@@ -498,8 +498,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         cmax = fmaxf(cmax, cand[h][q]);
       }
     }
-    cmax = max_xor16_xor32(cmax);
+    // a row's max can only pass m_run + slack where one of its lanes' own
+    // maxima does, so the wave-wide test needs no cross-lane reduction; the
+    // row max (over the row's 4 lanes) is formed only when some row moves
     if (__builtin_amdgcn_ballot_w64(cmax > m_run + kRescaleSlack) != 0) {
+      cmax = max_xor16_xor32(cmax);
       const float m_new = cmax > m_run + kRescaleSlack ? cmax : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -852,8 +855,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
       for (int t = 0; t < VT; t++) R.vw[t] &= mask;
     }
-    cmax = max_xor16_xor32(cmax);
+    // a row's max can only pass m_run + slack where one of its lanes' own
+    // maxima does, so the wave-wide test needs no cross-lane reduction; the
+    // row max (over the row's 4 lanes) is formed only when some row moves
     if (__builtin_amdgcn_ballot_w64(cmax > m_run + kRescaleSlack) != 0) {
+      cmax = max_xor16_xor32(cmax);
       const float m_new = cmax > m_run + kRescaleSlack ? cmax : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;

@@ -9,11 +9,15 @@
 // token, the K and V rows decoded from their packed nibbles and scales in
 // registers, never expanded in memory.
 //
-// Structure (one 64-lane wavefront per workgroup):
+// Structure (kDecodeWaves = 4 wavefronts per workgroup):
 //   grid = (splits, KV heads, batch).  A split is a run of whole 32-token
-//   chunks of one (sequence, KV head); its wavefront computes the partial
-//   (o, max, sum) of all G <= 16 query heads of the group and a second kernel
-//   merges the splits with the log-sum-exp rule in split order.
+//   chunks of one (sequence, KV head), dealt to the workgroup's wavefronts
+//   round-robin; each wavefront keeps a partial (o, max, sum) of all G <= 16
+//   query heads of the group, the workgroup combines its wavefronts' partials
+//   in LDS, and a second kernel merges the splits with the log-sum-exp rule
+//   in split order.  The page walk (chunk cursor, page-table reads, slab
+//   descriptors) is wavefront-uniform and runs on the scalar unit; each
+//   chunk's loads are issued one chunk ahead of its math.
 //   Per 32-token chunk (two 16-token halves, each inside one page):
 //     QK  S^T[token][query] = K[token][ch] Q^T[ch][query] with
 //         v_mfma_f32_16x16x32_f16 (G padded to 16); lane (j = lane/16,
@@ -26,15 +30,19 @@
 //         MFMA; lane (j, r) loads the 16-channel segment r of tokens
 //         4j..4j+3 of each half (again fully coalesced: 4 rows per load);
 //         token pairs are interleaved at nibble level so one conversion
-//         yields an fp16 pair (token a, token b) of one channel.
-//   Dequantization: NVFP4 nibbles -> fp16 with v_cvt_scalef32_pk_f16_fp4
-//   (unit scale), times the E4M3 block scale with a packed fp16 multiply --
+//         yields an fp16 pair (token a, token b) of one channel.  The value
+//         scales and the interleave are computed before the softmax, where
+//         they fill the wait for the QK products.
+//   Dequantization: NVFP4 nibbles -> fp16 times 2^8 with
+//   v_cvt_scalef32_pk_f16_fp4 (its scale operand acts as a power of two),
+//   times the E4M3 block scale times 2^-8 with a packed fp16 multiply --
 //   e2m1 * e4m3 has at most 6 significant bits, so K and V are exact in fp16;
 //   the per-layer global scales are applied to the fp32 scores / outputs.
 //   INT4 nibbles -> fp16 exactly via the 1024-offset trick; the per-token
 //   scales are folded into the score (K) and into the probability (V).
 //   q is scaled by a power of two so its largest magnitude sits in
-//   [2^14, 2^15), keeping fp16 exact for every finite bf16 input range.
+//   [2^14, 2^15): every bf16 element within 2^32 of the largest is then exact
+//   in fp16 (smaller ones round, far below the fp32 accumulation's precision).
 #include <type_traits>
 
 #include "kvq_device.h"

@@ -279,9 +279,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
         x *= kfac[tok];
         vf[e] = vfac[tok];
       }
-      s[e] = !masked || tok <= last ? x : -__builtin_inff();
-      cmax = fmaxf(cmax, s[e]);
+      s[e] = x;
     }
+    // only steps that reach a row's causal limit need the mask (a
+    // workgroup-uniform test, so the others skip it)
+    if (masked) {
+#pragma unroll
+      for (int e = 0; e < 8; e++)
+        if (16 * (e / 4) + 4 * j + (e % 4) > last) s[e] = -__builtin_inff();
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e++) cmax = fmaxf(cmax, s[e]);
     // a row's max can only pass m_run + slack where one of its lanes' own
     // maxima does, so the wave-wide test needs no cross-lane reduction; the
     // row max (over the row's 4 lanes) is formed only when some row moves

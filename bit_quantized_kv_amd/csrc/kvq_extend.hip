@@ -146,32 +146,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     return __builtin_amdgcn_make_buffer_rsrc((void*)(rows + (t0 - row_base) * p.kv_stride), (short)0, (int)bytes,
                                              0x00020000);
   };
-  auto gload = [&](int step) {
+  // paged prefix: page-table slot and row of this thread's row (krow0) in the
+  // step starting at token t0.  The step's first token sits in page t0 / P at
+  // row t0 % P; a page holds at least 16 rows, so a token of the step is at
+  // most two pages further.
+  auto page_slot = [&](int64_t t0, int& off) -> int {
+    const int pi0 = (int)(t0 / p.page_size);
+    int o = (int)(t0 - (int64_t)pi0 * p.page_size) + krow0, pi = pi0;
+    if (o >= p.page_size) { o -= p.page_size; pi++; }
+    if (o >= p.page_size) { o -= p.page_size; pi++; }
+    off = o;
+    return pi;
+  };
+  // the page holding this thread's row of a step, read from the page table
+  // one step before the step's codes are loaded, so the code loads never wait
+  // for it
+  auto page_id = [&](int step) -> int {
     const int64_t t0 = (int64_t)step * kExtStep;
-    // paged prefix: the step's first token t0 sits in page pi0 at row off0; a
-    // page holds at least 16 rows, so a token of the step is at most two pages
-    // further
-    int off0 = 0;
-    int pi0 = 0;
-    if (PAGED && t0 < Lp) {
-      pi0 = (int)(t0 / p.page_size);
-      off0 = (int)(t0 - (int64_t)pi0 * p.page_size);
-    }
-    // slab and row of token t0 + r (r < 32)
-    auto locate = [&](int r, int& off) -> const uint8_t* {
-      int o = off0 + r, pi = pi0;
-      if (o >= p.page_size) { o -= p.page_size; pi++; }
-      if (o >= p.page_size) { o -= p.page_size; pi++; }
-      off = o;
-      return p.pool + ((int64_t)p.pages[pi] * p.num_kv_heads + g) * p.slab;
-    };
+    if (!PAGED || step >= nsteps || t0 + krow0 >= Lp) return 0;
+    int off;
+    return ld_global<int32_t>(p.pages + page_slot(t0, off));
+  };
+  auto gload = [&](int step, int pid) {
+    const int64_t t0 = (int64_t)step * kExtStep;
     // one row's staging registers: K (kv 0) or V (kv 1)
     auto rows = [&](u32x4_t(&reg)[KV16], int kv) {
       if (PAGED && t0 + krow0 < Lp) {
         // the row's D/8 elements from kseg * D/8: D/16 code bytes, and D/128
         // E4M3 block scales (NVFP4) or the fp32 row scale (INT4), kept raw
         int off;
-        const uint8_t* sl = locate(krow0, off) + kv * p.half;
+        (void)page_slot(t0, off);
+        const uint8_t* sl = p.pool + ((int64_t)pid * p.num_kv_heads + g) * p.slab + kv * p.half;
         const uint8_t* cp = sl + (int64_t)off * (D / 2) + kseg * (D / 16);
         if (D == 256) {
           reg[0] = ld_global<u32x4_t>(cp);
@@ -218,6 +223,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       out[e] = bf16x2_rne(x);
     }
   };
+  // NVFP4 global scales, read once (a scalar load inside the loop would wait
+  // on the LDS counter it shares)
+  float gsf[2] = {1.0f, 1.0f};
+  if (SRC == FMT_NVFP4) {
+    gsf[0] = p.gs[0];
+    gsf[1] = p.gs[1];
+  }
   auto lstore = [&](int buf, int64_t t0) {
     uint8_t* base = lds + buf * Lds::BUF;
     float* fac = (float*)(base + Lds::KB + Lds::VB);  // [K factors][V factors], one per token
@@ -235,7 +247,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
             reg[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
           }
         }
-        if (kseg == 0) fac[kv * kExtStep + krow0] = pg ? (SRC == FMT_NVFP4 ? p.gs[kv] : as_f32(sw)) : 1.0f;
+        if (kseg == 0) fac[kv * kExtStep + krow0] = pg ? (SRC == FMT_NVFP4 ? gsf[kv] : as_f32(sw)) : 1.0f;
       }
       uint8_t* rbase = base + kv * Lds::KB;
 #pragma unroll
@@ -337,15 +349,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     }
   };
 
-  gload(0);
+  int pid = page_id(0);
+  gload(0, pid);
   lstore(0, 0);
-  if (nsteps > 1) gload(1);
+  pid = page_id(1);
+  if (nsteps > 1) gload(1, pid);
+  pid = page_id(2);
   __syncthreads();
   for (int st = 0; st < nsteps; st++) {
     compute(st & 1, (int64_t)st * kExtStep);
     if (st + 1 < nsteps) {
       lstore((st + 1) & 1, (int64_t)(st + 1) * kExtStep);
-      if (st + 2 < nsteps) gload(st + 2);
+      if (st + 2 < nsteps) {
+        gload(st + 2, pid);
+        pid = page_id(st + 3);
+      }
     }
     __syncthreads();
   }

@@ -27,6 +27,8 @@
 // INT4 q) and the remaining factor of each token (NVFP4: the global scale;
 // INT4: the token's scale; chunk tokens: 1) is staged per token and applied
 // to its score (K) and to its probability in the PV product (V).
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -101,15 +103,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   const int64_t lim_min = (int64_t)p.prefix_len + row0 / G;
   const int nsteps = (int)(kmax / kExtStep) + 1;
 
-  bf16x8_t qop[KCH];
-  {
+  // NVFP4 global scales, read once (a scalar load inside the loop would wait
+  // on the LDS counter it shares)
+  float gsf[2] = {1.0f, 1.0f};
+  if (SRC == FMT_NVFP4) {
+    gsf[0] = p.gs[0];
+    gsf[1] = p.gs[1];
+  }
+  // NVFP4 prefix: the steps whose 32 keys all lie in the cached prefix (every
+  // row sees all of them: no mask) run in fp16 -- codes expanded as
+  // (e2m1 * 2^8) * (E4M3 * 2^-8), exact; the global scales, uniform over these
+  // steps, go to the score (K) and, once after the last of them, to the output
+  // accumulators (V); p in fp16 (11 bits) feeds a single PV MFMA.  The steps
+  // from the first one that reaches the chunk on take the bf16 path.
+  constexpr bool F16P = SRC == FMT_NVFP4;
+  const int nsteps16 = F16P ? (int)min((int64_t)p.prefix_len / kExtStep, (int64_t)nsteps - 1) : 0;
+
+  // the query row's MFMA operands: bf16 bits, or on the fp16 steps fp16 bits
+  // of q * 2^kq, the power of two that puts the row's largest magnitude in
+  // [2^14, 2^15) (every bf16 element within 2^31 of it is then exact)
+  u32x4_t qw[KCH];
+  auto load_q = [&]() {
     const uint16_t* qrow = p.q + (int64_t)irow * p.q_stride + (int64_t)h * D + 8 * j;
 #pragma unroll
     for (int m = 0; m < KCH; m++) {
       u32x4_t raw = ld_global<u32x4_t>(qrow + 32 * m);
       if (!row_ok) raw = (u32x4_t){0u, 0u, 0u, 0u};
-      qop[m] = __builtin_bit_cast(bf16x8_t, raw);
+      qw[m] = raw;
     }
+  };
+  load_q();
+  float ck = 1.0f;  // fp16 steps: gs_K * 2^-kq turns the MFMA sum into the score
+  if (F16P && nsteps16 > 0) {
+    float qmax = 0.0f;
+#pragma unroll
+    for (int m = 0; m < KCH; m++) {
+      const uint32_t wq[4] = {qw[m].x, qw[m].y, qw[m].z, qw[m].w};
+#pragma unroll
+      for (int c = 0; c < 4; c++)
+        qmax = fmaxf(qmax, fmaxf(__builtin_fabsf(as_f32(wq[c] << 16)), __builtin_fabsf(as_f32(wq[c] & 0xFFFF0000u))));
+    }
+    qmax = max_xor16_xor32(qmax);  // lanes n, n + 16, n + 32, n + 48 hold the row
+    int qexp = 0;
+    if (qmax > 0.0f) (void)frexpf(qmax, &qexp);  // qmax < 2^qexp
+    const int kq = qmax > 0.0f ? 15 - qexp : 0;
+#pragma unroll
+    for (int m = 0; m < KCH; m++) {
+      uint32_t wq[4] = {qw[m].x, qw[m].y, qw[m].z, qw[m].w};
+#pragma unroll
+      for (int c = 0; c < 4; c++)
+        wq[c] = h2_as_u32((half2_t){(_Float16)ldexpf(as_f32(wq[c] << 16), kq),
+                                    (_Float16)ldexpf(as_f32(wq[c] & 0xFFFF0000u), kq)});
+      qw[m] = (u32x4_t){wq[0], wq[1], wq[2], wq[3]};
+    }
+    ck = gsf[0] * ldexpf(1.0f, -kq);
   }
   // scores stay unscaled (q.k, times the token's factor in the paged variant);
   // the running max is kept in the same units and p = 2^(s sm - m sm) is one
@@ -223,13 +270,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       out[e] = bf16x2_rne(x);
     }
   };
-  // NVFP4 global scales, read once (a scalar load inside the loop would wait
-  // on the LDS counter it shares)
-  float gsf[2] = {1.0f, 1.0f};
-  if (SRC == FMT_NVFP4) {
-    gsf[0] = p.gs[0];
-    gsf[1] = p.gs[1];
-  }
   auto lstore = [&](int buf, int64_t t0) {
     uint8_t* base = lds + buf * Lds::BUF;
     float* fac = (float*)(base + Lds::KB + Lds::VB);  // [K factors][V factors], one per token
@@ -257,13 +297,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     stage(kreg, 0);
     stage(vreg, 1);
   };
+  // fp16 staging of an NVFP4 prefix step (every row of it in the prefix): per
+  // code word, four conversions at a 2^8 scale and four packed multiplies by
+  // the block scale times 2^-8, exact (e2m1 * E4M3 has at most 6 significant
+  // bits and lies in [2^-10, 2688])
+  auto lstore16 = [&](int buf) {
+    uint8_t* base = lds + buf * Lds::BUF;
+    auto stage = [&](u32x4_t(&reg)[KV16], int kv) {
+      const u32x4_t raw = reg[0];
+      const uint32_t sw = reg[1].x;
+      const uint32_t cw[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int v = 0; v < KV16; v++) {
+        const uint32_t hb = e4m3_to_h_x2m8(sw >> (8 * (v / 2)));
+        const half2_t s2 = u32_as_h2(hb | (hb << 16));
+        reg[v] = (u32x4_t){h2_as_u32(e2m1x2_to_h2_x256<0>(cw[v]) * s2), h2_as_u32(e2m1x2_to_h2_x256<1>(cw[v]) * s2),
+                           h2_as_u32(e2m1x2_to_h2_x256<2>(cw[v]) * s2), h2_as_u32(e2m1x2_to_h2_x256<3>(cw[v]) * s2)};
+      }
+      uint8_t* rbase = base + kv * Lds::KB;
+#pragma unroll
+      for (int v = 0; v < KV16; v++)
+        *(u32x4_t*)(rbase + (krow_of(v) * Lds::KPD + kel_of(v) / 2) * 4) = reg[v];
+    };
+    stage(kreg, 0);
+    stage(vreg, 1);
+  };
 
   float4_t oacc[VT];
 #pragma unroll
   for (int t = 0; t < VT; t++) oacc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -__builtin_inff(), l_run = 0.0f;
 
-  auto compute = [&](int buf, int64_t t0) {
+  // one step: F16 (a std::bool_constant) selects the fp16 prefix form
+  auto compute = [&](auto f16_tag, int buf, int64_t t0) {
+    constexpr bool F16 = decltype(f16_tag)::value;
     const uint8_t* kb = lds + buf * Lds::BUF;
     const uint8_t* vrows = kb + Lds::KB;
     float4_t sacc[2];
@@ -273,21 +340,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       const uint8_t* krow_p = kb + (16 * hh + n) * Lds::KPD * 4 + 16 * j;
 #pragma unroll
       for (int m = 0; m < KCH; m++) {
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(krow_p + 64 * m));
-        sacc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[m], sacc[hh], 0, 0, 0);
+        const u32x4_t a = *(const u32x4_t*)(krow_p + 64 * m);
+        if constexpr (F16)
+          sacc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                            __builtin_bit_cast(half8_t, qw[m]), sacc[hh], 0, 0, 0);
+        else
+          sacc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                             __builtin_bit_cast(bf16x8_t, qw[m]), sacc[hh], 0, 0, 0);
       }
     }
     float s[8], vf[8];
     const float* kfac = (const float*)(kb + Lds::KB + Lds::VB);
     const float* vfac = kfac + kExtStep;
     float cmax = -__builtin_inff();
-    const bool masked = t0 + kExtStep - 1 > lim_min;  // workgroup-uniform
+    // fp16 steps lie below every row's causal limit
+    const bool masked = !F16 && t0 + kExtStep - 1 > lim_min;  // workgroup-uniform
     const int last = (int)min(lim - t0, (int64_t)kExtStep);  // last visible token of the step, in step units
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       const int tok = 16 * (e / 4) + 4 * j + (e % 4);
       float x = sacc[e / 4][e % 4];
-      if (PAGED) {
+      if (F16) {
+        x *= ck;
+      } else if (PAGED) {
         x *= kfac[tok];
         vf[e] = vfac[tok];
       }
@@ -321,17 +396,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sm, -msm));
       float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], sm, -msm));
       l_run += p0 + p1;
-      if (PAGED) {  // the value factor of each token rides on its probability
-        p0 *= vf[e];
-        p1 *= vf[e + 1];
+      if constexpr (F16) {
+        hi[e / 2] = h2_as_u32((half2_t){(_Float16)p0, (_Float16)p1});
+        lo[e / 2] = 0u;
+      } else {
+        if (PAGED) {  // the value factor of each token rides on its probability
+          p0 *= vf[e];
+          p1 *= vf[e + 1];
+        }
+        const uint32_t hw = bf16x2_rne((float2_t){p0, p1});
+        const float h0 = as_f32(hw << 16), h1 = as_f32(hw & 0xFFFF0000u);
+        hi[e / 2] = hw;
+        lo[e / 2] = bf16x2_rne((float2_t){p0 - h0, p1 - h1});
       }
-      const uint32_t hw = bf16x2_rne((float2_t){p0, p1});
-      const float h0 = as_f32(hw << 16), h1 = as_f32(hw & 0xFFFF0000u);
-      hi[e / 2] = hw;
-      lo[e / 2] = bf16x2_rne((float2_t){p0 - h0, p1 - h1});
     }
-    const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, (u32x4_t){hi[0], hi[1], hi[2], hi[3]});
-    const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, (u32x4_t){lo[0], lo[1], lo[2], lo[3]});
+    const u32x4_t phi = (u32x4_t){hi[0], hi[1], hi[2], hi[3]};
+    const u32x4_t plo = (u32x4_t){lo[0], lo[1], lo[2], lo[3]};
     // PV operand of tile t for lane (j, n): channel 16t + n of tokens 4j..4j+3
     // and 16+4j..16+4j+3 (the order of P's k index), by two transposing reads:
     // lane (j, n) names channels 16t + 4(n%4) .. +3 of token row 4j + n/4
@@ -341,31 +421,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     for (int t = 0; t < VT; t++) {
       const v4i16_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vop + 32 * t));
       const v4i16_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vop + 32 * t + 16 * Lds::KPD * 4));
-      const bf16x8_t a = __builtin_bit_cast(
-          bf16x8_t, (u32x4_t){__builtin_bit_cast(u32x2_t, lo4).x, __builtin_bit_cast(u32x2_t, lo4).y,
-                              __builtin_bit_cast(u32x2_t, hi4).x, __builtin_bit_cast(u32x2_t, hi4).y});
-      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, oacc[t], 0, 0, 0);
-      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, oacc[t], 0, 0, 0);
+      const u32x4_t a = (u32x4_t){__builtin_bit_cast(u32x2_t, lo4).x, __builtin_bit_cast(u32x2_t, lo4).y,
+                                  __builtin_bit_cast(u32x2_t, hi4).x, __builtin_bit_cast(u32x2_t, hi4).y};
+      if constexpr (F16) {
+        oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, phi),
+                                                         oacc[t], 0, 0, 0);
+      } else {
+        const bf16x8_t ab = __builtin_bit_cast(bf16x8_t, a);
+        oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, __builtin_bit_cast(bf16x8_t, phi), oacc[t], 0, 0, 0);
+        oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, __builtin_bit_cast(bf16x8_t, plo), oacc[t], 0, 0, 0);
+      }
     }
   };
 
   int pid = page_id(0);
   gload(0, pid);
-  lstore(0, 0);
+  if (F16P && nsteps16 > 0)
+    lstore16(0);
+  else
+    lstore(0, 0);
   pid = page_id(1);
   if (nsteps > 1) gload(1, pid);
   pid = page_id(2);
   __syncthreads();
-  for (int st = 0; st < nsteps; st++) {
-    compute(st & 1, (int64_t)st * kExtStep);
+  // stage step st + 1 (in its own form) and issue the loads of step st + 2
+  auto advance = [&](int st) {
     if (st + 1 < nsteps) {
-      lstore((st + 1) & 1, (int64_t)(st + 1) * kExtStep);
+      if (F16P && st + 1 < nsteps16)
+        lstore16((st + 1) & 1);
+      else
+        lstore((st + 1) & 1, (int64_t)(st + 1) * kExtStep);
       if (st + 2 < nsteps) {
         gload(st + 2, pid);
         pid = page_id(st + 3);
       }
     }
     __syncthreads();
+  };
+  int st = 0;
+  if constexpr (F16P) {
+    for (; st < nsteps16; st++) {
+      compute(std::true_type{}, st & 1, (int64_t)st * kExtStep);
+      advance(st);
+    }
+    if (nsteps16 > 0) {
+      // on to bf16: the query's bf16 operands again, and the value global
+      // scale of the prefix steps' sum applied once
+      load_q();
+#pragma unroll
+      for (int t = 0; t < VT; t++) oacc[t] *= gsf[1];
+    }
+  }
+  for (; st < nsteps; st++) {
+    compute(std::false_type{}, st & 1, (int64_t)st * kExtStep);
+    advance(st);
   }
 
   // ---- epilogue: each lane column is one query row

@@ -77,6 +77,7 @@ PAGED = [
     (1, 128, 2, 4, 16, 37, 70, (1.0, 0.125)),
     (2, 128, 3, 3, 16, 300, 17, (1.0, 1.0)),
     (1, 256, 2, 6, 16, 0, 50, (0.5, 0.5)),
+    (1, 256, 2, 6, 16, 2000, 40, (0.015625, 0.03125)),
 ]
 
 

@@ -197,13 +197,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   // step starting at token t0.  The step's first token sits in page t0 / P at
   // row t0 % P; a page holds at least 16 rows, so a token of the step is at
   // most two pages further.
+  // Token indices of the prefix fit 31 bits, so the step's page is a
+  // multiply-high by floor((2^32 - 1) / P), which is the quotient or one less,
+  // and one correction (instead of a 64-bit division every step).
+  const uint32_t psz = (uint32_t)p.page_size;
+  const uint32_t pmagic = PAGED ? 0xFFFFFFFFu / psz : 0u;
   auto page_slot = [&](int64_t t0, int& off) -> int {
-    const int pi0 = (int)(t0 / p.page_size);
-    int o = (int)(t0 - (int64_t)pi0 * p.page_size) + krow0, pi = pi0;
-    if (o >= p.page_size) { o -= p.page_size; pi++; }
-    if (o >= p.page_size) { o -= p.page_size; pi++; }
-    off = o;
-    return pi;
+    const uint32_t t = (uint32_t)t0;
+    uint32_t pi = __umulhi(t, pmagic);
+    uint32_t o = t - pi * psz;
+    if (o >= psz) { o -= psz; pi++; }
+    o += (uint32_t)krow0;
+    if (o >= psz) { o -= psz; pi++; }
+    if (o >= psz) { o -= psz; pi++; }
+    off = (int)o;
+    return (int)pi;
   };
   // the page holding this thread's row of a step, read from the page table
   // one step before the step's codes are loaded, so the code loads never wait

@@ -143,3 +143,28 @@ def test_extend_paged_agrees_with_workspace_path():
     a, b = ws.cpu().numpy(), fused.cpu().numpy()
     s = max(1.0, float(np.abs(a).max()))
     assert np.abs(a - b).max() <= 1e-3 * s
+
+
+def test_extend_paged_query_rows_of_any_magnitude():
+    """The fused NVFP4 extend scales each query row by a power of two into fp16's
+    range on the prefix steps: rows from 2^-20 to 2^4 times N(0,1) (near-uniform
+    to near-one-hot attention) still match the oracle."""
+    print("case: paged extend, query rows scaled by 2^-20 .. 2^4", flush=True)
+    from gpu_cases import ATOL, Case
+    D, Hkv, G, P, Lp, n = 256, 2, 6, 16, 700, 40
+    c = Case(1, D, Hkv, G, P, [Lp], kind="lognormal", in_dtype=torch.bfloat16, gs=(1.0, 1.0), seed=901)
+    Hq = Hkv * G
+    kc, vc = inputs.kv_lognormal_channels(59, 0, n, Hkv, D)
+    kc_d, vc_d = bf16(kc).cuda(), bf16(vc).cuda()
+    rng = np.random.default_rng(59)
+    row_scale = np.exp2(rng.integers(-20, 5, size=(n, Hq, 1))).astype(np.float32)
+    q = bf16(inputs.query(59, 1, n, Hq, D).reshape(n, Hq, D) * row_scale).cuda()
+    out = kvq.kvq_extend_attention_paged(c.cache, c.bt_dev[0].contiguous(), Lp, q, kc_d, vc_d,
+                                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kp, vp = _prefix_values(c, Lp)
+    k_all = np.concatenate([kp, kc_d.float().cpu().numpy()])
+    v_all = np.concatenate([vp, vc_d.float().cpu().numpy()])
+    ref, _ = oracle.extend_attention(q.float().cpu().numpy(), k_all, v_all, Lp)
+    s = max(1.0, float(np.abs(ref).max()))
+    check_attention(out.cpu().numpy() / s, ref / s, np.ones(n, np.int32), label="paged, scaled query rows")

@@ -46,9 +46,10 @@ WORKLOADS = {
                   split_sweep=(32, 64, 128, 256, 512),
                   desc="NVFP4, batch 1, context 1,048,576, split-context decode; plus kvq_dequant_prefix of "
                        "the full prefix into a bf16 workspace of 1,048,576 + 4,096 rows"),
-    "int4_220k": dict(fmt=2, batch=8, ctx=220000, page=1600, shuffled=False, kind="student_t",
+    "int4_220k": dict(fmt=2, batch=8, ctx=220000, page=1600, shuffled=False, kind="student_t", fused_extend=True,
                       desc="INT4 per-token-head, batch 8, context 220,000, 1,600-token pages (last page half "
-                           "full); 16 layers assumed"),
+                           "full); 16 layers assumed; plus the fused extend of a 4,096-token chunk over the "
+                           "first sequence's cached prefix"),
     "rot_32k": dict(fmt=1, batch=32, ctx=32768, page=16, shuffled=False, kind="lognormal", rotated=True,
                     desc="the 32K headline shape with a Hadamard-rotated NVFP4 cache: rotated stores, R q in, "
                          "R o rotated back (the decode call here includes both rotations)"),
@@ -565,6 +566,35 @@ def run_workload(torch, kvq, inputs, name, steps, warmup, n_layers, keep_for_cpu
                               "workspace_bytes": 0}
         res["extend_attention_fused"] = fused
         del k_ws, v_ws, qc, oc, kc_rows, vc_rows
+    if w.get("fused_extend"):
+        # the fused extend over this format's pages: a 4,096-token bf16 chunk
+        # over the first sequence's cached prefix (32,768 tokens, and all of it)
+        n = 4096
+        g = torch.Generator(device="cuda")
+        g.manual_seed(inputs.seed_int(wid, 0, 51))
+        kc_rows = torch.randn((n, HKV * D), generator=g, device="cuda").to(torch.bfloat16)
+        vc_rows = torch.randn((n, HKV * D), generator=g, device="cuda").to(torch.bfloat16)
+        qc = torch.randn((n, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
+        oc = torch.empty((n, HQ, D), dtype=torch.bfloat16, device="cuda")
+        fused = {}
+        lay = layers[0]
+        for lp in (32768, L):
+            reps = 1 if lp == L else 5
+            kvq.kvq_extend_attention_paged(lay.cache, lay.bt[0], lp, qc, kc_rows, vc_rows, out=oc)
+            a, b_ = ev(), ev()
+            a.record(stream)
+            for _ in range(reps):
+                kvq.kvq_extend_attention_paged(lay.cache, lay.bt[0], lp, qc, kc_rows, vc_rows, out=oc)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b_) / reps * 1e3
+            flops = 4.0 * HQ * D * (n * lp + n * (n + 1) / 2)
+            fused[str(lp)] = {"prefix_len": lp, "chunk_len": n, "us": us, "flops": flops,
+                              "tflops": flops / (us * 1e-6) / 1e12,
+                              "frac_bf16_mfma_peak": flops / (us * 1e-6) / 2.5e15,
+                              "workspace_bytes": 0}
+        res["extend_attention_fused"] = fused
+        del qc, oc, kc_rows, vc_rows
     keep = layers[0] if keep_for_cpu else None
     del layers, ws, chunk
     torch.cuda.empty_cache()

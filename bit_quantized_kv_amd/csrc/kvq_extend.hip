@@ -116,13 +116,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     gsf[0] = p.gs[0];
     gsf[1] = p.gs[1];
   }
-  // NVFP4 prefix: the steps whose 32 keys all lie in the cached prefix (every
-  // row sees all of them: no mask) run in fp16 -- codes expanded as
-  // (e2m1 * 2^8) * (E4M3 * 2^-8), exact; the global scales, uniform over these
-  // steps, go to the score (K) and, once after the last of them, to the output
-  // accumulators (V); p in fp16 (11 bits) feeds a single PV MFMA.  The steps
-  // from the first one that reaches the chunk on take the bf16 path.
-  constexpr bool F16P = SRC == FMT_NVFP4;
+  // Paged prefix: the steps whose 32 keys all lie in the cached prefix (every
+  // row sees all of them: no mask) run in fp16, with p in fp16 (11 bits)
+  // feeding a single PV MFMA.  NVFP4 codes are expanded as
+  // (e2m1 * 2^8) * (E4M3 * 2^-8), exact, and the global scales, uniform over
+  // these steps, go to the score (K) and, once after the last of them, to the
+  // output accumulators (V).  INT4 codes are the integers q, exact, with the
+  // token scales staged per token as on the bf16 steps; the value scale rides
+  // on p, so the running max also bounds p * scale (below).  The steps from
+  // the first one that reaches the chunk on take the bf16 path.
+  constexpr bool F16P = PAGED;
   const int nsteps16 = F16P ? (int)min((int64_t)p.prefix_len / kExtStep, (int64_t)nsteps - 1) : 0;
 
   // the query row's MFMA operands: bf16 bits, or on the fp16 steps fp16 bits
@@ -162,13 +165,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
                                     (_Float16)ldexpf(as_f32(wq[c] & 0xFFFF0000u), kq)});
       qw[m] = (u32x4_t){wq[0], wq[1], wq[2], wq[3]};
     }
-    ck = gsf[0] * ldexpf(1.0f, -kq);
+    ck = (SRC == FMT_NVFP4 ? gsf[0] : 1.0f) * ldexpf(1.0f, -kq);
   }
   // scores stay unscaled (q.k, times the token's factor in the paged variant);
   // the running max is kept in the same units and p = 2^(s sm - m sm) is one
   // fma and one exp
   const float sm = p.sm_scale * kExtLog2e;
-  const float slack_raw = kExtSlack / sm;
+  const float slack_raw = kExtSlack / sm, inv_sm = 1.0f / sm;
 
   // ---- staging.  K, workspace variant: pass v (< KV16) of thread t loads
   // 16-byte segment kseg of row krow0 + v * KRP (a wavefront reads whole rows,
@@ -311,23 +314,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     stage(kreg, 0);
     stage(vreg, 1);
   };
-  // fp16 staging of an NVFP4 prefix step (every row of it in the prefix): per
+  // fp16 staging of a prefix step (every row of it in the prefix).  NVFP4: per
   // code word, four conversions at a 2^8 scale and four packed multiplies by
   // the block scale times 2^-8, exact (e2m1 * E4M3 has at most 6 significant
-  // bits and lies in [2^-10, 2688])
+  // bits and lies in [2^-10, 2688]).  INT4: byte k of the word and of the word
+  // shifted by 4 side by side put nibbles 2k and 2k + 1 in the low bits of the
+  // two halves, which land in the mantissa of 1024 with the sign bit flipped
+  // (q + 8), less 1032: q exactly, three instructions per pair; the token's
+  // scale is staged as on the bf16 steps.
   auto lstore16 = [&](int buf) {
     uint8_t* base = lds + buf * Lds::BUF;
+    float* fac = (float*)(base + Lds::KB + Lds::VB);
     auto stage = [&](u32x4_t(&reg)[KV16], int kv) {
       const u32x4_t raw = reg[0];
       const uint32_t sw = reg[1].x;
       const uint32_t cw[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int v = 0; v < KV16; v++) {
-        const uint32_t hb = e4m3_to_h_x2m8(sw >> (8 * (v / 2)));
-        const half2_t s2 = u32_as_h2(hb | (hb << 16));
-        reg[v] = (u32x4_t){h2_as_u32(e2m1x2_to_h2_x256<0>(cw[v]) * s2), h2_as_u32(e2m1x2_to_h2_x256<1>(cw[v]) * s2),
-                           h2_as_u32(e2m1x2_to_h2_x256<2>(cw[v]) * s2), h2_as_u32(e2m1x2_to_h2_x256<3>(cw[v]) * s2)};
+        if constexpr (SRC == FMT_NVFP4) {
+          const uint32_t hb = e4m3_to_h_x2m8(sw >> (8 * (v / 2)));
+          const half2_t s2 = u32_as_h2(hb | (hb << 16));
+          reg[v] = (u32x4_t){h2_as_u32(e2m1x2_to_h2_x256<0>(cw[v]) * s2), h2_as_u32(e2m1x2_to_h2_x256<1>(cw[v]) * s2),
+                             h2_as_u32(e2m1x2_to_h2_x256<2>(cw[v]) * s2), h2_as_u32(e2m1x2_to_h2_x256<3>(cw[v]) * s2)};
+        } else {
+          const uint32_t w = cw[v], w4 = w >> 4;
+          uint32_t o[4];
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            const uint32_t t = (byte_perm(w4, w, (uint32_t)k | 0x0C00u | ((uint32_t)(4 + k) << 16) | 0x0C000000u) &
+                                0x000F000Fu) ^ 0x64086408u;
+            o[k] = h2_as_u32(u32_as_h2(t) - (half2_t){(_Float16)1032.0f, (_Float16)1032.0f});
+          }
+          reg[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
+        }
       }
+      if (SRC == FMT_INT4 && kseg == 0) fac[kv * kExtStep + krow0] = as_f32(sw);
       uint8_t* rbase = base + kv * Lds::KB;
 #pragma unroll
       for (int v = 0; v < KV16; v++)
@@ -363,7 +384,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
                                                              __builtin_bit_cast(bf16x8_t, qw[m]), sacc[hh], 0, 0, 0);
       }
     }
-    float s[8], vf[8];
+    float s[8], vf[8], cand[8];
     const float* kfac = (const float*)(kb + Lds::KB + Lds::VB);
     const float* vfac = kfac + kExtStep;
     float cmax = -__builtin_inff();
@@ -374,13 +395,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     for (int e = 0; e < 8; e++) {
       const int tok = 16 * (e / 4) + 4 * j + (e % 4);
       float x = sacc[e / 4][e % 4];
-      if (F16) {
-        x *= ck;
-      } else if (PAGED) {
+      if (F16) x *= ck;
+      if (SRC == FMT_INT4 || (PAGED && !F16)) {
         x *= kfac[tok];
         vf[e] = vfac[tok];
       }
       s[e] = x;
+      // INT4 fp16 steps: the running max also bounds p * (value scale), so
+      // the product p' stays below 2^slack in fp16; the scale's binary
+      // exponent (scale < 2^e) is the bound, clamped so that tiny scales
+      // cannot push p out of fp32 range
+      if (F16 && SRC == FMT_INT4) cand[e] = x + (float)max(__builtin_amdgcn_frexp_exp(vf[e]), -64) * inv_sm;
     }
     // only steps that reach a row's causal limit need the mask (a
     // workgroup-uniform test, so the others skip it)
@@ -390,7 +415,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
         if (16 * (e / 4) + 4 * j + (e % 4) > last) s[e] = -__builtin_inff();
     }
 #pragma unroll
-    for (int e = 0; e < 8; e++) cmax = fmaxf(cmax, s[e]);
+    for (int e = 0; e < 8; e++) cmax = fmaxf(cmax, F16 && SRC == FMT_INT4 ? cand[e] : s[e]);
     // a row's max can only pass m_run + slack where one of its lanes' own
     // maxima does, so the wave-wide test needs no cross-lane reduction; the
     // row max (over the row's 4 lanes) is formed only when some row moves
@@ -411,6 +436,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], sm, -msm));
       l_run += p0 + p1;
       if constexpr (F16) {
+        if (SRC == FMT_INT4) {  // the token's value scale rides on its probability
+          p0 *= vf[e];
+          p1 *= vf[e + 1];
+        }
         hi[e / 2] = h2_as_u32((half2_t){(_Float16)p0, (_Float16)p1});
         lo[e / 2] = 0u;
       } else {
@@ -479,11 +508,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       advance(st);
     }
     if (nsteps16 > 0) {
-      // on to bf16: the query's bf16 operands again, and the value global
-      // scale of the prefix steps' sum applied once
+      // on to bf16: the query's bf16 operands again, and (NVFP4) the value
+      // global scale of the prefix steps' sum applied once
       load_q();
+      if (SRC == FMT_NVFP4) {
 #pragma unroll
-      for (int t = 0; t < VT; t++) oacc[t] *= gsf[1];
+        for (int t = 0; t < VT; t++) oacc[t] *= gsf[1];
+      }
     }
   }
   for (; st < nsteps; st++) {

@@ -35,6 +35,14 @@ def kv_rows(kind: str, seed: int, layer: int, n: int, H: int, D: int):
         return inputs.kv_lognormal_channels(seed, layer, n, H, D)
     if kind == "student_t":
         return inputs.kv_student_t(seed, layer, n, H, D)
+    if kind == "token_scaled":
+        # Student-t rows, each (token, head) row scaled by its own 2^u, u in
+        # [-30, 12]: per-token scales over 42 binades
+        k, v = inputs.kv_student_t(seed, layer, n, H, D)
+        rng = np.random.default_rng(seed * 1000 + layer)
+        k = k * np.exp2(rng.integers(-30, 13, size=(n, H, 1))).astype(np.float32)
+        v = v * np.exp2(rng.integers(-30, 13, size=(n, H, 1))).astype(np.float32)
+        return k, v
     raise ValueError(kind)
 
 

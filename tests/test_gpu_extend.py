@@ -168,3 +168,40 @@ def test_extend_paged_query_rows_of_any_magnitude():
     ref, _ = oracle.extend_attention(q.float().cpu().numpy(), k_all, v_all, Lp)
     s = max(1.0, float(np.abs(ref).max()))
     check_attention(out.cpu().numpy() / s, ref / s, np.ones(n, np.int32), label="paged, scaled query rows")
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_extend_paged_token_scales_over_many_binades(fmt):
+    """Prefix rows whose scales span 2^-30 .. 2^12 token by token: on the fp16
+    prefix steps the INT4 value scale rides on p in fp16, kept in range by
+    bounding the running max with the scale's exponent; NVFP4 block scales
+    saturate or vanish at the ends, which the oracle reproduces byte for byte."""
+    print(f"case: paged extend, token scales 2^-30 .. 2^12, fmt {fmt}", flush=True)
+    from gpu_cases import ATOL, Case
+    D, Hkv, G, P, Lp, n = 256, 2, 6, 16, 900, 40
+    c = Case(fmt, D, Hkv, G, P, [Lp], kind="token_scaled", in_dtype=torch.float32, seed=911)
+    assert np.array_equal(c.gpu_pool(), c.ref.data), "cache bytes differ from the oracle's"
+    kc, vc = inputs.kv_lognormal_channels(60, 0, n, Hkv, D)
+    kc_d, vc_d = bf16(kc).cuda(), bf16(vc).cuda()
+    q = bf16(inputs.query(60, 1, n, Hkv * G, D).reshape(n, Hkv * G, D)).cuda()
+    out = kvq.kvq_extend_attention_paged(c.cache, c.bt_dev[0].contiguous(), Lp, q, kc_d, vc_d,
+                                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kp, vp = _prefix_values(c, Lp)
+    k_all = np.concatenate([kp, kc_d.float().cpu().numpy()])
+    v_all = np.concatenate([vp, vc_d.float().cpu().numpy()])
+    ref, _ = oracle.extend_attention(q.float().cpu().numpy(), k_all, v_all, Lp)
+    s = max(1.0, float(np.abs(ref).max()))
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref)
+    assert err.max() <= ATOL * s, err.max()
+    # cosine where the output is not numerically zero: attention can settle on a
+    # prefix token whose value row quantized to zero (a 2^-30 row under NVFP4's
+    # E4M3 block scale), leaving outputs of ~1e-300 where a cosine means nothing
+    from gpu_cases import MIN_COS, cosine
+    norms = np.linalg.norm(ref, axis=-1)
+    rows = np.argwhere(norms >= 1e-6 * s)
+    assert len(rows) >= ref.shape[0] * ref.shape[1] // 2
+    for i, h in rows:
+        assert cosine(got[i, h], ref[i, h]) >= MIN_COS, (i, h)

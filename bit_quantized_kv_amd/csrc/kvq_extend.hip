@@ -26,13 +26,13 @@
 // Prefix codes are expanded to bf16 exactly while staged (NVFP4 e2m1 * e4m3;
 // INT4 q) and the remaining factor of each token (NVFP4: the global scale;
 // INT4: the token's scale; chunk tokens: 1) is staged per token and applied
-// to its score (K) and to its probability in the PV product (V).  For NVFP4
-// those factors are the layer's two global scales, so the steps whose keys
-// all lie in the prefix run in fp16 instead: codes expanded exactly to fp16
-// (one scaled conversion and one packed multiply per pair), q scaled per row
-// by a power of two into fp16's range, QK and PV on
-// v_mfma_f32_16x16x32_f16 with p in fp16 (one PV MFMA), the global scales
-// applied to the score and, once, to the output accumulators.
+// to its score (K) and to its probability in the PV product (V).  The steps
+// whose keys all lie in the prefix run in fp16 instead: codes expanded
+// exactly to fp16, q scaled per row by a power of two into fp16's range, QK
+// and PV on v_mfma_f32_16x16x32_f16 with p in fp16 (one PV MFMA).  NVFP4's
+// factors there are the layer's two global scales, applied to the score and,
+// once, to the output accumulators; INT4's value scale rides on p, kept in
+// fp16's range by a running max that bounds p * scale.
 #include <type_traits>
 
 #include "kvq_device.h"

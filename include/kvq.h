@@ -238,7 +238,11 @@ kvq_status kvq_extend_attention(const void* q, int64_t q_token_stride, int32_t n
  * prefill workspace).  The chunk's own K/V come as bf16 rows k_chunk, v_chunk
  * [chunk_len][chunk_token_stride] (head g at g * head_dim).  NVFP4 and INT4
  * caches (FP8, K8V4: KVQ_ERR_UNSUPPORTED); for a rotated cache the caller passes
- * rotated q and chunk rows and rotates the output back. */
+ * rotated q and chunk rows and rotates the output back.  Arithmetic: prefix keys
+ * and values enter at their exact dequantized value; 32-key steps wholly inside
+ * the prefix multiply in fp16 with each probability rounded to fp16 (relative
+ * error at most 2^-12), later steps in bf16 with each probability split into
+ * two bf16 terms; products are exact and accumulate in fp32. */
 kvq_status kvq_extend_attention_paged(const kvq_cache* cache, const int32_t* block_table_row, int32_t prefix_len,
                                       const void* q, int64_t q_token_stride, int32_t num_q_heads, const void* k_chunk,
                                       const void* v_chunk, int64_t chunk_token_stride, int32_t chunk_len,

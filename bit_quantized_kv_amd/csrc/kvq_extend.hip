@@ -231,30 +231,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     int off;
     return ld_global<int32_t>(p.pages + page_slot(t0, off));
   };
+  // a prefix row's staging registers, K (kv 0) or V (kv 1): the row's D/8
+  // elements from kseg * D/8 as D/16 code bytes, and D/128 E4M3 block scales
+  // (NVFP4) or the fp32 row scale (INT4), kept raw
+  auto load_paged_row = [&](u32x4_t(&reg)[KV16], int kv, int64_t t0, int pid) {
+    int off;
+    (void)page_slot(t0, off);
+    const uint8_t* sl = p.pool + ((int64_t)pid * p.num_kv_heads + g) * p.slab + kv * p.half;
+    const uint8_t* cp = sl + (int64_t)off * (D / 2) + kseg * (D / 16);
+    if (D == 256) {
+      reg[0] = ld_global<u32x4_t>(cp);
+    } else {
+      const u32x2_t w = ld_global<u32x2_t>(cp);
+      reg[0].x = w.x;
+      reg[0].y = w.y;
+    }
+    const uint8_t* sc = sl + p.scales_off;
+    if (SRC == FMT_NVFP4)
+      reg[1].x = D == 256 ? (uint32_t)ld_global<uint16_t>(sc + (int64_t)off * (D / 16) + 2 * kseg)
+                          : (uint32_t)ld_global<uint8_t>(sc + (int64_t)off * (D / 16) + kseg);
+    else
+      reg[1].x = ld_global<uint32_t>(sc + (int64_t)off * 4);
+  };
+  // the loads of a step whose rows all lie in the prefix: no branch between
+  // page and bf16 rows, so the loads land in their staging registers (a
+  // register copy after a branch would wait for the load it copies)
+  auto gload16 = [&](int step, int pid) {
+    const int64_t t0 = (int64_t)step * kExtStep;
+    load_paged_row(kreg, 0, t0, pid);
+    load_paged_row(vreg, 1, t0, pid);
+  };
   auto gload = [&](int step, int pid) {
     const int64_t t0 = (int64_t)step * kExtStep;
     // one row's staging registers: K (kv 0) or V (kv 1)
     auto rows = [&](u32x4_t(&reg)[KV16], int kv) {
       if (PAGED && t0 + krow0 < Lp) {
-        // the row's D/8 elements from kseg * D/8: D/16 code bytes, and D/128
-        // E4M3 block scales (NVFP4) or the fp32 row scale (INT4), kept raw
-        int off;
-        (void)page_slot(t0, off);
-        const uint8_t* sl = p.pool + ((int64_t)pid * p.num_kv_heads + g) * p.slab + kv * p.half;
-        const uint8_t* cp = sl + (int64_t)off * (D / 2) + kseg * (D / 16);
-        if (D == 256) {
-          reg[0] = ld_global<u32x4_t>(cp);
-        } else {
-          const u32x2_t w = ld_global<u32x2_t>(cp);
-          reg[0].x = w.x;
-          reg[0].y = w.y;
-        }
-        const uint8_t* sc = sl + p.scales_off;
-        if (SRC == FMT_NVFP4)
-          reg[1].x = D == 256 ? (uint32_t)ld_global<uint16_t>(sc + (int64_t)off * (D / 16) + 2 * kseg)
-                              : (uint32_t)ld_global<uint8_t>(sc + (int64_t)off * (D / 16) + kseg);
-        else
-          reg[1].x = ld_global<uint32_t>(sc + (int64_t)off * 4);
+        load_paged_row(reg, kv, t0, pid);
       } else {
         const __amdgpu_buffer_rsrc_t rs = rows_rsrc(kv ? p.v : p.k, t0);
 #pragma unroll
@@ -501,8 +513,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     }
     __syncthreads();
   };
+  // the same while step st + 2 is a prefix step too
+  auto advance16 = [&](int st) {
+    lstore16((st + 1) & 1);
+    gload16(st + 2, pid);
+    pid = page_id(st + 3);
+    __syncthreads();
+  };
   int st = 0;
   if constexpr (F16P) {
+    for (; st + 2 < nsteps16; st++) {
+      compute(std::true_type{}, st & 1, (int64_t)st * kExtStep);
+      advance16(st);
+    }
     for (; st < nsteps16; st++) {
       compute(std::true_type{}, st & 1, (int64_t)st * kExtStep);
       advance(st);

@@ -261,21 +261,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     load_paged_row(kreg, 0, t0, pid);
     load_paged_row(vreg, 1, t0, pid);
   };
+  // a bf16 row's staging registers (K: kv 0, V: kv 1)
+  auto load_bf16_row = [&](u32x4_t(&reg)[KV16], int kv, int64_t t0) {
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(kv ? p.v : p.k, t0);
+#pragma unroll
+    for (int v = 0; v < KV16; v++)
+      reg[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, kvo + (PAGED ? 16 * v : v * KRP * rowb), 0, 0);
+  };
   auto gload = [&](int step, int pid) {
     const int64_t t0 = (int64_t)step * kExtStep;
     // one row's staging registers: K (kv 0) or V (kv 1)
     auto rows = [&](u32x4_t(&reg)[KV16], int kv) {
-      if (PAGED && t0 + krow0 < Lp) {
+      if (PAGED && t0 + krow0 < Lp)
         load_paged_row(reg, kv, t0, pid);
-      } else {
-        const __amdgpu_buffer_rsrc_t rs = rows_rsrc(kv ? p.v : p.k, t0);
-#pragma unroll
-        for (int v = 0; v < KV16; v++)
-          reg[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, kvo + (PAGED ? 16 * v : v * KRP * rowb), 0, 0);
-      }
+      else
+        load_bf16_row(reg, kv, t0);
     };
     rows(kreg, 0);
     rows(vreg, 1);
+  };
+  // the loads of a step whose rows all lie in the chunk (paged variant): bf16
+  // rows only, no branch (as gload16 for the prefix)
+  auto gloadc = [&](int step) {
+    const int64_t t0 = (int64_t)step * kExtStep;
+    load_bf16_row(kreg, 0, t0);
+    load_bf16_row(vreg, 1, t0);
   };
   // bf16 pairs of 8 codes (element 0 low): NVFP4 e2m1 * block scale, exact;
   // INT4 the integers q, exact
@@ -540,9 +550,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       }
     }
   }
-  for (; st < nsteps; st++) {
+  // paged variant: from the step whose prefetch target lies wholly in the
+  // chunk on, the loads are gloadc's, issued on every step but the last two
+  // (a conditional load would again need a register merge)
+  const int st_chunk = PAGED ? (int)((Lp + kExtStep - 1) / kExtStep) : 0;  // first step with no prefix row
+  for (; st < nsteps && (!PAGED || st + 2 < st_chunk); st++) {
     compute(std::false_type{}, st & 1, (int64_t)st * kExtStep);
     advance(st);
+  }
+  if constexpr (PAGED) {
+    for (; st + 2 < nsteps; st++) {
+      compute(std::false_type{}, st & 1, (int64_t)st * kExtStep);
+      lstore((st + 1) & 1, (int64_t)(st + 1) * kExtStep);
+      gloadc(st + 2);
+      __syncthreads();
+    }
+    for (; st < nsteps; st++) {
+      compute(std::false_type{}, st & 1, (int64_t)st * kExtStep);
+      advance(st);
+    }
   }
 
   // ---- epilogue: each lane column is one query row

@@ -78,6 +78,10 @@ PAGED = [
     (2, 128, 3, 3, 16, 300, 17, (1.0, 1.0)),
     (1, 256, 2, 6, 16, 0, 50, (0.5, 0.5)),
     (1, 256, 2, 6, 16, 2000, 40, (0.015625, 0.03125)),
+    # page sizes that are not powers of two, prefixes over many pages ending mid-page
+    (2, 256, 2, 6, 1600, 5000, 40, (1.0, 1.0)),
+    (1, 256, 1, 6, 48, 1000, 37, (1.0, 1.0)),
+    (2, 128, 1, 4, 80, 3333, 20, (1.0, 1.0)),
 ]
 
 

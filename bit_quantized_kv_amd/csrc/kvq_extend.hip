@@ -183,6 +183,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   constexpr int KSEG = PAGED ? 8 : D / 8, KRP = 256 / KSEG;
   const int krow0 = PAGED ? (D == 256 ? ((tid >> 2) & 3) + 4 * (tid >> 5) : tid >> 3) : tid / KSEG;
   const int kseg = PAGED ? (D == 256 ? (tid & 3) + 4 * ((tid >> 4) & 1) : tid & 7) : tid % KSEG;
+  // bit position of this thread's first NVFP4 block-scale byte in the dword
+  // load_paged_row reads
+  const int nv_sshift = D == 256 ? 16 * (kseg & 1) : 8 * (kseg & 3);
   // row and first element of pass v
   auto krow_of = [&](int v) { return PAGED ? krow0 : krow0 + v * KRP; };
   auto kel_of = [&](int v) { return PAGED ? kseg * (D / 8) + 8 * v : 8 * kseg; };
@@ -247,19 +250,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       reg[0].y = w.y;
     }
     const uint8_t* sc = sl + p.scales_off;
+    // NVFP4: the aligned dword holding the row's scale bytes, shifted by
+    // nv_sshift where used (a narrower load's zero extension would be an
+    // instruction on the loaded value, and waiting for it a stall)
     if (SRC == FMT_NVFP4)
-      reg[1].x = D == 256 ? (uint32_t)ld_global<uint16_t>(sc + (int64_t)off * (D / 16) + 2 * kseg)
-                          : (uint32_t)ld_global<uint8_t>(sc + (int64_t)off * (D / 16) + kseg);
+      reg[1].x = ld_global<uint32_t>(sc + (int64_t)off * (D / 16) + ((D == 256 ? 2 * kseg : kseg) & ~3));
     else
       reg[1].x = ld_global<uint32_t>(sc + (int64_t)off * 4);
   };
   // the loads of a step whose rows all lie in the prefix: no branch between
   // page and bf16 rows, so the loads land in their staging registers (a
   // register copy after a branch would wait for the load it copies)
-  auto gload16 = [&](int step, int pid) {
+  auto gload16 = [&](u32x4_t(&kr)[KV16], u32x4_t(&vr)[KV16], int step, int pid) {
     const int64_t t0 = (int64_t)step * kExtStep;
-    load_paged_row(kreg, 0, t0, pid);
-    load_paged_row(vreg, 1, t0, pid);
+    load_paged_row(kr, 0, t0, pid);
+    load_paged_row(vr, 1, t0, pid);
   };
   // a bf16 row's staging registers (K: kv 0, V: kv 1)
   auto load_bf16_row = [&](u32x4_t(&reg)[KV16], int kv, int64_t t0) {
@@ -322,7 +327,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 #pragma unroll
           for (int v = 0; v < KV16; v++) {
             uint32_t o[4];
-            expand8(cw[v], SRC == FMT_NVFP4 ? e4m3_decode((sw >> (8 * (v / 2))) & 0xFFu) : 1.0f, o);
+            expand8(cw[v], SRC == FMT_NVFP4 ? e4m3_decode((sw >> (nv_sshift + 8 * (v / 2))) & 0xFFu) : 1.0f, o);
             reg[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
           }
         }
@@ -344,7 +349,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   // two halves, which land in the mantissa of 1024 with the sign bit flipped
   // (q + 8), less 1032: q exactly, three instructions per pair; the token's
   // scale is staged as on the bf16 steps.
-  auto lstore16 = [&](int buf) {
+  auto lstore16 = [&](u32x4_t(&kr)[KV16], u32x4_t(&vr)[KV16], int buf) {
     uint8_t* base = lds + buf * Lds::BUF;
     float* fac = (float*)(base + Lds::KB + Lds::VB);
     auto stage = [&](u32x4_t(&reg)[KV16], int kv) {
@@ -354,7 +359,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 #pragma unroll
       for (int v = 0; v < KV16; v++) {
         if constexpr (SRC == FMT_NVFP4) {
-          const uint32_t hb = e4m3_to_h_x2m8(sw >> (8 * (v / 2)));
+          const uint32_t hb = e4m3_to_h_x2m8(sw >> (nv_sshift + 8 * (v / 2)));
           const half2_t s2 = u32_as_h2(hb | (hb << 16));
           reg[v] = (u32x4_t){h2_as_u32(e2m1x2_to_h2_x256<0>(cw[v]) * s2), h2_as_u32(e2m1x2_to_h2_x256<1>(cw[v]) * s2),
                              h2_as_u32(e2m1x2_to_h2_x256<2>(cw[v]) * s2), h2_as_u32(e2m1x2_to_h2_x256<3>(cw[v]) * s2)};
@@ -376,8 +381,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       for (int v = 0; v < KV16; v++)
         *(u32x4_t*)(rbase + (krow_of(v) * Lds::KPD + kel_of(v) / 2) * 4) = reg[v];
     };
-    stage(kreg, 0);
-    stage(vreg, 1);
+    stage(kr, 0);
+    stage(vr, 1);
   };
 
   float4_t oacc[VT];
@@ -502,7 +507,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   int pid = page_id(0);
   gload(0, pid);
   if (F16P && nsteps16 > 0)
-    lstore16(0);
+    lstore16(kreg, vreg, 0);
   else
     lstore(0, 0);
   pid = page_id(1);
@@ -513,7 +518,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   auto advance = [&](int st) {
     if (st + 1 < nsteps) {
       if (F16P && st + 1 < nsteps16)
-        lstore16((st + 1) & 1);
+        lstore16(kreg, vreg, (st + 1) & 1);
       else
         lstore((st + 1) & 1, (int64_t)(st + 1) * kExtStep);
       if (st + 2 < nsteps) {
@@ -524,17 +529,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     __syncthreads();
   };
   // the same while step st + 2 is a prefix step too
-  auto advance16 = [&](int st) {
-    lstore16((st + 1) & 1);
-    gload16(st + 2, pid);
-    pid = page_id(st + 3);
-    __syncthreads();
-  };
+  // Prefix steps with two steps of loads in flight: a second staging set
+  // (kreg2, vreg2) alternates with the first, so the loads of step st + 3
+  // issued in step st are staged two steps later; each set's page entries are
+  // fetched a pair of steps ahead (pid_a, pid_b), so that waiting for them
+  // never waits for the other set's loads (the load counter is in order).
+  // Entering at st = 0: the first set holds step 1, the second step 2,
+  // pid_a the page of step 3 and pid_b that of step 4.
+  u32x4_t kreg2[KV16], vreg2[KV16];
   int st = 0;
   if constexpr (F16P) {
-    for (; st + 2 < nsteps16; st++) {
-      compute(std::true_type{}, st & 1, (int64_t)st * kExtStep);
-      advance16(st);
+    if (nsteps16 > 4) {
+      gload16(kreg2, vreg2, 2, pid);
+      int pid_a = page_id(3), pid_b = page_id(4);
+      for (; st + 4 < nsteps16; st += 2) {
+        compute(std::true_type{}, st & 1, (int64_t)st * kExtStep);
+        lstore16(kreg, vreg, (st + 1) & 1);
+        gload16(kreg, vreg, st + 3, pid_a);
+        pid_a = page_id(st + 5);
+        __syncthreads();
+        compute(std::true_type{}, (st + 1) & 1, (int64_t)(st + 1) * kExtStep);
+        lstore16(kreg2, vreg2, st & 1);
+        gload16(kreg2, vreg2, st + 4, pid_b);
+        pid_b = page_id(st + 6);
+        __syncthreads();
+      }
+      // back to one set: the first holds step st + 1; the page of step st + 2
+      // is looked up again (the second set's step st + 2 is reloaded)
+      pid = page_id(st + 2);
     }
     for (; st < nsteps16; st++) {
       compute(std::true_type{}, st & 1, (int64_t)st * kExtStep);

@@ -13,7 +13,8 @@
 // consecutive rows (16 per wavefront, the MFMA's column dimension) and walks
 // the keys its rows can see in 32-token steps.  Each step's K rows and
 // transposed V rows are staged once in LDS (double-buffered, the next step's
-// global loads in flight in registers) and read by all 4 wavefronts:
+// global loads in flight in registers -- two steps' on the paged variant's
+// prefix steps) and read by all 4 wavefronts:
 //   QK  S^T[token][row] = K[token][ch] Q^T[ch][row] on v_mfma_f32_16x16x32_bf16
 //       (bf16 K and q exactly, fp32 accumulation);
 //   online softmax in base 2 per row, lazily rescaled as in decode;

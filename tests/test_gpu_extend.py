@@ -82,6 +82,8 @@ PAGED = [
     (2, 256, 2, 6, 1600, 5000, 40, (1.0, 1.0)),
     (1, 256, 1, 6, 48, 1000, 37, (1.0, 1.0)),
     (2, 128, 1, 4, 80, 3333, 20, (1.0, 1.0)),
+    # head dim 128 over many fp16 prefix steps (the two-deep loop)
+    (1, 128, 2, 4, 16, 700, 50, (0.5, 2.0)),
 ]
 
 

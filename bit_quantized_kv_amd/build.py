@@ -48,6 +48,22 @@ def _compile(src: str) -> str:
     return obj
 
 
+CONVCHECK_SRC = os.path.join(ROOT, "tests", "conv_check.hip")
+CONVCHECK_LIB = os.path.join(ROOT, "tests", "libkvq_convcheck.so")
+
+
+def build_convcheck() -> str:
+    """The test suite's exhaustive conversion checks (tests/conv_check.hip), built
+    with the library's device flags so the instructions run in the same modes."""
+    tmp = CONVCHECK_LIB + ".tmp"
+    cmd = [_hipcc(), "-x", "hip", *COMMON, "-shared", CONVCHECK_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for conv_check.hip:\n{r.stderr}")
+    os.replace(tmp, CONVCHECK_LIB)
+    return CONVCHECK_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:

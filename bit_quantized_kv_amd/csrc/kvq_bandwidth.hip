@@ -1,5 +1,6 @@
-// kvq_bandwidth.hip -- a plain streaming-read kernel, the practical HBM read
-// ceiling that the decode kernel's bandwidth is compared with.
+// kvq_bandwidth.hip -- plain streaming read, write and copy kernels: the
+// practical HBM ceilings that the decode kernel (read), the bulk store and
+// the prefix dequantization (read + write, write-dominated) are compared with.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -25,6 +26,37 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* __restr
     acc ^= __builtin_amdgcn_raw_buffer_load_b128(r, (int)threadIdx.x * 16, 0, kLoadStream);
   }
   if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[0] = 1u;
+}
+
+// Grid-stride write of n16 16-byte vectors (the value's 16 bytes), one vector
+// per lane per iteration: the write ceiling.
+__global__ __launch_bounds__(256) void stream_write_kernel(uint8_t* __restrict__ a, int64_t n16, u32x4_t value) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride)
+    __builtin_nontemporal_store(value, (__attribute__((address_space(1))) u32x4_t*)(a + i * 16));
+}
+
+// Grid-stride copy of n16 16-byte vectors (non-temporal loads as decode's,
+// non-temporal stores): the read + write ceiling of a streaming transform.
+__global__ __launch_bounds__(256) void stream_copy_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                          int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) {
+    const u32x4_t v = ld_stream<u32x4_t>(src + i * 16);
+    __builtin_nontemporal_store(v, (__attribute__((address_space(1))) u32x4_t*)(dst + i * 16));
+  }
+}
+
+hipError_t launch_stream_write(void* buf, int64_t bytes, uint32_t value, int workgroups, hipStream_t stream) {
+  hipLaunchKernelGGL(stream_write_kernel, dim3(workgroups), dim3(256), 0, stream, (uint8_t*)buf, bytes / 16,
+                     (u32x4_t){value, value, value, value});
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int workgroups, hipStream_t stream) {
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(workgroups), dim3(256), 0, stream, (const uint8_t*)src, (uint8_t*)dst,
+                     bytes / 16);
+  return hipGetLastError();
 }
 
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t stream) {

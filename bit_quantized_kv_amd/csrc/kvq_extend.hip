@@ -34,6 +34,7 @@
 // factors there are the layer's two global scales, applied to the score and,
 // once, to the output accumulators; INT4's value scale rides on p, kept in
 // fp16's range by a running max that bounds p * scale.
+#include <mutex>
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -45,6 +46,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kExtRows = 64;   // query rows per workgroup, 16 per wavefront
 constexpr int kExtStep = 32;   // key tokens per step
+constexpr int kExtFlush = 32;  // steps an MFMA accumulator runs before it is added into the total
 static constexpr float kExtLog2e = 1.4426950408889634f;
 static constexpr float kExtLn2 = 0.6931471805599453f;
 static constexpr float kExtSlack = 8.0f;
@@ -390,6 +392,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
 #pragma unroll
   for (int t = 0; t < VT; t++) oacc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -__builtin_inff(), l_run = 0.0f;
+  // Two-level accumulation.  The MFMA accumulation aligns each product to
+  // the accumulator's exponent and keeps only about 3 bits below its ulp
+  // (measured on gfx950: with C = 1.0, 32 products of 2^-27 add nothing), and
+  // an fp32 sum of many small terms into a large one loses every term below
+  // half its ulp; over the tens of thousands of steps of a long prefix both
+  // drop the small late contributions with a bias.  So the running sums
+  // restart from zero every kExtFlush steps and are added into totals on VALU
+  // (round to nearest): l_run into l_tot always, oacc into otot in the
+  // workspace variant (the paged variant has no registers to spare for it).
+  constexpr bool TWO_LEVEL = !PAGED;
+  float4_t otot[TWO_LEVEL ? VT : 1];
+#pragma unroll
+  for (int t = 0; t < (TWO_LEVEL ? VT : 1); t++) otot[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  float l_tot = 0.0f;
+  auto flush = [&]() {
+    l_tot += l_run;
+    l_run = 0.0f;
+    if constexpr (TWO_LEVEL) {
+#pragma unroll
+      for (int t = 0; t < VT; t++) {
+        otot[t] += oacc[t];
+        oacc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+  };
 
   // one step: F16 (a std::bool_constant) selects the fp16 prefix form
   auto compute = [&](auto f16_tag, int buf, int64_t t0) {
@@ -453,8 +480,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sm);
       m_run = m_new;
       l_run *= alpha;
+      l_tot *= alpha;
 #pragma unroll
       for (int t = 0; t < VT; t++) oacc[t] *= alpha;
+      if constexpr (TWO_LEVEL) {
+#pragma unroll
+        for (int t = 0; t < VT; t++) otot[t] *= alpha;
+      }
     }
     const float msm = m_run * sm;
     uint32_t hi[4], lo[4];
@@ -550,6 +582,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
         pid_a = page_id(st + 5);
         __syncthreads();
         compute(std::true_type{}, (st + 1) & 1, (int64_t)(st + 1) * kExtStep);
+        if ((st + 2) % kExtFlush == 0) flush();  // st is even and kExtFlush a multiple of 2
         lstore16(kreg2, vreg2, st & 1);
         gload16(kreg2, vreg2, st + 4, pid_b);
         pid_b = page_id(st + 6);
@@ -561,6 +594,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     }
     for (; st < nsteps16; st++) {
       compute(std::true_type{}, st & 1, (int64_t)st * kExtStep);
+      if ((st + 1) % kExtFlush == 0) flush();
       advance(st);
     }
     if (nsteps16 > 0) {
@@ -579,22 +613,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   const int st_chunk = PAGED ? (int)((Lp + kExtStep - 1) / kExtStep) : 0;  // first step with no prefix row
   for (; st < nsteps && (!PAGED || st + 2 < st_chunk); st++) {
     compute(std::false_type{}, st & 1, (int64_t)st * kExtStep);
+    if ((st + 1) % kExtFlush == 0) flush();
     advance(st);
   }
   if constexpr (PAGED) {
     for (; st + 2 < nsteps; st++) {
       compute(std::false_type{}, st & 1, (int64_t)st * kExtStep);
+      if ((st + 1) % kExtFlush == 0) flush();
       lstore((st + 1) & 1, (int64_t)(st + 1) * kExtStep);
       gloadc(st + 2);
       __syncthreads();
     }
     for (; st < nsteps; st++) {
       compute(std::false_type{}, st & 1, (int64_t)st * kExtStep);
+      if ((st + 1) % kExtFlush == 0) flush();
       advance(st);
     }
   }
 
   // ---- epilogue: each lane column is one query row
+  if constexpr (TWO_LEVEL) {
+#pragma unroll
+    for (int t = 0; t < VT; t++) oacc[t] += otot[t];
+  }
+  l_run += l_tot;
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (!row_ok) return;
@@ -614,14 +656,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     p.lse[(int64_t)irow * p.lse_stride + h] = l_run > 0.0f ? (m_run * sm + log2f(l_run)) * kExtLn2 : -__builtin_inff();
 }
 
+// The double-buffered staging (74 KB at head dim 256) is above HIP's default
+// 64 KB dynamic-LDS limit per workgroup (gfx950 has 160 KB per CU), so each
+// instantiation raises its limit -- once per device, on its first launch
+// there, not on every launch (a host call that a captured graph would
+// otherwise repeat).  A failure is kept and returned by every later launch.
+constexpr int kExtMaxDevices = 64;
+
+template <int D, int SRC>
+static hipError_t extend_lds_limit() {
+  static std::once_flag once[kExtMaxDevices];
+  static hipError_t result[kExtMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kExtMaxDevices) {
+    (void)hipGetLastError();
+    return hipFuncSetAttribute((const void*)extend_kernel<D, SRC>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               ExtLds<D>::TOTAL);
+  }
+  std::call_once(once[dev], [dev] {
+    result[dev] = hipFuncSetAttribute((const void*)extend_kernel<D, SRC>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, ExtLds<D>::TOTAL);
+  });
+  return result[dev];
+}
+
 template <int D, int SRC>
 static hipError_t launch_extend_t(const ExtendParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.chunk_len * p.group;
   const dim3 grid((unsigned)((rows + kExtRows - 1) / kExtRows), (unsigned)p.num_kv_heads), block(256);
-  // the double-buffered staging (74 KB at head dim 256) is above HIP's default
-  // 64 KB dynamic-LDS limit per workgroup; gfx950 has 160 KB per CU
-  const hipError_t e = hipFuncSetAttribute((const void*)extend_kernel<D, SRC>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, ExtLds<D>::TOTAL);
+  const hipError_t e = extend_lds_limit<D, SRC>();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((extend_kernel<D, SRC>), grid, block, ExtLds<D>::TOTAL, stream, p);
   return hipGetLastError();

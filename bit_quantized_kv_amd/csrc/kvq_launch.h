@@ -84,5 +84,7 @@ hipError_t launch_hadamard(const RotateParams& p, int head_dim, int in_bf16, int
 hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream_t stream);
 hipError_t launch_extend(const ExtendParams& p, int head_dim, int src_fmt, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
+hipError_t launch_stream_write(void* buf, int64_t bytes, uint32_t value, int workgroups, hipStream_t stream);
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int workgroups, hipStream_t stream);
 
 }  // namespace kvq

@@ -63,6 +63,8 @@ def lib():
         "kvq_decode_attention": (i32, [C, P, i32, P, i32, P, i32, i32, f32, i32, P, i32, P, P, sz, P]),
         "kvq_dequant_prefix": (i32, [C, P, i32, P, P, i64, P]),
         "kvq_stream_read": (i32, [P, sz, P, i32, P]),
+        "kvq_stream_write": (i32, [P, sz, ctypes.c_uint32, i32, P]),
+        "kvq_stream_copy": (i32, [P, P, sz, i32, P]),
         "kvq_calibrate_amax": (i32, [C, P, P, i32, i64, i32, P, P]),
         "kvq_calibrate_global_scale": (i32, [C, P, P]),
         "kvq_hadamard_rotate": (i32, [P, i32, i64, P, i32, i64, i32, i32, P]),
@@ -194,6 +196,23 @@ def kvq_stream_read(buf: torch.Tensor, sink: torch.Tensor, num_workgroups: int =
     assert buf.is_contiguous() and sink.dtype in (torch.int32, torch.uint32) and sink.numel() >= 1
     nbytes = buf.numel() * buf.element_size() // 16 * 16
     _check("kvq_stream_read", lib().kvq_stream_read(_ptr(buf), nbytes, _ptr(sink), int(num_workgroups),
+                                                    _stream(stream)))
+
+
+def kvq_stream_write(buf: torch.Tensor, value: int = 0, num_workgroups: int = 0, stream=None):
+    """Plain streaming write over a contiguous device tensor (bandwidth reference)."""
+    assert buf.is_contiguous()
+    nbytes = buf.numel() * buf.element_size() // 16 * 16
+    _check("kvq_stream_write", lib().kvq_stream_write(_ptr(buf), nbytes, int(value) & 0xFFFFFFFF,
+                                                      int(num_workgroups), _stream(stream)))
+
+
+def kvq_stream_copy(src: torch.Tensor, dst: torch.Tensor, num_workgroups: int = 0, stream=None):
+    """Plain streaming copy between contiguous device tensors of equal size (bandwidth reference)."""
+    assert src.is_contiguous() and dst.is_contiguous()
+    nbytes = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() == nbytes
+    _check("kvq_stream_copy", lib().kvq_stream_copy(_ptr(src), _ptr(dst), nbytes // 16 * 16, int(num_workgroups),
                                                     _stream(stream)))
 
 

@@ -58,7 +58,8 @@
  *
  * Conventions
  *   - The caller owns all memory.  The library allocates and frees nothing and
- *     keeps no state between calls.
+ *     keeps no state between calls beyond per-device constants it looks up
+ *     once (compute-unit count, kernel attributes).
  *   - All work is enqueued on the caller's HIP stream (`stream`, a
  *     hipStream_t; NULL = the default stream) and is asynchronous.  The calls
  *     record nothing but kernel launches (no allocation, copy or memset), so
@@ -283,6 +284,15 @@ kvq_status kvq_hadamard_rotate(const void* in, int32_t in_dtype, int64_t in_row_
  * is).  buf 16-byte aligned, bytes a multiple of 16; num_workgroups <= 0 picks
  * 2048 (8 per CU).  Asynchronous on `stream`. */
 kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t num_workgroups, void* stream);
+
+/* Measurement aids, likewise: a plain streaming write of `bytes` bytes (every
+ * 32-bit word set to `value`) and a plain streaming copy of `bytes` bytes from
+ * src to dst (non-overlapping) -- the write and read + write ceilings against
+ * which the bulk store and the prefix dequantization are judged.  Pointers
+ * 16-byte aligned, bytes a multiple of 16; num_workgroups <= 0 picks 2048.
+ * Asynchronous on `stream`. */
+kvq_status kvq_stream_write(void* buf, size_t bytes, uint32_t value, int32_t num_workgroups, void* stream);
+kvq_status kvq_stream_copy(const void* src, void* dst, size_t bytes, int32_t num_workgroups, void* stream);
 
 /* Static description of a status code. */
 const char* kvq_status_string(int32_t status);

@@ -70,6 +70,8 @@ def _load():
         "kvqo_quantize_store": (None, [i32, P, i32, i32, i32, P, P, P, i32, P, i32]),
         "kvqo_hadamard_row": (None, [P, i32]),
         "kvqo_extend_attention": (None, [P, i64, i32, P, P, i64, i32, i32, i64, i64, f64, P, P]),
+        "kvqo_extend_attention_paged": (None, [i32, P, i32, i32, i32, P, P, i64, P, i64, i32, P, i64, P, P, i64,
+                                               f64, P, P, P]),
         "kvqo_decode_attention": (None, [i32, P, i32, i32, i32, P, P, i32, P, i32, P, i32, f64, i64, P, P]),
         "kvqo_dequant_prefix": (None, [i32, P, i32, i32, i32, P, P, i64, P, P, i64]),
         "kvqo_num_threads": (i32, []),
@@ -246,6 +248,35 @@ class Pool:
                                       _ptr(q), Hq, _ptr(bt), bt.shape[1], _ptr(sl), B, float(sm_scale),
                                       int(split_tokens), _ptr(out), _ptr(lse))
         return out, lse
+
+    def extend_attention(self, q, pages, prefix_len: int, k_chunk, v_chunk, q_pos=None,
+                         sm_scale: float | None = None, want_abs: bool = False):
+        """Extend attention over [this pool's cached prefix | bf16 chunk rows]
+        with the prefix at its exact dequantized value (kvqo_extend_attention_paged).
+        q: [n_q][Hq][D]; pages: the sequence's page list; k_chunk, v_chunk:
+        [chunk rows][Hkv][D] (bf16 values widened to fp32); q_pos: the sequence
+        position of each query row (default prefix_len + row).  Returns (out
+        fp64 [n_q][Hq][D], lse fp64 [n_q][Hq]) and, with want_abs, the
+        softmax-weighted mean of |v| per output element as a third array."""
+        q, pages = _f32(q), _i32(pages)
+        kc, vc = _f32(k_chunk), _f32(v_chunk)
+        n, Hq, D = q.shape
+        Hkv = self.num_kv_heads
+        assert D == self.head_dim and Hq % Hkv == 0 and kc.shape == vc.shape and kc.shape[1:] == (Hkv, D)
+        pos = np.arange(prefix_len, prefix_len + n, dtype=np.int64) if q_pos is None else \
+            np.ascontiguousarray(np.asarray(q_pos, dtype=np.int64))
+        assert pos.shape == (n,) and np.all(pos >= prefix_len) and np.all(pos < prefix_len + kc.shape[0])
+        assert pages.shape[0] * self.page_size >= prefix_len
+        if sm_scale is None or sm_scale <= 0:
+            sm_scale = 1.0 / np.sqrt(D)
+        out = np.zeros((n, Hq, D), np.float64)
+        lse = np.zeros((n, Hq), np.float64)
+        oabs = np.zeros((n, Hq, D), np.float64) if want_abs else None
+        _load().kvqo_extend_attention_paged(self.fmt, _ptr(self.data), self.page_size, Hkv, D, _ptr(self.gs),
+                                            _ptr(pages), int(prefix_len), _ptr(q), Hq * D, Hq, _ptr(pos), n,
+                                            _ptr(kc), _ptr(vc), Hkv * D, float(sm_scale), _ptr(out), _ptr(lse),
+                                            _ptr(oabs) if want_abs else None)
+        return (out, lse, oabs) if want_abs else (out, lse)
 
     def dequant_prefix(self, pages, prefix_len: int, out_token_stride: int | None = None):
         """Returns (k_out, v_out) as uint16 bf16 bit patterns [prefix_len][Hkv][D]

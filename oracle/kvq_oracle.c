@@ -570,6 +570,99 @@ void kvqo_extend_attention(const float* q, int64_t q_stride, int Hq, const float
   }
 }
 
+/* Extend attention over [cached 4-bit prefix | bf16 chunk] without a
+ * workspace (the fused form of the same Figure 2 extend step; the pages leave
+ * that form open).  Reading: the keys and values are those the workspace
+ * would hold, except that the prefix enters at its exact dequantized value
+ * (e2m1 * e4m3 * gs, q * s) in fp64 rather than rounded to bf16 -- identical
+ * at gs = 1 for NVFP4.  Cache tokens t < prefix_len come from the pool
+ * (page list `pages`, read_token), tokens t >= prefix_len from chunk row
+ * t - prefix_len of k_chunk / v_chunk ([chunk rows][chunk_stride], head g at
+ * g * D, bf16 values widened to fp32).  Query row j of q ([n_q][q_stride],
+ * head h at h * D) sits at sequence position q_pos[j] >= prefix_len and
+ * attends causally to keys 0 .. q_pos[j], query head h reading KV head h / G.
+ * Outputs per (j, h): out [n_q][Hq][D], lse [n_q][Hq] (natural log) and, when
+ * out_abs is not NULL, the softmax-weighted mean of |v| per channel,
+ * sum_t w_t |v_t,c| (the scale of the error that rounding each weight to a
+ * fixed relative precision can cause). */
+void kvqo_extend_attention_paged(int fmt, const uint8_t* pool, int P, int Hkv, int D, const float* gs,
+                                 const int32_t* pages, int64_t prefix_len, const float* q, int64_t q_stride, int Hq,
+                                 const int64_t* q_pos, int64_t n_q, const float* k_chunk, const float* v_chunk,
+                                 int64_t chunk_stride, double sm_scale, double* out, double* lse, double* out_abs) {
+  const int G = Hq / Hkv;
+  /* one (query row, KV head) per iteration: each key and value row is read
+   * once and used by the G query heads of the group */
+#pragma omp parallel for schedule(dynamic) collapse(2)
+  for (int64_t j = 0; j < n_q; j++) {
+    for (int g = 0; g < Hkv; g++) {
+      const int64_t nk = q_pos[j] + 1;
+      double* s = (double*)malloc(sizeof(double) * (size_t)nk * G);  /* [G][nk] */
+      double* row = (double*)malloc(sizeof(double) * (size_t)D);
+      double* m = (double*)malloc(sizeof(double) * G);
+      double* l = (double*)malloc(sizeof(double) * G);
+      for (int e = 0; e < G; e++) m[e] = -INFINITY;
+      for (int64_t t = 0; t < nk; t++) {
+        if (t < prefix_len) {
+          read_token(pool, fmt, P, Hkv, D, gs, pages, t, g, 0, row);
+        } else {
+          const float* kt = k_chunk + (t - prefix_len) * chunk_stride + (int64_t)g * D;
+          for (int c = 0; c < D; c++) row[c] = (double)kt[c];
+        }
+        for (int e = 0; e < G; e++) {
+          const float* qh = q + j * q_stride + (int64_t)(g * G + e) * D;
+          double dot = 0.0;
+          for (int c = 0; c < D; c++) dot += (double)qh[c] * row[c];
+          s[(size_t)e * nk + t] = dot * sm_scale;
+          if (s[(size_t)e * nk + t] > m[e]) m[e] = s[(size_t)e * nk + t];
+        }
+      }
+      for (int e = 0; e < G; e++) {
+        const int h = g * G + e;
+        double* o = out + ((size_t)j * Hq + h) * D;
+        double* oa = out_abs ? out_abs + ((size_t)j * Hq + h) * D : NULL;
+        for (int c = 0; c < D; c++) {
+          o[c] = 0.0;
+          if (oa) oa[c] = 0.0;
+        }
+        l[e] = 0.0;
+      }
+      for (int64_t t = 0; t < nk; t++) {
+        if (t < prefix_len) {
+          read_token(pool, fmt, P, Hkv, D, gs, pages, t, g, 1, row);
+        } else {
+          const float* vt = v_chunk + (t - prefix_len) * chunk_stride + (int64_t)g * D;
+          for (int c = 0; c < D; c++) row[c] = (double)vt[c];
+        }
+        for (int e = 0; e < G; e++) {
+          const int h = g * G + e;
+          const double p = exp(s[(size_t)e * nk + t] - m[e]);
+          l[e] += p;
+          double* o = out + ((size_t)j * Hq + h) * D;
+          for (int c = 0; c < D; c++) o[c] += p * row[c];
+          if (out_abs) {
+            double* oa = out_abs + ((size_t)j * Hq + h) * D;
+            for (int c = 0; c < D; c++) oa[c] += p * fabs(row[c]);
+          }
+        }
+      }
+      for (int e = 0; e < G; e++) {
+        const int h = g * G + e;
+        double* o = out + ((size_t)j * Hq + h) * D;
+        for (int c = 0; c < D; c++) o[c] /= l[e];
+        if (out_abs) {
+          double* oa = out_abs + ((size_t)j * Hq + h) * D;
+          for (int c = 0; c < D; c++) oa[c] /= l[e];
+        }
+        lse[(size_t)j * Hq + h] = m[e] + log(l[e]);
+      }
+      free(s);
+      free(row);
+      free(m);
+      free(l);
+    }
+  }
+}
+
 /* Global-scale calibration ("SGLang's 4-bit KV cache ...", section
  * '"Near-lossless" is narrower than it sounds': the measured NVFP4 runs
  * without its per-tensor FP32 scale and calibration is listed as ongoing

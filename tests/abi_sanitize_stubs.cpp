@@ -1,0 +1,49 @@
+// abi_sanitize_stubs.cpp -- host stand-ins for everything kvq_api.cpp calls
+// below the C ABI (the kernel launchers and the three HIP runtime queries),
+// so that the argument validation can be built for the host alone with
+// AddressSanitizer and UndefinedBehaviorSanitizer and run without a GPU
+// (test infrastructure: tests/test_abi_sanitized.py).
+// Each launcher records which kernel family was asked for; nothing runs.
+#include <hip/hip_runtime.h>
+
+#include "kvq_launch.h"
+
+int g_launch_count = 0;
+int g_last_launch = 0;  // 1 store, 2 dequant, 3 amax, 4 global scale, 5 hadamard, 6 decode, 7 extend, 8 read,
+                        // 9 write, 10 copy
+
+namespace {
+hipError_t record(int kind) {
+  g_launch_count++;
+  g_last_launch = kind;
+  return hipSuccess;
+}
+}  // namespace
+
+namespace kvq {
+hipError_t launch_quantize_store(const StoreParams&, int, int, int, hipStream_t) { return record(1); }
+hipError_t launch_dequant_prefix(const DequantParams&, int, int, hipStream_t) { return record(2); }
+hipError_t launch_calibrate_amax(const StoreParams&, int, int, float*, hipStream_t) { return record(3); }
+hipError_t launch_global_scale(const float*, float*, hipStream_t) { return record(4); }
+hipError_t launch_hadamard(const RotateParams&, int, int, int, hipStream_t) { return record(5); }
+hipError_t launch_decode(const DecodeParams& p, int, int, hipStream_t) {
+  // the partials must lie inside the workspace the entry point was given
+  return p.part_o != nullptr && p.part_ml != nullptr ? record(6) : hipErrorInvalidValue;
+}
+hipError_t launch_extend(const ExtendParams&, int, int, hipStream_t) { return record(7); }
+hipError_t launch_stream_read(const void*, int64_t, uint32_t*, int, hipStream_t) { return record(8); }
+hipError_t launch_stream_write(void*, int64_t, uint32_t, int, hipStream_t) { return record(9); }
+hipError_t launch_stream_copy(const void*, void*, int64_t, int, hipStream_t) { return record(10); }
+}  // namespace kvq
+
+extern "C" {
+hipError_t hipGetDevice(int* dev) {
+  *dev = 0;
+  return hipSuccess;
+}
+hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t, int) {
+  *value = 256;  // MI355X compute units
+  return hipSuccess;
+}
+hipError_t hipGetLastError(void) { return hipSuccess; }
+}

@@ -11,21 +11,66 @@ import torch
 import oracle
 from bit_quantized_kv_amd import inputs, kvq
 
-# Attention tolerance.  The oracle attends in fp64 over the exactly
-# dequantized cache; the kernel computes scores in fp32 from exact fp16 K,
-# rounds probabilities to fp16 for the PV product and accumulates in fp32.
-# fp32 output: |gpu - oracle| <= 2e-3 everywhere.  bf16 output adds the
-# unavoidable output rounding: |gpu - oracle| <= 2e-3 + half a bf16 ulp of
-# the oracle value.
+# Attention tolerance (one bar per path; see the derivations below).
+# The oracle attends in fp64 over the exactly dequantized cache.
+#  - fp32 output: |gpu - oracle| <= ATOL = 2e-3 everywhere.
+#  - bf16 output (the reading of "max-abs-error 2e-3 with bf16 out"): the
+#    output rounding alone is up to half a bf16 ulp (3.9e-3 for 1 <= |o| < 2),
+#    so where |oracle| < 0.5 (half an ulp is below 1e-3 there) every element
+#    must lie within 2e-3 of the oracle, and where |oracle| >= 0.5 within one
+#    bf16 ulp of bf16_rne(oracle) and within 2e-3 plus half an ulp of the
+#    oracle.  (Below 0.5 an output that results from cancellation can be a few
+#    of its own tiny ulps away from the oracle at an absolute error of 1e-7,
+#    so the ulp count is not the measure there.)
+#  - paths that round each softmax weight to fp16 before the PV product (the
+#    fused extend's steps wholly inside the cached prefix): each weight then
+#    carries a relative error of at most 2^-11, which moves an output element
+#    by at most 2^-11 * sum_t w_t |v_t,c| -- the softmax-weighted mean of |v|,
+#    computed by the oracle -- so the bar there is ATOL + 2^-11 * that mean
+#    (plus the bf16 output rounding for bf16 output).
+# cosine to the oracle >= MIN_COS per (sequence, head); lse within LSE_ATOL.
 ATOL = 2e-3
 LSE_ATOL = 1e-3
 MIN_COS = 0.9995
+F16_WEIGHT_REL = 2.0 ** -11
 
 
 def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
     ax = np.abs(x)
     e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
     return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
+
+
+def bf16_rne(x: np.ndarray) -> np.ndarray:
+    """Round to bf16 (nearest even, torch's cast) and widen back to fp64."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float64)).to(torch.bfloat16).double().numpy()
+
+
+def check_values(out, ref, bf16=False, extra=None, label=""):
+    """The element-wise bar above; extra (same shape as ref, or None) is the
+    derived fp16-weight term.  Returns (max |gpu - oracle|, largest error / bar)."""
+    out = np.asarray(out, np.float64)
+    assert np.all(np.isfinite(out)), f"{label}: non-finite output"
+    err = np.abs(out - ref)
+    tol = np.full(ref.shape, ATOL)
+    if extra is not None:
+        tol = tol + extra
+    if bf16:
+        tol = tol + np.where(np.abs(ref) < 0.5, 0.0, bf16_half_ulp(ref))
+        if extra is None:
+            r = bf16_rne(ref)
+            ulp = 2.0 * bf16_half_ulp(r)
+            off = (np.abs(ref) >= 0.5) & (np.abs(out - r) > ulp)
+            assert not off.any(), (f"{label}: {off.sum()} bf16 elements more than one ulp from bf16_rne(oracle), "
+                                   f"first at {np.argwhere(off)[0].tolist()}")
+    bad = err > tol
+    assert not bad.any(), (f"{label}: {bad.sum()} elements out of tolerance, max err {err.max():.3g} "
+                           f"at {np.unravel_index(err.argmax(), err.shape)} (bar there "
+                           f"{tol.ravel()[err.argmax()]:.3g})")
+    use = float((err / tol).max()) if err.size else 0.0
+    print(f"  {label}: max |err| {err.max() if err.size else 0.0:.3g}, max |o| "
+          f"{np.abs(ref).max() if ref.size else 0.0:.3g}, largest err / bar {use:.3f}", flush=True)
+    return float(err.max()) if err.size else 0.0, use
 
 
 def kv_rows(kind: str, seed: int, layer: int, n: int, H: int, D: int):
@@ -35,13 +80,16 @@ def kv_rows(kind: str, seed: int, layer: int, n: int, H: int, D: int):
         return inputs.kv_lognormal_channels(seed, layer, n, H, D)
     if kind == "student_t":
         return inputs.kv_student_t(seed, layer, n, H, D)
-    if kind == "token_scaled":
-        # Student-t rows, each (token, head) row scaled by its own 2^u, u in
-        # [-30, 12]: per-token scales over 42 binades
+    if kind in ("token_scaled", "token_scaled_o1"):
+        # Student-t rows, each (token, head) row scaled by its own 2^u: u in
+        # [-30, 12] (per-token scales over 42 binades), or u in [-30, 3] (33
+        # binades with outputs of order 1 to 10, where an absolute bar is
+        # meaningful)
+        hi = 13 if kind == "token_scaled" else 4
         k, v = inputs.kv_student_t(seed, layer, n, H, D)
         rng = np.random.default_rng(seed * 1000 + layer)
-        k = k * np.exp2(rng.integers(-30, 13, size=(n, H, 1))).astype(np.float32)
-        v = v * np.exp2(rng.integers(-30, 13, size=(n, H, 1))).astype(np.float32)
+        k = k * np.exp2(rng.integers(-30, hi, size=(n, H, 1))).astype(np.float32)
+        v = v * np.exp2(rng.integers(-30, hi, size=(n, H, 1))).astype(np.float32)
         return k, v
     raise ValueError(kind)
 
@@ -122,14 +170,9 @@ def cosine(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.dot(a.ravel(), b.ravel()) / (na * nb))
 
 
-def check_attention(out, ref, lens, bf16=False, lse=None, ref_lse=None, label=""):
-    """Element-wise tolerance, per-(sequence, head) cosine, lse."""
-    assert np.all(np.isfinite(out)), f"{label}: non-finite output"
-    err = np.abs(out.astype(np.float64) - ref)
-    tol = ATOL + (bf16_half_ulp(ref) if bf16 else 0.0)
-    bad = err > tol
-    assert not bad.any(), (f"{label}: {bad.sum()} elements out of tolerance, max err {err.max():.3g} "
-                           f"at {np.unravel_index(err.argmax(), err.shape)}")
+def check_attention(out, ref, lens, bf16=False, lse=None, ref_lse=None, label="", extra=None):
+    """Element-wise bar (check_values), per-(sequence, head) cosine, lse."""
+    err, _ = check_values(out, ref, bf16=bf16, extra=extra, label=label)
     for b in range(out.shape[0]):
         if lens[b] == 0:
             assert np.all(out[b] == 0), f"{label}: empty sequence must give zeros"
@@ -144,7 +187,7 @@ def check_attention(out, ref, lens, bf16=False, lse=None, ref_lse=None, label=""
             else:
                 d = np.abs(lse[b] - ref_lse[b]).max()
                 assert d <= LSE_ATOL, f"{label}: lse differs by {d}"
-    return float(err.max())
+    return err
 
 
 def check_dequant_prefix(case: Case, stride_extra: int = 0):

@@ -119,6 +119,12 @@ def test_workspace_and_split_plan(lib):
     assert lib.kvq_decode_num_splits(ctypes.byref(c), 1, 4, 0, ctypes.byref(splits)) == OK
     assert splits.value == 1
     assert lib.kvq_decode_num_splits(ctypes.byref(c), 1, 4, 10, None) == ERR_NULL
+    # a wavefront sums at most 256 chunks (8,192 tokens) into its accumulators:
+    # 1,024 sequences x 4 heads at 1M tokens need 32 splits of 4 wavefronts
+    assert lib.kvq_decode_num_splits(ctypes.byref(c), 1024, 24, 1 << 20, ctypes.byref(splits)) == OK
+    assert splits.value == 32
+    assert lib.kvq_decode_num_splits(ctypes.byref(c), 32, 24, 1 << 20, ctypes.byref(splits)) == OK
+    assert -(-(1 << 15) // splits.value) <= 4 * 256
 
 
 def test_dequant_prefix_validation(lib):

@@ -7,7 +7,11 @@ packed bytes of sampled rows against the oracle's quantization of the same
 input rows (bit-exact); decode attention of sampled (sequence, query head)
 pairs against the oracle run on that sequence's pages copied to the host
 (tolerance of gpu_cases); and, where the workload has them, the chunked-prefill
-store and prefix dequantization of sampled pages (bit-exact)."""
+store and prefix dequantization of sampled pages (bit-exact); and extend
+attention of a 4,096-token chunk over the cached prefix -- through the bf16
+workspace and fused over the 4-bit pages -- at the prefixes the benchmark
+times (32K, 1M, the INT4 220K), on sampled chunk rows against the oracle's
+paged extend (the prefix at its exact dequantized value)."""
 import math
 
 import numpy as np
@@ -16,7 +20,7 @@ import torch
 
 import oracle
 from bit_quantized_kv_amd import inputs, kvq
-from gpu_cases import check_attention
+from gpu_cases import F16_WEIGHT_REL, check_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -121,6 +125,54 @@ class FullLayer:
                             label=f"seq {b} heads {heads}")
 
 
+def check_extend_rows(lay, pool, Lp, rows, label, workspace=True, fused=True, seed=0):
+    """Extend attention of a 4,096-token chunk (N(0,1) bf16 K, V, q) over the
+    first Lp cached tokens of sequence 0, run whole on the GPU in the bench's
+    launch configuration; sampled rows against the oracle's paged extend over
+    the same pages.  The workspace path (prefix through kvq_dequant_prefix;
+    exact in bf16 at gs = 1) is held to the absolute bar, the fused path to
+    its derived bar (fp16 weights on the steps inside the prefix)."""
+    n = 4096
+    g = torch.Generator(device="cuda")
+    g.manual_seed(inputs.seed_int(lay.wid, 1, 50 + seed))
+    kc = torch.randn((n, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((n, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((n, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
+    bt0 = lay.bt_dev[0]
+    outs = {}
+    if workspace:
+        k_ws = torch.empty((Lp + n, HKV, D), dtype=torch.bfloat16, device="cuda")
+        v_ws = torch.empty_like(k_ws)
+        kvq.kvq_dequant_prefix(lay.cache, bt0, Lp, k_ws, v_ws)
+        k_ws[Lp:] = kc
+        v_ws[Lp:] = vc
+        lse = torch.empty((n, HQ), dtype=torch.float32, device="cuda")
+        o = kvq.kvq_extend_attention(q, k_ws, v_ws, Lp, lse=lse, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        outs["workspace"] = (o[rows].cpu().numpy(), lse[rows].cpu().numpy(), False)
+        del k_ws, v_ws, o
+    if fused:
+        lse = torch.empty((n, HQ), dtype=torch.float32, device="cuda")
+        o = kvq.kvq_extend_attention_paged(lay.cache, bt0, Lp, q, kc, vc, lse=lse, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        outs["fused"] = (o[rows].cpu().numpy(), lse[rows].cpu().numpy(), True)
+        del o
+    pps = -(-Lp // lay.P)
+    sub = oracle.Pool(lay.fmt, pps, lay.P, HKV, D)
+    sub.data[:] = pool[lay.bt[0, :pps]]
+    qh = q[rows].float().cpu().numpy()
+    ref, ref_lse, oabs = sub.extend_attention(qh, np.arange(pps, dtype=np.int32), Lp, kc.float().cpu().numpy(),
+                                              vc.float().cpu().numpy(), q_pos=Lp + np.array(rows), want_abs=True)
+    failures = []
+    for name, (got, got_lse, f16) in outs.items():
+        try:
+            check_attention(got, ref, np.ones(len(rows), np.int32), lse=got_lse, ref_lse=ref_lse,
+                            label=f"{label} {name} rows {rows}", extra=F16_WEIGHT_REL * oabs if f16 else None)
+        except AssertionError as e:
+            failures.append(str(e))
+    assert not failures, "; ".join(failures)
+
+
 def test_full_32k_nvfp4_batch32():
     # Qwen3.8-27B-shaped layer: 4 KV heads x D 256, 24 q heads, batch 32, 32,768 tokens, 16-token pages
     print("case: full 32K NVFP4 layer", flush=True)
@@ -170,6 +222,9 @@ def test_full_1m_nvfp4_split_context_and_prefix_dequant():
             g = got[t0:t0 + 64].view(torch.int16).cpu().numpy().view(np.uint16).reshape(64, HKV, D)
             assert np.array_equal(g, ref), t0
     del k_ws, v_ws
+    torch.cuda.empty_cache()
+    # extend of a 4,096-token chunk over the whole 1M prefix, both paths
+    check_extend_rows(lay, pool, L, [0, 2047, 4095], "1M extend")
 
 
 def test_full_int4_220k_page1600():
@@ -177,6 +232,8 @@ def test_full_int4_220k_page1600():
     lay = FullLayer(5, 2, 8, 220000, 1600, False, "student_t")
     pool = lay.check_packing()
     lay.check_decode(pool, seqs=[0, 7], heads_per_group=1)
+    # the fused extend of a 4,096-token chunk over the first sequence's 220K prefix
+    check_extend_rows(lay, pool, 220000, [0, 1, 4095], "INT4 220K extend", workspace=False)
 
 
 def test_full_32k_fp8_comparator_batch32():
@@ -264,23 +321,10 @@ def test_full_fused_extend_4096_over_32k_cached_prefix(fmt):
     ref_pool = oracle.Pool(fmt, pps, P, HKV, D)
     ref_pool.quantize_store(kp.float().cpu().numpy(), vp.float().cpu().numpy(), slots)
     assert np.array_equal(cache.pool.cpu().numpy(), ref_pool.data), "cache bytes differ from the oracle's"
-    # prefix values: exact dequantization (bf16 holds e2m1 x e4m3 exactly at gs = 1; INT4 rows as q x s)
-    if fmt == 1:
-        kq, vq = ref_pool.dequant_prefix(bt, Lp)
-        kq = (kq.astype(np.uint32) << 16).view(np.float32)
-        vq = (vq.astype(np.uint32) << 16).view(np.float32)
-    else:
-        kq = np.zeros((Lp, HKV, D), np.float32)
-        vq = np.zeros((Lp, HKV, D), np.float32)
-        for t in range(Lp):
-            for h in range(HKV):
-                kq[t, h] = ref_pool.dequant_token(int(bt[t // P]), h, t % P, 0)
-                vq[t, h] = ref_pool.dequant_token(int(bt[t // P]), h, t % P, 1)
-    kh = np.concatenate([kq, kc.float().cpu().numpy()])
-    vh = np.concatenate([vq, vc.float().cpu().numpy()])
-    qh = q.float().cpu().numpy()
-    out, lse = out.cpu().numpy(), lse.cpu().numpy()
-    for i in (0, 1, 63, 64, 2047, 4095):
-        ref, ref_lse = oracle.extend_attention(qh[i:i + 1], kh, vh, Lp + i)
-        check_attention(out[i:i + 1], ref, np.ones(1, np.int32), lse=lse[i:i + 1], ref_lse=ref_lse,
-                        label=f"fused extend row {i}")
+    # the oracle's paged extend reads the prefix at its exact (fp64) dequantized value
+    rows = [0, 1, 63, 64, 2047, 4095]
+    ref, ref_lse, oabs = ref_pool.extend_attention(q[rows].float().cpu().numpy(), bt, Lp, kc.float().cpu().numpy(),
+                                                   vc.float().cpu().numpy(), q_pos=Lp + np.array(rows),
+                                                   want_abs=True)
+    check_attention(out[rows].cpu().numpy(), ref, np.ones(len(rows), np.int32), lse=lse[rows].cpu().numpy(),
+                    ref_lse=ref_lse, label="fused extend 32K", extra=F16_WEIGHT_REL * oabs)

@@ -29,12 +29,11 @@ def test_k8v4_store_and_decode(D, Hkv, G, P, lens, kind, dtype, scales):
     check_pool_bitexact(c)
     ref, ref_lse = c.oracle_decode()
     out, lse = c.decode(torch.float32)
-    s = max(1.0, float(np.abs(ref).max()))
-    check_attention(out / s, ref / s, c.lens, lse=lse, ref_lse=ref_lse, label="fp32 out")
+    check_attention(out, ref, c.lens, lse=lse, ref_lse=ref_lse, label="fp32 out")
     outb, _ = c.decode(torch.bfloat16, want_lse=False)
     check_attention(outb, ref, c.lens, bf16=True, label="bf16 out")
     for ns in (1, 3, 0):
         o1, l1 = c.decode(torch.float32, num_splits=ns)
         o2, l2 = c.decode(torch.float32, num_splits=ns)
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
-        check_attention(o1 / s, ref / s, c.lens, lse=l1, ref_lse=ref_lse, label=f"splits {ns}")
+        check_attention(o1, ref, c.lens, lse=l1, ref_lse=ref_lse, label=f"splits {ns}")

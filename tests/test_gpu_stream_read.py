@@ -26,3 +26,19 @@ def test_stream_read_sees_every_vector(n16, where, wgs, want):
     kvq.kvq_stream_read(buf, sink, num_workgroups=wgs)
     torch.cuda.synchronize()
     assert int(sink.item()) == want
+
+
+@pytest.mark.parametrize("n16,wgs", [(256 * 5 + 37, 0), (1, 0), (4096, 3)])
+def test_stream_write_and_copy_touch_exactly_their_bytes(n16, wgs):
+    """The write and copy ceiling kernels cover every 16-byte vector of their
+    range (a ragged tail included) and nothing past it."""
+    print(f"case: stream write/copy n16 {n16} wgs {wgs}", flush=True)
+    buf = torch.full((n16 + 8, 4), -1, dtype=torch.int32, device="cuda")
+    kvq.kvq_stream_write(buf[:n16], value=0x01020304, num_workgroups=wgs)
+    torch.cuda.synchronize()
+    assert bool((buf[:n16] == 0x01020304).all()) and bool((buf[n16:] == -1).all())
+    src = torch.arange((n16 + 8) * 4, dtype=torch.int32, device="cuda").reshape(n16 + 8, 4)
+    dst = torch.full_like(src, -7)
+    kvq.kvq_stream_copy(src[:n16], dst[:n16], num_workgroups=wgs)
+    torch.cuda.synchronize()
+    assert bool((dst[:n16] == src[:n16]).all()) and bool((dst[n16:] == -7).all())

@@ -694,3 +694,73 @@ def test_extend_attention_closed_forms(oracle):
     k2 = np.repeat(k[:1], 3, axis=0)
     out2, _ = oracle.extend_attention(q, k2, v, 0)
     np.testing.assert_allclose(out2[2, 0], v[:3, 0].astype(np.float64).mean(axis=0), rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------- extend attention (paged prefix, no workspace)
+
+def _sdpa_fp64(q, K, V, G, prefix_len, q_pos):
+    """torch fp64 attention: query j (head h) over keys 0 .. q_pos[j] of KV head h // G."""
+    qt = torch.from_numpy(np.asarray(q, np.float64)).transpose(0, 1)             # [Hq][n][D]
+    kt = torch.from_numpy(K).repeat_interleave(G, dim=1).transpose(0, 1)          # [Hq][Lk][D]
+    vt = torch.from_numpy(V).repeat_interleave(G, dim=1).transpose(0, 1)
+    Lk = K.shape[0]
+    mask = torch.arange(Lk)[None, :] <= torch.from_numpy(np.asarray(q_pos))[:, None]
+    D = q.shape[-1]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt.contiguous(), attn_mask=mask,
+                                                         scale=1 / math.sqrt(D))
+    s = (qt @ kt.transpose(1, 2).contiguous()) / math.sqrt(D)
+    lse = torch.logsumexp(s.masked_fill(~mask, float("-inf")), dim=-1)
+    return o.transpose(0, 1).numpy(), lse.transpose(0, 1).numpy()
+
+
+@pytest.mark.parametrize("fmt,P,G,Hkv,D,Lp,n,gs", [(1, 16, 4, 2, 64, 45, 7, (0.37, 2.5)),
+                                                   (2, 4, 6, 1, 32, 33, 5, (1.0, 1.0)),
+                                                   (1, 3, 1, 2, 64, 10, 4, (1.0, 1.0)),
+                                                   (2, 16, 2, 2, 64, 0, 6, (1.0, 1.0))])
+def test_extend_paged_matches_torch_over_exact_rows(oracle, fmt, P, G, Hkv, D, Lp, n, gs):
+    """The paged extend oracle against torch's fp64 attention over the pool's
+    exactly dequantized prefix rows (each gathered by dequant_token, whose
+    codecs are pinned above) followed by the chunk rows; and its weighted |v|
+    against the same torch attention with |V|."""
+    Hq = G * Hkv
+    pages_n = max(1, -(-Lp // P))
+    bt = inputs.page_tables(31, 1, pages_n, num_pages=pages_n + 2, shuffled=True)
+    pool = oracle.Pool(fmt, pages_n + 2, P, Hkv, D, global_scale=gs)
+    k, v = inputs.kv_outlier_channels(31, 0, Lp, Hkv, D)
+    pool.quantize_store(k, v, inputs.slots_for(bt, P, 0, 0, Lp))
+    kc, vc = inputs.kv_lognormal_channels(32, 0, n, Hkv, D)
+    q = inputs.query(33, 0, n, Hq, D).reshape(n, Hq, D)
+    out, lse, oabs = pool.extend_attention(q, bt[0], Lp, kc, vc, want_abs=True)
+    K = np.concatenate([_gather(pool, bt, Lp, 0, 0), kc.astype(np.float64)])
+    V = np.concatenate([_gather(pool, bt, Lp, 0, 1), vc.astype(np.float64)])
+    pos = np.arange(Lp, Lp + n)
+    o_ref, lse_ref = _sdpa_fp64(q, K, V, G, Lp, pos)
+    np.testing.assert_allclose(out, o_ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-10, atol=1e-12)
+    a_ref, _ = _sdpa_fp64(q, K, np.abs(V), G, Lp, pos)
+    np.testing.assert_allclose(oabs, a_ref, rtol=1e-10, atol=1e-12)
+    assert np.all(oabs >= np.abs(out) - 1e-12)  # |sum w v| <= sum w |v|
+    # sampled query positions give the rows of the full computation
+    sel = [n - 1, 0]
+    o2, l2 = pool.extend_attention(q[sel], bt[0], Lp, kc, vc, q_pos=pos[sel])
+    np.testing.assert_array_equal(o2, out[sel])
+    np.testing.assert_array_equal(l2, lse[sel])
+
+
+def test_extend_paged_equals_workspace_oracle_at_unit_scale(oracle):
+    """At gs = 1 an NVFP4 prefix dequantizes exactly into bf16, so the paged
+    oracle and the workspace oracle over kvq_dequant_prefix's rows attend over
+    the same values."""
+    P, Hkv, D, G, Lp, n = 16, 2, 64, 3, 70, 9
+    bt = inputs.page_tables(41, 1, 5, num_pages=7, shuffled=True)
+    pool = oracle.Pool(1, 7, P, Hkv, D)
+    k, v = inputs.kv_lognormal_channels(41, 0, Lp, Hkv, D)
+    pool.quantize_store(k, v, inputs.slots_for(bt, P, 0, 0, Lp))
+    kc, vc = inputs.kv_lognormal_channels(42, 0, n, Hkv, D)
+    q = inputs.query(43, 0, n, G * Hkv, D).reshape(n, G * Hkv, D)
+    out, lse = pool.extend_attention(q, bt[0], Lp, kc, vc)
+    kw, vw = pool.dequant_prefix(bt[0], Lp)
+    widen = lambda a: (a.astype(np.uint32) << 16).view(np.float32)  # noqa: E731
+    ref, ref_lse = oracle.extend_attention(q, np.concatenate([widen(kw), kc]), np.concatenate([widen(vw), vc]), Lp)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-13)

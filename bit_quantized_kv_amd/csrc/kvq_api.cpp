@@ -232,6 +232,23 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
                        out, out_dtype, lse_out, workspace, stream);
 }
 
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q, int32_t num_q_heads,
+                                        const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                                        int32_t batch, int32_t max_seq_len, float sm_scale, int32_t num_splits,
+                                        void* out, int32_t out_dtype, float* lse_out, void* stream) {
+  kvq_status st = decode_args(cache, q, num_q_heads, block_table, max_pages, seq_lens, batch, max_seq_len, out,
+                              out_dtype, lse_out);
+  if (st != KVQ_OK) return st;
+  const int32_t splits = num_splits > 0 ? num_splits : auto_splits(cache->fmt, batch, cache->num_kv_heads, max_seq_len);
+  if (splits > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (workspace_bytes(cache, batch, num_q_heads, splits) > kvq::kDecodeScratchBytes) return KVQ_ERR_SCRATCH;
+  void* scratch = nullptr;
+  const kvq_status sst = hip_status(kvq::decode_scratch(&scratch));
+  if (sst != KVQ_OK) return sst;
+  return decode_launch(cache, q, num_q_heads, block_table, max_pages, seq_lens, batch, max_seq_len, sm_scale, splits,
+                       out, out_dtype, lse_out, scratch, stream);
+}
+
 kvq_status kvq_dequant_prefix(const kvq_cache* cache, const int32_t* block_table_row, int32_t prefix_len,
                               void* k_out, void* v_out, int64_t out_token_stride, void* stream) {
   kvq_status st = check_cache(cache);
@@ -445,6 +462,7 @@ const char* kvq_status_string(int32_t status) {
     case KVQ_ERR_ALIGN: return "a pointer or stride is not 16-byte aligned";
     case KVQ_ERR_WORKSPACE: return "workspace smaller than kvq_decode_workspace_size";
     case KVQ_ERR_HIP: return "HIP launch failed (see kvq_last_hip_error)";
+    case KVQ_ERR_SCRATCH: return "decode partials exceed the static scratch of kvq_decode_attention_noalloc";
     default: return "unknown status";
   }
 }

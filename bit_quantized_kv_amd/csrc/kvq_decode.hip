@@ -43,6 +43,7 @@
 //   q is scaled by a power of two so its largest magnitude sits in
 //   [2^14, 2^15): every bf16 element within 2^32 of the largest is then exact
 //   in fp16 (smaller ones round, far below the fp32 accumulation's precision).
+#include <mutex>
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -1100,6 +1101,34 @@ __global__ __launch_bounds__(256) void merge_wide_kernel(const DecodeParams p) {
     ((float*)p.out)[oi] = o;
   if (p.lse != nullptr && cb == 0 && cl == 0)
     p.lse[(int64_t)b * p.num_q_heads + h] = den > 0.0f ? (M + log2f(den)) * kLn2 : -__builtin_inff();
+}
+
+// ---------------------------------------------------------------- static scratch
+// The split partials of kvq_decode_attention_noalloc live in this array (one
+// copy per device, held until the process ends) instead of a caller
+// workspace.  Host code never passes the array's name to a kernel -- on the
+// host it is only a stand-in for the symbol -- but the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept.  Calls that overlap on one device share the array and
+// race; no part of it needs to start at zero (an empty split writes zeros).
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kScratchMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream_t stream) {

@@ -10,6 +10,11 @@ namespace kvq {
 // chunk of the workgroup's split, and the workgroup merges them in LDS.
 constexpr int kDecodeWaves = 4;
 
+// Size of the static device scratch that kvq_decode_attention_noalloc uses in
+// place of a caller workspace (16 MiB per device), and the devices it tracks.
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+constexpr int kScratchMaxDevices = 64;
+
 struct StoreParams {
   uint8_t* pool;
   const float* gs;  // {gs_K, gs_V} (NVFP4 global / FP8 per-tensor scales)
@@ -82,6 +87,9 @@ hipError_t launch_calibrate_amax(const StoreParams& p, int head_dim, int in_bf16
 hipError_t launch_global_scale(const float* running, float* gs, hipStream_t stream);
 hipError_t launch_hadamard(const RotateParams& p, int head_dim, int in_bf16, int out_bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream_t stream);
+// Device address of the current device's static decode scratch
+// (kDecodeScratchBytes), looked up on the first call per device.
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_extend(const ExtendParams& p, int head_dim, int src_fmt, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
 hipError_t launch_stream_write(void* buf, int64_t bytes, uint32_t value, int workgroups, hipStream_t stream);

@@ -61,6 +61,7 @@ def lib():
         "kvq_decode_num_splits": (i32, [C, i32, i32, i32, ctypes.POINTER(i32)]),
         "kvq_decode_workspace_size": (i32, [C, i32, i32, i32, i32, ctypes.POINTER(sz)]),
         "kvq_decode_attention": (i32, [C, P, i32, P, i32, P, i32, i32, f32, i32, P, i32, P, P, sz, P]),
+        "kvq_decode_attention_noalloc": (i32, [C, P, i32, P, i32, P, i32, i32, f32, i32, P, i32, P, P]),
         "kvq_dequant_prefix": (i32, [C, P, i32, P, P, i64, P]),
         "kvq_stream_read": (i32, [P, sz, P, i32, P]),
         "kvq_stream_write": (i32, [P, sz, ctypes.c_uint32, i32, P]),
@@ -177,6 +178,23 @@ def kvq_decode_attention(cache: Cache, q: torch.Tensor, block_table: torch.Tenso
         ctypes.byref(d), _ptr(q), Hq, _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, int(max_seq_len),
         float(sm_scale), int(num_splits), _ptr(out), odt, _ptr(lse), _ptr(workspace), workspace.numel(),
         _stream(stream)))
+    return out
+
+
+def kvq_decode_attention_noalloc(cache: Cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                                 max_seq_len: int, out: torch.Tensor, lse: torch.Tensor | None = None,
+                                 sm_scale: float = 0.0, num_splits: int = 0, stream=None) -> torch.Tensor:
+    """kvq_decode_attention with the library's static scratch instead of a
+    workspace: the caller passes every buffer (out bf16 or fp32 [B][Hq][D],
+    optional lse fp32 [B][Hq]) and nothing is allocated."""
+    B, Hq, D = q.shape
+    assert q.dtype == torch.bfloat16 and q.is_contiguous()
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous() and seq_lens.dtype == torch.int32
+    odt = {torch.float32: DT_F32, torch.bfloat16: DT_BF16}[out.dtype]
+    d = cache.desc()
+    _check("kvq_decode_attention_noalloc", lib().kvq_decode_attention_noalloc(
+        ctypes.byref(d), _ptr(q), Hq, _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, int(max_seq_len),
+        float(sm_scale), int(num_splits), _ptr(out), odt, _ptr(lse), _stream(stream)))
     return out
 
 

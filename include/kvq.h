@@ -59,7 +59,9 @@
  * Conventions
  *   - The caller owns all memory.  The library allocates and frees nothing and
  *     keeps no state between calls beyond per-device constants it looks up
- *     once (compute-unit count, kernel attributes).
+ *     once (compute-unit count, kernel attributes) and the static decode
+ *     scratch of kvq_decode_attention_noalloc (16 MiB per device, a device
+ *     array of the library itself).
  *   - All work is enqueued on the caller's HIP stream (`stream`, a
  *     hipStream_t; NULL = the default stream) and is asynchronous.  The calls
  *     record nothing but kernel launches (no allocation, copy or memset), so
@@ -93,7 +95,9 @@ typedef enum {
   KVQ_ERR_UNSUPPORTED = -3, /* outside the supported formats / limits */
   KVQ_ERR_ALIGN = -4,       /* a pointer or stride breaks 16-byte alignment */
   KVQ_ERR_WORKSPACE = -5,   /* workspace smaller than kvq_decode_workspace_size */
-  KVQ_ERR_HIP = -6          /* a HIP launch failed; see kvq_last_hip_error() */
+  KVQ_ERR_HIP = -6,         /* a HIP launch failed; see kvq_last_hip_error() */
+  KVQ_ERR_SCRATCH = -7      /* kvq_decode_attention_noalloc: the shape needs more
+                               than its static scratch (16 MiB) */
 } kvq_status;
 
 typedef enum { KVQ_FMT_NVFP4 = 1, KVQ_FMT_INT4_TOKHEAD = 2, KVQ_FMT_FP8_E4M3 = 3, KVQ_FMT_K8V4 = 4 } kvq_format;
@@ -194,6 +198,25 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
                                 int32_t batch, int32_t max_seq_len, float sm_scale, int32_t num_splits, void* out,
                                 int32_t out_dtype, float* lse_out, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* kvq_decode_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, kernels and split plan,
+ * so the results equal kvq_decode_attention's for the same num_splits
+ * bit for bit; the split partials go to a static scratch array of the library
+ * instead: 16 MiB per device, held from the first call on a device until the
+ * process ends (kvq_decode_workspace_size gives a shape's need; a larger need
+ * returns KVQ_ERR_SCRATCH and launches nothing).  The first call on a device
+ * looks the array's device address up once (hipGetSymbolAddress); no call
+ * allocates or frees.  Every call on a device shares that device's array, so
+ * calls that overlap on one device (different streams or threads, without
+ * ordering between them) race and give undefined results; calls ordered on
+ * one stream are safe.  The array needs no clearing: every call writes all of
+ * the partials it reads. */
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q, int32_t num_q_heads,
+                                        const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                                        int32_t batch, int32_t max_seq_len, float sm_scale, int32_t num_splits,
+                                        void* out, int32_t out_dtype, float* lse_out, void* stream);
 
 /* Prefix dequantization for chunked prefill / extend ("SGLang's 4-bit KV cache
  * ...", Figure 2 caption: the cached prefix is dequantized into a reused

@@ -95,7 +95,7 @@ int main() {
   kvq_cache i4 = cache(KVQ_FMT_INT4_TOKHEAD, 64, 1600, 4, 256, F, nullptr);
   CHECK("store int4 no gs", kvq_quantize_store(&i4, F, F, 1, 1024, (const int32_t*)F, 4, nullptr), KVQ_OK, 1);
 
-  // ---- decode, split plan and workspace size
+  // ---- decode (workspace and static scratch), split plan and workspace size
   int32_t splits = 0;
   size_t bytes = 0;
   CHECK("num splits", kvq_decode_num_splits(&c, 32, 24, 32768, &splits), KVQ_OK, 0);
@@ -144,6 +144,14 @@ int main() {
   CHECK("decode splits 70000",
         kvq_decode_attention(&c, F, 24, T, 1 << 18, T, 1, 1 << 22, 0.f, 70000, F, 1, nullptr, F, 1ull << 40, nullptr),
         KVQ_ERR_UNSUPPORTED, 0);
+  CHECK("noalloc ok", kvq_decode_attention_noalloc(&c, F, 24, T, 2048, T, 32, 32768, 0.f, 0, F, 1, nullptr, nullptr),
+        KVQ_OK, 6);
+  CHECK("noalloc scratch",
+        kvq_decode_attention_noalloc(&c, F, 24, T, 2048, T, 4096, 32768, 0.f, 1, F, 1, nullptr, nullptr),
+        KVQ_ERR_SCRATCH, 0);
+  CHECK("noalloc out null",
+        kvq_decode_attention_noalloc(&c, F, 24, T, 2048, T, 32, 32768, 0.f, 0, nullptr, 1, nullptr, nullptr),
+        KVQ_ERR_NULL, 0);
 
   // ---- prefix dequant
   CHECK("dequant ok", kvq_dequant_prefix(&c, T, 16, F, F, 1024, nullptr), KVQ_OK, 2);
@@ -197,7 +205,7 @@ int main() {
   CHECK("write null", kvq_stream_write(nullptr, 4096, 7u, 0, nullptr), KVQ_ERR_NULL, 0);
   CHECK("copy ok", kvq_stream_copy(F, off(F, 4096), 4096, 0, nullptr), KVQ_OK, 10);
   CHECK("copy align", kvq_stream_copy(F, off(F, 8), 4096, 0, nullptr), KVQ_ERR_ALIGN, 0);
-  for (int s = -7; s <= 1; s++) {
+  for (int s = -8; s <= 1; s++) {
     const char* str = kvq_status_string(s);
     if (str == nullptr || str[0] == 0) {
       fprintf(stderr, "FAIL status string %d\n", s);

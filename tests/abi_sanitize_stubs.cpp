@@ -1,8 +1,8 @@
 // abi_sanitize_stubs.cpp -- host stand-ins for everything kvq_api.cpp calls
-// below the C ABI (the kernel launchers and the three HIP runtime queries),
-// so that the argument validation can be built for the host alone with
-// AddressSanitizer and UndefinedBehaviorSanitizer and run without a GPU
-// (test infrastructure: tests/test_abi_sanitized.py).
+// below the C ABI (the kernel launchers, the static-scratch lookup and the
+// three HIP runtime queries), so that the argument validation can be built
+// for the host alone with AddressSanitizer and UndefinedBehaviorSanitizer and
+// run without a GPU (test infrastructure: tests/test_abi_sanitized.py).
 // Each launcher records which kernel family was asked for; nothing runs.
 #include <hip/hip_runtime.h>
 
@@ -34,6 +34,10 @@ hipError_t launch_extend(const ExtendParams&, int, int, hipStream_t) { return re
 hipError_t launch_stream_read(const void*, int64_t, uint32_t*, int, hipStream_t) { return record(8); }
 hipError_t launch_stream_write(void*, int64_t, uint32_t, int, hipStream_t) { return record(9); }
 hipError_t launch_stream_copy(const void*, void*, int64_t, int, hipStream_t) { return record(10); }
+hipError_t decode_scratch(void** ptr) {
+  *ptr = (void*)(uintptr_t)0x200000;  // a stand-in device address, never dereferenced
+  return hipSuccess;
+}
 }  // namespace kvq
 
 extern "C" {

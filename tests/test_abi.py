@@ -12,7 +12,7 @@ from bit_quantized_kv_amd import kvq
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvq.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 
 
 def declared_functions():
@@ -100,6 +100,34 @@ def test_decode_validation(lib):
     assert decode(lib, cache(D=96)) == ERR_UNSUPPORTED
 
 
+def decode_noalloc(lib, c, q=FAKE, hq=24, bt=FAKE, maxp=2048, sl=FAKE, B=32, L=32768, ns=0, out=FAKE, odt=1,
+                   lse=None):
+    return lib.kvq_decode_attention_noalloc(ctypes.byref(c), q, hq, bt, maxp, sl, B, L, 0.0, ns, out, odt, lse, None)
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode checks its arguments like kvq_decode_attention
+    and refuses, before touching any device, a shape whose split partials need
+    more than its 16 MiB static scratch."""
+    c = cache()
+    assert decode_noalloc(lib, c, q=0) == ERR_NULL
+    assert decode_noalloc(lib, c, out=0) == ERR_NULL
+    assert decode_noalloc(lib, c, hq=26) == ERR_SHAPE
+    assert decode_noalloc(lib, c, hq=4 * 17) == ERR_UNSUPPORTED
+    assert decode_noalloc(lib, c, maxp=100) == ERR_SHAPE
+    assert decode_noalloc(lib, c, odt=5) == ERR_UNSUPPORTED
+    assert decode_noalloc(lib, c, out=FAKE + 4) == ERR_ALIGN
+    assert decode_noalloc(lib, cache(D=96)) == ERR_UNSUPPORTED
+    size = ctypes.c_size_t(0)
+    # 4096 sequences x 4 KV heads x 6 query heads x (256 + 2) floats: 101 MB of partials
+    assert lib.kvq_decode_workspace_size(ctypes.byref(c), 4096, 24, 32768, 1, ctypes.byref(size)) == OK
+    assert size.value > 16 << 20
+    assert decode_noalloc(lib, c, B=4096, ns=1, maxp=2048) == ERR_SCRATCH
+    # 256 splits of one sequence: 6.3 MB, within the scratch -- but a 70,000-split plan is not
+    assert decode_noalloc(lib, c, B=1, ns=70000, L=1 << 22, maxp=1 << 18) == ERR_UNSUPPORTED
+    assert decode_noalloc(lib, c, B=1, ns=4096, L=1 << 22, maxp=1 << 18) == ERR_SCRATCH
+
+
 def test_workspace_and_split_plan(lib):
     c = cache()
     splits = ctypes.c_int32(0)
@@ -140,7 +168,7 @@ def test_dequant_prefix_validation(lib):
 
 
 def test_status_strings(lib):
-    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP):
+    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH):
         assert kvq.status_string(s) and kvq.status_string(s) != "unknown status"
     assert kvq.status_string(42) == "unknown status"
     assert lib.kvq_last_hip_error() == 0

@@ -85,10 +85,10 @@ def token_head_bytes(fmt: int) -> int:
 REPO = os.path.dirname(os.path.abspath(__file__))
 DECODE_SOURCES = ["bit_quantized_kv_amd/csrc/kvq_decode.hip", "bit_quantized_kv_amd/csrc/kvq_device.h",
                   "bit_quantized_kv_amd/csrc/kvq_launch.h"]
-PMC_RUN = ('cd /tmp && export TMPDIR=/tmp && cd "$GRAFT_REPO_ROOT" && timeout -s KILL 150 rocprofv3 --pmc {counter} '
+PMC_RUN = ('cd /tmp && export TMPDIR=/tmp && cd "$GRAFT_REPO_ROOT" && timeout -s KILL 200 rocprofv3 --pmc {counter} '
            '--output-format csv -d gpurun_out/pmc_{tag} -o run -- python -u bench.py --workload {workload} '
            '--secondary "" --no-cpu-baseline --no-quality --steps 5 --warmup 1 --layers 2 --copy-calibration-gib 1')
-CALIB_BYTES = 1 << 30
+CALIB_BYTES = 4 << 30  # bytes read (and written) by one kvq_stream_copy of the copy ceiling
 
 
 def decode_source_digest() -> str:
@@ -138,15 +138,29 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> str:
         def avg(pred):
             v = [float(r["Counter_Value"]) for r in rows if pred(r)]
             return (sum(v) / len(v), len(v)) if v else (None, 0)
-        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        big = max(int(r["Grid_Size"]) for r in copies)
+        # the decode call of the workload's own split plan: the most frequent
+        # decode grid (a split sweep adds other grids), and the merge launched with it
+        grids = [int(r["Grid_Size"]) for r in rows if "decode_kernel" in r["Kernel_Name"]]
+        main_grid = max(set(grids), key=grids.count)
+        n_main = grids.count(main_grid)
+        merges = [int(r["Grid_Size"]) for r in rows if "merge" in r["Kernel_Name"]]
+        merge_grid = max(set(merges), key=merges.count) if merges else None
         per[counter] = {
-            "decode_kernel": avg(lambda r: "decode_kernel" in r["Kernel_Name"]),
-            "merge_kernel": avg(lambda r: "merge_kernel" in r["Kernel_Name"]),
-            "copy_1gib": avg(lambda r: "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) == big),
+            "decode_kernel": avg(lambda r: "decode_kernel" in r["Kernel_Name"] and int(r["Grid_Size"]) == main_grid),
+            "merge_kernel": avg(lambda r: "merge" in r["Kernel_Name"] and int(r["Grid_Size"]) == merge_grid),
+            "stream_copy": avg(lambda r: "stream_copy_kernel" in r["Kernel_Name"]),
         }
-    f_fac = CALIB_BYTES / 1024 / per["FETCH_SIZE"]["copy_1gib"][0]
-    w_fac = CALIB_BYTES / 1024 / per["WRITE_SIZE"]["copy_1gib"][0]
+        # every other library kernel, per (name, grid): the write-side kernels
+        others = {}
+        for r in rows:
+            name = r["Kernel_Name"]
+            if "kvq::" not in name or "decode_kernel" in name or "merge" in name or "stream_" in name:
+                continue
+            key = (name.split("(")[0].replace("void kvq::", ""), int(r["Grid_Size"]))
+            others.setdefault(key, []).append(float(r["Counter_Value"]))
+        per[counter]["others"] = {k: (sum(v) / len(v), len(v)) for k, v in others.items()}
+    f_fac = CALIB_BYTES / 1024 / per["FETCH_SIZE"]["stream_copy"][0]
+    w_fac = CALIB_BYTES / 1024 / per["WRITE_SIZE"]["stream_copy"][0]
     fetch_kib = per["FETCH_SIZE"]["decode_kernel"][0] + per["FETCH_SIZE"]["merge_kernel"][0]
     write_kib = per["WRITE_SIZE"]["decode_kernel"][0] + per["WRITE_SIZE"]["merge_kernel"][0]
     traffic = 1024 * (f_fac * fetch_kib + w_fac * write_kib)
@@ -158,24 +172,39 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> str:
            "traffic_bytes_per_call": traffic, "algorithmic_bytes_per_call": algo}
     lines = [f"# HBM traffic of the decode call: {workload}", "",
              "Two counter passes (run from the repository root on one MI355X):", "", "```",
-             PMC_RUN.format(counter="FETCH_SIZE", tag="fetch", workload=workload),
-             PMC_RUN.format(counter="WRITE_SIZE", tag="write", workload=workload),
-             f"python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write --workload {workload}",
+             PMC_RUN.format(counter="FETCH_SIZE", tag=f"fetch_{workload}", workload=workload),
+             PMC_RUN.format(counter="WRITE_SIZE", tag=f"write_{workload}", workload=workload),
+             f"python bench.py --summarize-pmc gpurun_out/pmc_fetch_{workload} gpurun_out/pmc_write_{workload} "
+             f"--workload {workload}",
              "```", "",
              "Per-dispatch averages (KiB as the counters report them):", "",
              "| kernel | FETCH_SIZE | dispatches | WRITE_SIZE | dispatches |", "|---|---|---|---|---|"]
-    for k in ("decode_kernel", "merge_kernel", "copy_1gib"):
+    for k in ("decode_kernel", "merge_kernel", "stream_copy"):
         fv, fn = per["FETCH_SIZE"][k]
         wv, wn = per["WRITE_SIZE"][k]
         lines.append(f"| {k} | {fv:,.1f} | {fn} | {wv:,.1f} | {wn} |")
     lines += ["",
-              f"Calibration: a 1 GiB device copy (1,048,576 KiB read and written) reads "
-              f"{per['FETCH_SIZE']['copy_1gib'][0]:,.1f} KiB of FETCH_SIZE and "
-              f"{per['WRITE_SIZE']['copy_1gib'][0]:,.1f} KiB of WRITE_SIZE, so the factors are "
+              f"Calibration: the library's plain 4 GiB copy (kvq_stream_copy in the bench's copy ceiling, "
+              f"4,194,304 KiB read and written) reads {per['FETCH_SIZE']['stream_copy'][0]:,.1f} KiB of FETCH_SIZE "
+              f"and {per['WRITE_SIZE']['stream_copy'][0]:,.1f} KiB of WRITE_SIZE, so the factors are "
               f"{f_fac:.4f} (fetch) and {w_fac:.4f} (write).", "",
               f"Traffic per decode call (decode + merge kernels): {traffic:,.0f} B = "
-              f"{traffic / algo:.4f} x the algorithmic {algo:,} B of packed KV.", "",
-              "```json", json.dumps(rec, indent=1), "```", ""]
+              f"{traffic / algo:.4f} x the algorithmic {algo:,} B of packed KV.", ""]
+    keys = sorted(set(per["FETCH_SIZE"]["others"]) | set(per["WRITE_SIZE"]["others"]))
+    if keys:
+        lines += ["Other library kernels of the same run, per dispatch (MB = the counters x the calibration "
+                  "factors / 1e6; stores are cache population in 65,536-token chunks and the step's new "
+                  "tokens, the dequant is the whole prefix):", "",
+                  "| kernel | grid (threads) | fetched MB | written MB | dispatches |", "|---|---|---|---|---|"]
+        for k in keys:
+            fv, fn = per["FETCH_SIZE"]["others"].get(k, (0.0, 0))
+            wv, wn = per["WRITE_SIZE"]["others"].get(k, (0.0, 0))
+            lines.append(f"| `{k[0]}` | {k[1]:,} | {fv * f_fac * 1024 / 1e6:,.2f} | {wv * w_fac * 1024 / 1e6:,.2f} | "
+                         f"{max(fn, wn)} |")
+            rec.setdefault("other_kernels", []).append(
+                {"kernel": k[0], "grid": k[1], "fetch_bytes": fv * f_fac * 1024, "write_bytes": wv * w_fac * 1024})
+        lines.append("")
+    lines += ["```json", json.dumps(rec, indent=1), "```", ""]
     return "\n".join(lines)
 
 

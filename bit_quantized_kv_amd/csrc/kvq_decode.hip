@@ -56,6 +56,62 @@ static constexpr float kLn2 = 0.6931471805599453f;
 static constexpr float kRescaleSlack = 8.0f;  // log2 of the largest unnormalised p
 static constexpr int kWaves = kDecodeWaves;   // wavefronts per decode workgroup
 
+// lane l + (l ^ 8): DPP row rotation by 8 within each 16-lane row (VALU only).
+__device__ inline float add_xor8(float x) {
+  return x + as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(x), 0x128, 0xF, 0xF, false));
+}
+
+// The workgroup's partial result.  Each wave has put its unnormalised o in
+// sm_o ([kWaves][G][D], its own slice) and its running (m, l) per query in
+// sm_ml ([kWaves][G][2]).  After one barrier every thread takes float4s of
+// the [G][D] result: o = sum over waves, in wave order, of o_w * 2^(m_w - M)
+// * vscale (an empty wave, m_w = -inf, weighs 0), M the largest m_w; and the
+// first G threads write (M, l = sum of 2^(m_w - M) l_w).  Fixed order
+// throughout: the partial is reproducible.
+template <int D>
+__device__ inline void finish_partial(const float* sm_o, const float* sm_ml, int G, float vscale, float* po,
+                                      float* ml) {
+  __syncthreads();
+  const int tid = threadIdx.x;
+  for (int i = tid; i < G * (D / 4); i += 64 * kWaves) {
+    const int n = i / (D / 4);
+    float mw[kWaves], M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+      mw[w] = sm_ml[(w * G + n) * 2];
+      M = fmaxf(M, mw[w]);
+    }
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+      const float sc = mw[w] == -__builtin_inff() ? 0.0f : exp2f(mw[w] - M) * vscale;
+      const float4 x = ((const float4*)(sm_o + (size_t)w * G * D))[i];
+      if (w == 0) {
+        acc = make_float4(x.x * sc, x.y * sc, x.z * sc, x.w * sc);
+      } else {
+        acc.x += x.x * sc;
+        acc.y += x.y * sc;
+        acc.z += x.z * sc;
+        acc.w += x.w * sc;
+      }
+    }
+    ((float4*)po)[i] = acc;
+  }
+  if (tid < G) {
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, sm_ml[(w * G + tid) * 2]);
+    float l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+      const float m = sm_ml[(w * G + tid) * 2];
+      if (m != -__builtin_inff()) l += exp2f(m - M) * sm_ml[(w * G + tid) * 2 + 1];
+    }
+    ml[2 * tid] = M;
+    ml[2 * tid + 1] = l;
+  }
+}
+
 template <int D, int FMT>
 struct ChunkRegs {
   static constexpr int VEC = D / 128;  // 16-byte 4-bit K vectors per lane and token
@@ -271,7 +327,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   using Dec = Decoder<D, FMT>;
   using Regs = typename Dec::Regs;
   constexpr int VEC = Dec::VEC, VW = Dec::VW, KCH = Dec::KCH, VT = Dec::VT;
-  extern __shared__ float smem[];  // [G][D] partial o, then [kWaves][G] (m, l)
+  extern __shared__ float smem[];  // [kWaves][G][D] partial o, then [kWaves][G] (m, l)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: the page walk stays scalar
@@ -662,65 +718,30 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
     for (int t = 0; t < VT; t++) {
 #pragma unroll
-      for (int rr = 0; rr < 4; rr++) oacc[t][rr] += __shfl_xor(oacc[t][rr], 8, 64);
+      for (int rr = 0; rr < 4; rr++) oacc[t][rr] = add_xor8(oacc[t][rr]);
     }
   }
-  float* sm_o = smem;              // [G][D]: the waves' o, accumulated in wave order
-  float* sm_ml = smem + G * D;     // [kWaves][G][2]
-  if (j == 0 && n < G) {
-    sm_ml[(wave * G + n) * 2] = m_run;
-    sm_ml[(wave * G + n) * 2 + 1] = l_run;
-  }
-  __syncthreads();
-  float scale_o = 0.0f;
+  float* sm_o = smem;                        // [kWaves][G][D]: each wave's o
+  float* sm_ml = smem + kWaves * G * D;      // [kWaves][G][2]
   if (n < G) {
-    float M = -__builtin_inff();
+    if (j == 0) {
+      sm_ml[(wave * G + n) * 2] = m_run;
+      sm_ml[(wave * G + n) * 2 + 1] = l_run;
+    }
+    // O^T tile t, row 4j + rr <-> channel (4j + rr) * (D/16) + t
+    float* dst = sm_o + (wave * G + n) * D;
 #pragma unroll
-    for (int w = 0; w < kWaves; w++) M = fmaxf(M, sm_ml[(w * G + n) * 2]);
-    scale_o = m_run == -__builtin_inff() ? 0.0f : exp2f(m_run - M) * (FMT != FMT_INT4 ? p.gs[1] : 1.0f);
-  }
+    for (int rr = 0; rr < 4; rr++) {
+      float* row = dst + (4 * j + rr) * VT;
 #pragma unroll
-  for (int w = 0; w < kWaves; w++) {
-    if (wave == w && n < G) {
-      float* dst = sm_o + n * D;
-      // O^T tile t, row 4j + rr <-> channel (4j + rr) * (D/16) + t
-#pragma unroll
-      for (int rr = 0; rr < 4; rr++) {
-        float* row = dst + (4 * j + rr) * VT;
-#pragma unroll
-        for (int t = 0; t < VT; t += 4) {
-          // INT4: odd tiles were accumulated from values times 16
-          const float so = FMT == FMT_INT4 ? scale_o * 0.0625f : scale_o;
-          float4 x = make_float4(oacc[t][rr] * scale_o, oacc[t + 1][rr] * so, oacc[t + 2][rr] * scale_o,
-                                 oacc[t + 3][rr] * so);
-          if (w > 0) {
-            const float4 y = *(float4*)(row + t);
-            x.x += y.x;
-            x.y += y.y;
-            x.z += y.z;
-            x.w += y.w;
-          }
-          *(float4*)(row + t) = x;
-        }
+      for (int t = 0; t < VT; t += 4) {
+        // INT4: odd tiles were accumulated from values times 16
+        const float od = FMT == FMT_INT4 ? 0.0625f : 1.0f;
+        *(float4*)(row + t) = make_float4(oacc[t][rr], oacc[t + 1][rr] * od, oacc[t + 2][rr], oacc[t + 3][rr] * od);
       }
     }
-    __syncthreads();
   }
-  for (int i = threadIdx.x; i < G * D; i += 64 * kWaves) po[i] = sm_o[i];
-  if (threadIdx.x < G) {
-    const int q = threadIdx.x;
-    float M = -__builtin_inff();
-#pragma unroll
-    for (int w = 0; w < kWaves; w++) M = fmaxf(M, sm_ml[(w * G + q) * 2]);
-    float l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; w++) {
-      const float mw = sm_ml[(w * G + q) * 2];
-      if (mw != -__builtin_inff()) l += exp2f(mw - M) * sm_ml[(w * G + q) * 2 + 1];
-    }
-    ml[2 * q] = M;
-    ml[2 * q + 1] = l;
-  }
+  finish_partial<D>(sm_o, sm_ml, G, FMT != FMT_INT4 ? p.gs[1] : 1.0f, po, ml);
 }
 
 // ---------------------------------------------------------------- FP8 comparator
@@ -934,58 +955,21 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
     for (int t = 0; t < VT; t++) {
 #pragma unroll
-      for (int rr = 0; rr < 4; rr++) oacc[t][rr] += __shfl_xor(oacc[t][rr], 8, 64);
+      for (int rr = 0; rr < 4; rr++) oacc[t][rr] = add_xor8(oacc[t][rr]);
     }
   }
-  float* sm_o = smem;
-  float* sm_ml = smem + G * D;
-  if (j == 0 && n < G) {
-    sm_ml[(wave * G + n) * 2] = m_run;
-    sm_ml[(wave * G + n) * 2 + 1] = l_run;
-  }
-  __syncthreads();
-  float scale_o = 0.0f;
+  float* sm_o = smem;                    // [kWaves][G][D]: each wave's o
+  float* sm_ml = smem + kWaves * G * D;  // [kWaves][G][2]
   if (n < G) {
-    float M = -__builtin_inff();
-#pragma unroll
-    for (int w = 0; w < kWaves; w++) M = fmaxf(M, sm_ml[(w * G + n) * 2]);
-    scale_o = m_run == -__builtin_inff() ? 0.0f : exp2f(m_run - M) * p.gs[1];
-  }
-#pragma unroll
-  for (int w = 0; w < kWaves; w++) {
-    if (wave == w && n < G) {
-      float* dst = sm_o + n * D + 4 * j;
-#pragma unroll
-      for (int t = 0; t < VT; t++) {
-        float4 x = make_float4(oacc[t][0] * scale_o, oacc[t][1] * scale_o, oacc[t][2] * scale_o,
-                               oacc[t][3] * scale_o);
-        if (w > 0) {
-          const float4 y = *(float4*)(dst + 16 * t);
-          x.x += y.x;
-          x.y += y.y;
-          x.z += y.z;
-          x.w += y.w;
-        }
-        *(float4*)(dst + 16 * t) = x;
-      }
+    if (j == 0) {
+      sm_ml[(wave * G + n) * 2] = m_run;
+      sm_ml[(wave * G + n) * 2 + 1] = l_run;
     }
-    __syncthreads();
-  }
-  for (int i = threadIdx.x; i < G * D; i += 64 * kWaves) po[i] = sm_o[i];
-  if (threadIdx.x < G) {
-    const int q = threadIdx.x;
-    float M = -__builtin_inff();
+    float* dst = sm_o + (wave * G + n) * D + 4 * j;
 #pragma unroll
-    for (int w = 0; w < kWaves; w++) M = fmaxf(M, sm_ml[(w * G + q) * 2]);
-    float l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; w++) {
-      const float mw = sm_ml[(w * G + q) * 2];
-      if (mw != -__builtin_inff()) l += exp2f(mw - M) * sm_ml[(w * G + q) * 2 + 1];
-    }
-    ml[2 * q] = M;
-    ml[2 * q + 1] = l;
+    for (int t = 0; t < VT; t++) *(float4*)(dst + 16 * t) = make_float4(oacc[t][0], oacc[t][1], oacc[t][2], oacc[t][3]);
   }
+  finish_partial<D>(sm_o, sm_ml, G, p.gs[1], po, ml);
 }
 
 // Merge the splits of one (sequence, query head): M = max m_s,
@@ -1131,9 +1115,47 @@ hipError_t decode_scratch(void** ptr) {
   return hipSuccess;
 }
 
+// LDS of a decode workgroup: each wave's [G][D] o and its G (m, l) pairs.
+static size_t decode_lds_bytes(int G, int head_dim) { return (size_t)kWaves * G * (head_dim + 2) * sizeof(float); }
+
+// Above 64 KiB (16 query heads per KV head at head dim 256) the kernels need
+// the larger dynamic-LDS limit: set once per device for every instantiation.
+static hipError_t decode_lds_limit() {
+  static std::once_flag once[kScratchMaxDevices];
+  static hipError_t result[kScratchMaxDevices];
+  const int bytes = (int)decode_lds_bytes(16, 256);
+  const void* kernels[] = {
+      (const void*)decode_kernel<256, FMT_NVFP4, true>, (const void*)decode_kernel<256, FMT_NVFP4, false>,
+      (const void*)decode_kernel<256, FMT_INT4, true>,  (const void*)decode_kernel<256, FMT_INT4, false>,
+      (const void*)decode_kernel<256, FMT_K8V4, true>,  (const void*)decode_kernel<256, FMT_K8V4, false>,
+      (const void*)decode_kernel<128, FMT_NVFP4, true>, (const void*)decode_kernel<128, FMT_NVFP4, false>,
+      (const void*)decode_kernel<128, FMT_INT4, true>,  (const void*)decode_kernel<128, FMT_INT4, false>,
+      (const void*)decode_kernel<128, FMT_K8V4, true>,  (const void*)decode_kernel<128, FMT_K8V4, false>,
+      (const void*)decode_fp8_kernel<256, true>,        (const void*)decode_fp8_kernel<256, false>,
+      (const void*)decode_fp8_kernel<128, true>,        (const void*)decode_fp8_kernel<128, false>};
+  auto set_all = [&]() {
+    for (const void* k : kernels) {
+      const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  };
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchMaxDevices) {
+    (void)hipGetLastError();
+    return set_all();
+  }
+  std::call_once(once[dev], [&] { result[dev] = set_all(); });
+  return result[dev];
+}
+
 hipError_t launch_decode(const DecodeParams& p, int fmt, int head_dim, hipStream_t stream) {
   const dim3 grid(p.num_splits, p.num_kv_heads, p.batch), block(64 * kWaves);
-  const size_t lds = (size_t)p.group * (head_dim + 2 * kWaves) * sizeof(float);
+  const size_t lds = decode_lds_bytes(p.group, head_dim);
+  if (lds > 65536) {
+    const hipError_t e = decode_lds_limit();
+    if (e != hipSuccess) return e;
+  }
   const int64_t munits = (int64_t)p.batch * p.num_q_heads * (head_dim / 64);
   const bool narrow = p.num_splits <= kMergePre;
   const dim3 mgrid = narrow ? dim3((unsigned)((munits + 3) / 4)) : dim3(p.num_q_heads * (head_dim / 64), p.batch);

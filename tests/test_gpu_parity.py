@@ -44,6 +44,9 @@ SWEEP = [
     (2, 256, 1, 3, 48, [200], "lognormal", torch.float32, (1.0, 1.0)),
     (2, 128, 2, 8, 16, [31, 32, 33], "outliers", torch.bfloat16, (1.0, 1.0)),
     (2, 128, 1, 16, 32, [97], "student_t", torch.float32, (1.0, 1.0)),
+    # 16 query heads per KV head at head dim 256: the largest decode workgroup
+    # LDS (four waves' [16][256] partial o), above the default 64 KiB limit
+    (2, 256, 2, 16, 16, [77, 300], "student_t", torch.bfloat16, (1.0, 1.0)),
     # per-token scales over 33 binades: INT4's bound of the running max by the
     # value scale's exponent (p times the scale stays in fp16), NVFP4 block
     # scales that underflow or saturate E4M3 token by token

@@ -9,12 +9,16 @@
 // attends causally to keys 0 .. prefix_len + i.
 //
 // Structure: the (chunk token, query head) pairs of one KV head are flattened
-// into query rows r = i * G + h; a workgroup of 4 wavefronts takes 64
+// into query rows r = i * G + h; a workgroup of 8 wavefronts takes 128
 // consecutive rows (16 per wavefront, the MFMA's column dimension) and walks
-// the keys its rows can see in 32-token steps.  Each step's K rows and
-// transposed V rows are staged once in LDS (double-buffered, the next step's
-// global loads in flight in registers -- two steps' on the paged variant's
-// prefix steps) and read by all 4 wavefronts:
+// the keys its rows can see in 32-token steps.  Each step's K rows and V
+// rows are staged once in LDS and read by all 8 wavefronts.  LDS holds four
+// steps (step s in buffer s mod 4): one step is computed while the next is
+// staged, its global loads in flight in registers; on the paged variant's
+// prefix steps, two steps are computed per barrier while the next two are
+// staged, from two sets of loads issued a pair of steps ahead.  At head dim
+// 256 the workgroup fills a compute unit (two wavefronts per SIMD, 140 KB of
+// LDS), so every wavefront of the unit shares one staging:
 //   QK  S^T[token][row] = K[token][ch] Q^T[ch][row] on v_mfma_f32_16x16x32_bf16
 //       (bf16 K and q exactly, fp32 accumulation);
 //   online softmax in base 2 per row, lazily rescaled as in decode;
@@ -44,8 +48,10 @@ namespace kvq {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kExtRows = 64;   // query rows per workgroup, 16 per wavefront
+constexpr int kExtThreads = 512;  // 8 wavefronts per workgroup
+constexpr int kExtRows = 128;     // query rows per workgroup, 16 per wavefront
 constexpr int kExtStep = 32;   // key tokens per step
+constexpr int kExtBufs = 4;    // staged steps in LDS (step s in buffer s mod 4)
 constexpr int kExtFlush = 32;  // steps an MFMA accumulator runs before it is added into the total
 static constexpr float kExtLog2e = 1.4426950408889634f;
 static constexpr float kExtLn2 = 0.6931471805599453f;
@@ -66,7 +72,7 @@ struct ExtLds {
   static constexpr int KB = kExtStep * KPD * 4;
   static constexpr int VB = KB;
   static constexpr int BUF = KB + VB + 2 * kExtStep * 4;  // + per-token K and V factors
-  static constexpr int TOTAL = 2 * BUF;
+  static constexpr int TOTAL = kExtBufs * BUF;
 };
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -75,14 +81,14 @@ typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
 constexpr int kExtWorkspace = 0;  // SRC: every key from the bf16 workspace (else the cache format)
 
 template <int D, int SRC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void extend_kernel(const ExtendParams p) {
+__global__ __launch_bounds__(kExtThreads) __attribute__((amdgpu_waves_per_eu(2))) void extend_kernel(const ExtendParams p) {
   using Lds = ExtLds<D>;
   constexpr bool PAGED = SRC != kExtWorkspace;
   constexpr int KCH = D / 32, VT = D / 16;
-  constexpr int KV16 = D / 64;       // 16-byte K vectors per thread and step
+  constexpr int KV16 = D / 128;      // 16-byte K vectors (staging passes) per thread and step
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane >> 4, n = lane & 15;
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin in launch
   // order, so launch index w runs on XCD w mod 8.  Remapping w to the logical
@@ -176,27 +182,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   const float sm = p.sm_scale * kExtLog2e;
   const float slack_raw = kExtSlack / sm, inv_sm = 1.0f / sm;
 
-  // ---- staging.  K, workspace variant: pass v (< KV16) of thread t loads
-  // 16-byte segment kseg of row krow0 + v * KRP (a wavefront reads whole rows,
-  // 512 contiguous bytes per half-wavefront at head dim 256; LDS writes as
-  // fast as a linear store).  K, paged variant: thread t takes the D/8
-  // elements from kseg * D/8 of one row, krow0 (one page lookup and one code
-  // load per row and step; at head dim 256 a quarter-wavefront covers 4 rows x
-  // 4 segments).  V rows are staged exactly like K rows.
-  constexpr int KSEG = PAGED ? 8 : D / 8, KRP = 256 / KSEG;
-  const int krow0 = PAGED ? (D == 256 ? ((tid >> 2) & 3) + 4 * (tid >> 5) : tid >> 3) : tid / KSEG;
-  const int kseg = PAGED ? (D == 256 ? (tid & 3) + 4 * ((tid >> 4) & 1) : tid & 7) : tid % KSEG;
-  // bit position of this thread's first NVFP4 block-scale byte in the dword
-  // load_paged_row reads
-  const int nv_sshift = D == 256 ? 16 * (kseg & 1) : 8 * (kseg & 3);
+  // ---- staging.  A quarter-wavefront writes 256 contiguous bytes of one
+  // staged row per pass, which is conflict-free whatever the row's offset.
+  // Workspace variant: pass v (< KV16) of thread t loads 16-byte segment kseg
+  // of row krow0 + v * KRP (a wavefront reads whole rows).  Paged variant: 16
+  // threads per row, one row per thread (one page lookup per row and step):
+  // thread (krow0, kseg) takes the 8 elements from 8 kseg + v D/2 in pass v,
+  // i.e. one 4-byte code word and (NVFP4) one E4M3 block scale per pass.
+  // V rows are staged exactly like K rows.
+  constexpr int KSEG = PAGED ? 16 : D / 8, KRP = kExtThreads / KSEG;
+  const int krow0 = tid / KSEG, kseg = tid % KSEG;
+  // bit position of this thread's NVFP4 block-scale byte (block kseg / 2 +
+  // v D/32) in the aligned dword load_paged_row reads
+  const int nv_sshift = 8 * ((kseg >> 1) & 3);
   // row and first element of pass v
   auto krow_of = [&](int v) { return PAGED ? krow0 : krow0 + v * KRP; };
-  auto kel_of = [&](int v) { return PAGED ? kseg * (D / 8) + 8 * v : 8 * kseg; };
+  auto kel_of = [&](int v) { return PAGED ? 8 * kseg + (D / 2) * v : 8 * kseg; };
   const int64_t Lp = p.prefix_len;
   // bf16 rows: the workspace holds every token; the paged variant's rows are the chunk's
   const int64_t row_base = PAGED ? Lp : 0;
-  // staged rows in flight: bf16 values, or for a paged prefix row its raw
-  // code words (reg[0]) and scale word (reg[1].x), expanded to bf16 in lstore
+  // staged rows in flight: bf16 values, or for a paged prefix row per pass
+  // its raw code word (reg[v].x) and scale word (reg[v].y), expanded in lstore
   u32x4_t kreg[KV16], vreg[KV16];
   // bf16 rows through buffer descriptors rebased per step (uniform, scalar
   // math); the record count ends at row Lk, so rows past the end read zeros,
@@ -230,36 +236,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   };
   // the page holding this thread's row of a step, read from the page table
   // one step before the step's codes are loaded, so the code loads never wait
-  // for it
+  // for it.  A branch-free buffer load whose record count ends at the
+  // prefix's last page: a slot past it reads 0 (page 0, whose rows then go
+  // unused), so the load counter sees the same loads on every path and its
+  // waits stay exact.
+  const __amdgpu_buffer_rsrc_t pages_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.pages, (short)0, PAGED ? (int)min(4 * ((Lp + p.page_size - 1) / p.page_size), (int64_t)0x7FFFFFF0) : 0,
+      0x00020000);
   auto page_id = [&](int step) -> int {
-    const int64_t t0 = (int64_t)step * kExtStep;
-    if (!PAGED || step >= nsteps || t0 + krow0 >= Lp) return 0;
+    if (!PAGED) return 0;
+    const int64_t t0 = min((int64_t)step * kExtStep, (int64_t)0x7FFFFFC0);
     int off;
-    return ld_global<int32_t>(p.pages + page_slot(t0, off));
+    return __builtin_amdgcn_raw_buffer_load_b32(pages_rsrc, 4 * page_slot(t0, off), 0, 0);
   };
-  // a prefix row's staging registers, K (kv 0) or V (kv 1): the row's D/8
-  // elements from kseg * D/8 as D/16 code bytes, and D/128 E4M3 block scales
-  // (NVFP4) or the fp32 row scale (INT4), kept raw
+  // a prefix row's staging registers, K (kv 0) or V (kv 1): per pass the
+  // code word of the pass's 8 elements and the aligned dword holding their
+  // E4M3 block scale (NVFP4; shifted by nv_sshift where used -- a narrower
+  // load's zero extension would be an instruction on the loaded value, and
+  // waiting for it a stall) or the row's fp32 scale (INT4), kept raw
   auto load_paged_row = [&](u32x4_t(&reg)[KV16], int kv, int64_t t0, int pid) {
     int off;
     (void)page_slot(t0, off);
     const uint8_t* sl = p.pool + ((int64_t)pid * p.num_kv_heads + g) * p.slab + kv * p.half;
-    const uint8_t* cp = sl + (int64_t)off * (D / 2) + kseg * (D / 16);
-    if (D == 256) {
-      reg[0] = ld_global<u32x4_t>(cp);
-    } else {
-      const u32x2_t w = ld_global<u32x2_t>(cp);
-      reg[0].x = w.x;
-      reg[0].y = w.y;
-    }
+    const uint8_t* cp = sl + (int64_t)off * (D / 2) + 4 * kseg;
     const uint8_t* sc = sl + p.scales_off;
-    // NVFP4: the aligned dword holding the row's scale bytes, shifted by
-    // nv_sshift where used (a narrower load's zero extension would be an
-    // instruction on the loaded value, and waiting for it a stall)
-    if (SRC == FMT_NVFP4)
-      reg[1].x = ld_global<uint32_t>(sc + (int64_t)off * (D / 16) + ((D == 256 ? 2 * kseg : kseg) & ~3));
-    else
-      reg[1].x = ld_global<uint32_t>(sc + (int64_t)off * 4);
+#pragma unroll
+    for (int v = 0; v < KV16; v++) {
+      reg[v].x = ld_global<uint32_t>(cp + (D / 4) * v);
+      if (SRC == FMT_NVFP4)
+        reg[v].y = ld_global<uint32_t>(sc + (int64_t)off * (D / 16) + (((kseg >> 1) + (D / 32) * v) & ~3));
+      else
+        reg[v].y = ld_global<uint32_t>(sc + (int64_t)off * 4);
+    }
   };
   // the loads of a step whose rows all lie in the prefix: no branch between
   // page and bf16 rows, so the loads land in their staging registers (a
@@ -274,7 +282,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     const __amdgpu_buffer_rsrc_t rs = rows_rsrc(kv ? p.v : p.k, t0);
 #pragma unroll
     for (int v = 0; v < KV16; v++)
-      reg[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, kvo + (PAGED ? 16 * v : v * KRP * rowb), 0, 0);
+      reg[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, kvo + (PAGED ? D * v : v * KRP * rowb), 0, 0);
   };
   auto gload = [&](int step, int pid) {
     const int64_t t0 = (int64_t)step * kExtStep;
@@ -323,18 +331,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     auto stage = [&](u32x4_t(&reg)[KV16], int kv) {
       if (PAGED) {
         const bool pg = t0 + krow0 < Lp;
-        const u32x4_t raw = reg[0];
-        const uint32_t sw = reg[1].x;  // read before the expansion overwrites them
+        const uint32_t rs = reg[0].y;  // INT4 row scale, read before the expansion overwrites it
         if (pg) {
-          const uint32_t cw[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
           for (int v = 0; v < KV16; v++) {
             uint32_t o[4];
-            expand8(cw[v], SRC == FMT_NVFP4 ? e4m3_decode((sw >> (nv_sshift + 8 * (v / 2))) & 0xFFu) : 1.0f, o);
+            expand8(reg[v].x, SRC == FMT_NVFP4 ? e4m3_decode((reg[v].y >> nv_sshift) & 0xFFu) : 1.0f, o);
             reg[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
           }
         }
-        if (kseg == 0) fac[kv * kExtStep + krow0] = pg ? (SRC == FMT_NVFP4 ? gsf[kv] : as_f32(sw)) : 1.0f;
+        if (kseg == 0) fac[kv * kExtStep + krow0] = pg ? (SRC == FMT_NVFP4 ? gsf[kv] : as_f32(rs)) : 1.0f;
       }
       uint8_t* rbase = base + kv * Lds::KB;
 #pragma unroll
@@ -356,18 +362,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     uint8_t* base = lds + buf * Lds::BUF;
     float* fac = (float*)(base + Lds::KB + Lds::VB);
     auto stage = [&](u32x4_t(&reg)[KV16], int kv) {
-      const u32x4_t raw = reg[0];
-      const uint32_t sw = reg[1].x;
-      const uint32_t cw[4] = {raw.x, raw.y, raw.z, raw.w};
+      const uint32_t rs = reg[0].y;  // INT4 row scale
 #pragma unroll
       for (int v = 0; v < KV16; v++) {
+        const uint32_t cw = reg[v].x;
         if constexpr (SRC == FMT_NVFP4) {
-          const uint32_t hb = e4m3_to_h_x2m8(sw >> (nv_sshift + 8 * (v / 2)));
+          const uint32_t hb = e4m3_to_h_x2m8(reg[v].y >> nv_sshift);
           const half2_t s2 = u32_as_h2(hb | (hb << 16));
-          reg[v] = (u32x4_t){h2_as_u32(e2m1x2_to_h2_x256<0>(cw[v]) * s2), h2_as_u32(e2m1x2_to_h2_x256<1>(cw[v]) * s2),
-                             h2_as_u32(e2m1x2_to_h2_x256<2>(cw[v]) * s2), h2_as_u32(e2m1x2_to_h2_x256<3>(cw[v]) * s2)};
+          reg[v] = (u32x4_t){h2_as_u32(e2m1x2_to_h2_x256<0>(cw) * s2), h2_as_u32(e2m1x2_to_h2_x256<1>(cw) * s2),
+                             h2_as_u32(e2m1x2_to_h2_x256<2>(cw) * s2), h2_as_u32(e2m1x2_to_h2_x256<3>(cw) * s2)};
         } else {
-          const uint32_t w = cw[v], w4 = w >> 4;
+          const uint32_t w = cw, w4 = w >> 4;
           uint32_t o[4];
 #pragma unroll
           for (int k = 0; k < 4; k++) {
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
           reg[v] = (u32x4_t){o[0], o[1], o[2], o[3]};
         }
       }
-      if (SRC == FMT_INT4 && kseg == 0) fac[kv * kExtStep + krow0] = as_f32(sw);
+      if (SRC == FMT_INT4 && kseg == 0) fac[kv * kExtStep + krow0] = as_f32(rs);
       uint8_t* rbase = base + kv * Lds::KB;
 #pragma unroll
       for (int v = 0; v < KV16; v++)
@@ -423,14 +428,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     constexpr bool F16 = decltype(f16_tag)::value;
     const uint8_t* kb = lds + buf * Lds::BUF;
     const uint8_t* vrows = kb + Lds::KB;
+    // the two 16-token halves are independent accumulation chains: their
+    // products alternate, so neither waits on its own previous product
     float4_t sacc[2];
+    sacc[0] = sacc[1] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int hh = 0; hh < 2; hh++) {
-      sacc[hh] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-      const uint8_t* krow_p = kb + (16 * hh + n) * Lds::KPD * 4 + 16 * j;
+    for (int m = 0; m < KCH; m++) {
 #pragma unroll
-      for (int m = 0; m < KCH; m++) {
-        const u32x4_t a = *(const u32x4_t*)(krow_p + 64 * m);
+      for (int hh = 0; hh < 2; hh++) {
+        const u32x4_t a = *(const u32x4_t*)(kb + (16 * hh + n) * Lds::KPD * 4 + 16 * j + 64 * m);
         if constexpr (F16)
           sacc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
                                                             __builtin_bit_cast(half8_t, qw[m]), sacc[hh], 0, 0, 0);
@@ -439,6 +445,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
                                                              __builtin_bit_cast(bf16x8_t, qw[m]), sacc[hh], 0, 0, 0);
       }
     }
+    // operand reads four products ahead of the products that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KCH - 4; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     float s[8], vf[8], cand[8];
     const float* kfac = (const float*)(kb + Lds::KB + Lds::VB);
     const float* vfac = kfac + kExtStep;
@@ -551,9 +565,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   auto advance = [&](int st) {
     if (st + 1 < nsteps) {
       if (F16P && st + 1 < nsteps16)
-        lstore16(kreg, vreg, (st + 1) & 1);
+        lstore16(kreg, vreg, (st + 1) & 3);
       else
-        lstore((st + 1) & 1, (int64_t)(st + 1) * kExtStep);
+        lstore((st + 1) & 3, (int64_t)(st + 1) * kExtStep);
       if (st + 2 < nsteps) {
         gload(st + 2, pid);
         pid = page_id(st + 3);
@@ -561,39 +575,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     }
     __syncthreads();
   };
-  // the same while step st + 2 is a prefix step too
-  // Prefix steps with two steps of loads in flight: a second staging set
-  // (kreg2, vreg2) alternates with the first, so the loads of step st + 3
-  // issued in step st are staged two steps later; each set's page entries are
+  // Prefix steps, two per barrier: steps st and st + 1 are computed from
+  // buffers st and st + 1 (mod 4) while steps st + 2 and st + 3 are staged
+  // into the other two, from two staging sets (kreg, vreg; kreg2, vreg2)
+  // whose loads -- steps st + 4 and st + 5 -- are issued right after, so a
+  // set's loads have a pair of steps to land.  Each set's page entries are
   // fetched a pair of steps ahead (pid_a, pid_b), so that waiting for them
   // never waits for the other set's loads (the load counter is in order).
-  // Entering at st = 0: the first set holds step 1, the second step 2,
-  // pid_a the page of step 3 and pid_b that of step 4.
   u32x4_t kreg2[KV16], vreg2[KV16];
   int st = 0;
   if constexpr (F16P) {
-    if (nsteps16 > 4) {
-      gload16(kreg2, vreg2, 2, pid);
-      int pid_a = page_id(3), pid_b = page_id(4);
-      for (; st + 4 < nsteps16; st += 2) {
-        compute(std::true_type{}, st & 1, (int64_t)st * kExtStep);
-        lstore16(kreg, vreg, (st + 1) & 1);
-        gload16(kreg, vreg, st + 3, pid_a);
-        pid_a = page_id(st + 5);
-        __syncthreads();
-        compute(std::true_type{}, (st + 1) & 1, (int64_t)(st + 1) * kExtStep);
+    if (nsteps16 > 6) {
+      // entering: buffer 0 holds step 0, the first set the loads of step 1
+      lstore16(kreg, vreg, 1);
+      gload16(kreg, vreg, 2, pid);
+      gload16(kreg2, vreg2, 3, page_id(3));
+      int pid_a = page_id(4), pid_b = page_id(5);
+      __syncthreads();
+      // the two wavefronts of a SIMD (w and w + 4) take the pair in opposite
+      // orders -- stage then compute, compute then stage -- so one's
+      // conversions overlap the other's products instead of both queuing for
+      // the matrix core at once
+      const bool stage_first = wave >= 4;
+      auto stage_pair = [&](int st) {
+        lstore16(kreg, vreg, (st + 2) & 3);
+        gload16(kreg, vreg, st + 4, pid_a);
+        pid_a = page_id(st + 6);
+        lstore16(kreg2, vreg2, (st + 3) & 3);
+        gload16(kreg2, vreg2, st + 5, pid_b);
+        pid_b = page_id(st + 7);
+      };
+      for (; st + 5 < nsteps16; st += 2) {
+        if (stage_first) stage_pair(st);
+        compute(std::true_type{}, st & 3, (int64_t)st * kExtStep);
+        compute(std::true_type{}, (st + 1) & 3, (int64_t)(st + 1) * kExtStep);
         if ((st + 2) % kExtFlush == 0) flush();  // st is even and kExtFlush a multiple of 2
-        lstore16(kreg2, vreg2, st & 1);
-        gload16(kreg2, vreg2, st + 4, pid_b);
-        pid_b = page_id(st + 6);
+        if (!stage_first) stage_pair(st);
         __syncthreads();
       }
-      // back to one set: the first holds step st + 1; the page of step st + 2
-      // is looked up again (the second set's step st + 2 is reloaded)
+      // back to one set: step st is computed here, step st + 1 is staged and
+      // the first set holds the loads of step st + 2 (the second set's step
+      // st + 3 is dropped and loaded again)
+      compute(std::true_type{}, st & 3, (int64_t)st * kExtStep);
+      if ((st + 1) % kExtFlush == 0) flush();
+      st++;
       pid = page_id(st + 2);
     }
     for (; st < nsteps16; st++) {
-      compute(std::true_type{}, st & 1, (int64_t)st * kExtStep);
+      compute(std::true_type{}, st & 3, (int64_t)st * kExtStep);
       if ((st + 1) % kExtFlush == 0) flush();
       advance(st);
     }
@@ -612,20 +641,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   // (a conditional load would again need a register merge)
   const int st_chunk = PAGED ? (int)((Lp + kExtStep - 1) / kExtStep) : 0;  // first step with no prefix row
   for (; st < nsteps && (!PAGED || st + 2 < st_chunk); st++) {
-    compute(std::false_type{}, st & 1, (int64_t)st * kExtStep);
+    compute(std::false_type{}, st & 3, (int64_t)st * kExtStep);
     if ((st + 1) % kExtFlush == 0) flush();
     advance(st);
   }
   if constexpr (PAGED) {
     for (; st + 2 < nsteps; st++) {
-      compute(std::false_type{}, st & 1, (int64_t)st * kExtStep);
+      compute(std::false_type{}, st & 3, (int64_t)st * kExtStep);
       if ((st + 1) % kExtFlush == 0) flush();
-      lstore((st + 1) & 1, (int64_t)(st + 1) * kExtStep);
+      lstore((st + 1) & 3, (int64_t)(st + 1) * kExtStep);
       gloadc(st + 2);
       __syncthreads();
     }
     for (; st < nsteps; st++) {
-      compute(std::false_type{}, st & 1, (int64_t)st * kExtStep);
+      compute(std::false_type{}, st & 3, (int64_t)st * kExtStep);
       if ((st + 1) % kExtFlush == 0) flush();
       advance(st);
     }
@@ -656,7 +685,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
     p.lse[(int64_t)irow * p.lse_stride + h] = l_run > 0.0f ? (m_run * sm + log2f(l_run)) * kExtLn2 : -__builtin_inff();
 }
 
-// The double-buffered staging (74 KB at head dim 256) is above HIP's default
+// The four staging buffers (140 KB at head dim 256) are above HIP's default
 // 64 KB dynamic-LDS limit per workgroup (gfx950 has 160 KB per CU), so each
 // instantiation raises its limit -- once per device, on its first launch
 // there, not on every launch (a host call that a captured graph would
@@ -683,7 +712,7 @@ static hipError_t extend_lds_limit() {
 template <int D, int SRC>
 static hipError_t launch_extend_t(const ExtendParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.chunk_len * p.group;
-  const dim3 grid((unsigned)((rows + kExtRows - 1) / kExtRows), (unsigned)p.num_kv_heads), block(256);
+  const dim3 grid((unsigned)((rows + kExtRows - 1) / kExtRows), (unsigned)p.num_kv_heads), block(kExtThreads);
   const hipError_t e = extend_lds_limit<D, SRC>();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((extend_kernel<D, SRC>), grid, block, ExtLds<D>::TOTAL, stream, p);

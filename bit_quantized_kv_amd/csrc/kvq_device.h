@@ -108,6 +108,24 @@ __device__ inline uint32_t quad_bcast(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, I * 0x55, 0xF, 0xF, false);
 }
 
+// x of lane l ^ m (m = 1, 2, 4 or 8) within the lane's 16-lane row, with
+// DPP moves only (no LDS round trip): quad permutations for 1 and 2, a
+// half-row mirror followed by a quad reversal for 4, a row rotation by 8
+// for 8.  m must be a compile-time constant after unrolling.
+__device__ inline float lane_xor16(float x, int m) {
+  const int v = (int)as_u32(x);
+  int r;
+  if (m == 1)
+    r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+  else if (m == 2)
+    r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+  else if (m == 4)
+    r = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false), 0x1B, 0xF, 0xF, false);
+  else
+    r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
+  return as_f32((uint32_t)r);
+}
+
 // max over lanes {l, l^16, l^32, l^48} with the gfx950 lane-swap instructions
 // (VALU only, no LDS round trip).
 __device__ inline float max_xor16_xor32(float x) {

@@ -79,7 +79,7 @@ __device__ inline void hadamard_row(float x[16], int b, float scale) {
     const bool upper = (b & m) != 0;
 #pragma unroll
     for (int e = 0; e < 16; e++) {
-      const float partner = __shfl_xor(x[e], m, 64);
+      const float partner = lane_xor16(x[e], m);
       x[e] = upper ? partner - x[e] : x[e] + partner;
     }
   }
@@ -195,33 +195,70 @@ __global__ __launch_bounds__(256) void nvfp4_store_kernel(StoreParams p) {
 
 // FP8 E4M3 with one FP32 scale per tensor (the comparator format): K rows
 // are stored by token (D bytes), V by channel (the slab's V section holds D
-// rows of page_size bytes), so thread (i, b) writes 16 contiguous K bytes or
-// 16 single V bytes page_size apart.  code = E4M3(fp32(x / s)) with the sign
-// kept, saturating at 448.
+// rows of page_size bytes).  code = E4M3(fp32(x / s)) with the sign kept,
+// saturating at 448.  Thread (i, b) holds the 16 codes of elements 16b ..
+// 16b + 15 of token i: a K row segment, one 16-byte store.  V: when the
+// workgroup's tokens come in runs of 16 that fill 16 consecutive slots of
+// one page from a multiple of 16 (chunked prefill into fresh pages), each
+// run is a 16-byte-aligned 16-byte segment of every channel row; the codes
+// go through LDS (token-major in, channel-major out) and each thread writes
+// one channel's segment with a single 16-byte store.  Other workgroups
+// (single tokens, skipped slots, unaligned runs) store V byte by byte.
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void fp8_store_kernel(StoreParams p) {
+  constexpr int NB = D / 16, TOK = 256 / NB;  // tokens per workgroup: 16 (D 256) or 32 (D 128)
+  __shared__ __attribute__((aligned(16))) uint8_t tile[TOK * D];
   const int kv = (int)blockIdx.y >= p.num_kv_heads ? 1 : 0;
   const int g = (int)blockIdx.y - kv * p.num_kv_heads;
-  const int b = threadIdx.x % (D / 16);
+  const int b = threadIdx.x % NB, il = threadIdx.x / NB;
   const int64_t i = store_token<D>(threadIdx.x);
-  if (i >= p.num_tokens) return;
-  float x[16];
-  Row16<TIn>::load((const TIn*)(kv ? p.v : p.k) + i * p.in_stride + (int64_t)g * D + 16 * b, x);
-  if (p.rotate) hadamard_row<D>(x, b, p.rot_scale);
-  const int32_t slot = p.slots[i];
-  uint32_t w[4];
-  fp8_block(x, p.gs[kv], w);
+  const bool valid = i < p.num_tokens;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  int32_t slot = -1;
+  if (valid) {
+    float x[16];
+    Row16<TIn>::load((const TIn*)(kv ? p.v : p.k) + i * p.in_stride + (int64_t)g * D + 16 * b, x);
+    if (p.rotate) hadamard_row<D>(x, b, p.rot_scale);
+    slot = p.slots[i];
+    fp8_block(x, p.gs[kv], w);
+  }
+  if (kv == 0) {
+    if (slot < 0) return;
+    const int64_t page = slot / p.page_size;
+    const int off = slot % p.page_size;
+    uint8_t* base = p.pool + (page * p.num_kv_heads + g) * p.slab;
+    *(uint4*)(base + (int64_t)off * D + 16 * b) = make_uint4(w[0], w[1], w[2], w[3]);
+    return;
+  }
+  // V (a workgroup-uniform branch): tile or scatter for the whole workgroup
+  const int run0 = il & ~15;  // first token of this thread's run of 16, in the workgroup
+  const int64_t i0 = (int64_t)blockIdx.x * TOK + run0;
+  const int32_t first = i0 < p.num_tokens ? p.slots[i0] : -1;
+  const bool in_run = valid && first >= 0 && (first & 15) == 0 && slot == first + (il - run0);
+  const bool tiled = (p.page_size & 15) == 0 && __syncthreads_and(in_run);
+  if (tiled) {
+    *(uint4*)(tile + il * D + 16 * b) = make_uint4(w[0], w[1], w[2], w[3]);
+    __syncthreads();
+    // thread t writes channel c = t % D of run t / D (the workgroup's runs
+    // are TOK / 16 = 256 / D, so every thread has one)
+    const int c = threadIdx.x % D, run = threadIdx.x / D;
+    const int32_t fs = p.slots[(int64_t)blockIdx.x * TOK + 16 * run];
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 16; k++) o[k / 4] |= (uint32_t)tile[(16 * run + k) * D + c] << (8 * (k % 4));
+    const int64_t page = fs / p.page_size;
+    const int off = fs % p.page_size;
+    uint8_t* vrow = p.pool + (page * p.num_kv_heads + g) * p.slab + (int64_t)p.page_size * D +
+                    (int64_t)c * p.page_size + off;
+    *(uint4*)vrow = make_uint4(o[0], o[1], o[2], o[3]);
+    return;
+  }
   if (slot < 0) return;
   const int64_t page = slot / p.page_size;
   const int off = slot % p.page_size;
-  uint8_t* base = p.pool + (page * p.num_kv_heads + g) * p.slab;
-  if (kv == 0) {
-    *(uint4*)(base + (int64_t)off * D + 16 * b) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
-    uint8_t* col = base + (int64_t)p.page_size * D + (int64_t)(16 * b) * p.page_size + off;
+  uint8_t* col = p.pool + (page * p.num_kv_heads + g) * p.slab + (int64_t)p.page_size * D + (int64_t)(16 * b) * p.page_size + off;
 #pragma unroll
-    for (int e = 0; e < 16; e++) col[(int64_t)e * p.page_size] = (uint8_t)(w[e / 4] >> (8 * (e % 4)));
-  }
+  for (int e = 0; e < 16; e++) col[(int64_t)e * p.page_size] = (uint8_t)(w[e / 4] >> (8 * (e % 4)));
 }
 
 // FP8 keys with NVFP4 values: K rows as in the FP8 format (by token, D bytes,
@@ -255,14 +292,43 @@ __global__ __launch_bounds__(256) void k8v4_store_kernel(StoreParams p) {
   }
 }
 
-// INT4: the D/16 threads of one row reduce the row amax with lane shuffles.
-// q = rint(RN(x / s)) with RN(x / s) from the FMA-corrected quotient; where
-// that quotient lies within two ulps of a rounding boundary (a half-integer)
-// the lane recomputes the row with IEEE division, so the codes never depend
-// on the quotient's last bit.
+// INT4 rounding of a quotient near a half-integer: rint(RN(x / s)) when
+// x / s lies within 2^-19 + 2^-20 of the half-integer h, without a division.
+// The residual d = x - h s is exact in one FMA (a multiple of 2^(e - 24) for
+// s in [2^e, 2^(e+1)), below 2^(e - 17) in magnitude: at most 7 significant
+// bits).  RN(x / s) = h exactly when |x / s - h| <= ulp(h) / 2 -- h = k + 1/2
+// has a zero last significand bit, so a midpoint rounds to h -- i.e. when
+// |d| <= s ulp(h) / 2, with the smaller ulp of the binade below on the side
+// toward zero of a power-of-two |h| (0.5); rint(h) is then the even one of
+// floor(h), ceil(h).  Otherwise RN(x / s) is on the side of h that d's sign
+// gives.
+__device__ inline float int4_near_half(float x, float s, float h) {
+  const float d = __builtin_fmaf(-h, s, x);
+  const float ah = __builtin_fabsf(h);
+  const int e = __builtin_amdgcn_frexp_exp(ah) - 1;  // ah in [2^e, 2^(e+1))
+  const bool toward_zero = (d < 0.0f) == (h > 0.0f);
+  const bool pow2 = ah == __builtin_ldexpf(1.0f, e);
+  const float half_ulp_s = __builtin_ldexpf(s, e - 24 - ((toward_zero && pow2) ? 1 : 0));
+  const float lo = __builtin_floorf(h), hi = lo + 1.0f;
+  if (__builtin_fabsf(d) <= half_ulp_s) return ((int)lo & 1) ? hi : lo;
+  return d > 0.0f ? hi : lo;
+}
+
+// INT4: the D/16 threads of one row reduce the row amax with DPP lane
+// exchanges; s = RN(amax / 7) and q = clamp(rint(RN(x / s)), -7, 7).  The
+// quotient is taken as y = RN(x RN(1 / s)): both roundings are relative
+// errors below 2^-24 and |x / s| <= 7 (1 + 2^-23), so |y - x/s| < 2^-20, and
+// RN(x / s) is within 2^-21 of x / s: where y lies farther than 2^-19 from
+// every half-integer, rint(y) = rint(RN(x / s)).  rint(y) comes from adding
+// 1.5 * 2^23 (round to nearest even), whose low mantissa bits then hold the
+// integer in two's complement -- the nibble itself.  An element closer to a
+// half-integer (bf16 inputs make exact ratios such as x = amax / 2 common)
+// is decided by int4_near_half; a row with s below 2^-100 takes IEEE
+// division.
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void int4_store_kernel(StoreParams p) {
   constexpr int NB = D / 16;
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
   const int kv = (int)blockIdx.y >= p.num_kv_heads ? 1 : 0;
   const int g = (int)blockIdx.y - kv * p.num_kv_heads;
   const int b = threadIdx.x % NB;
@@ -277,34 +343,33 @@ __global__ __launch_bounds__(256) void int4_store_kernel(StoreParams p) {
 #pragma unroll
   for (int e = 0; e < 16; e++) amax = fmaxf(amax, __builtin_fabsf(x[e]));
 #pragma unroll
-  for (int m = 1; m < NB; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, NB));
+  for (int m = 1; m < NB; m <<= 1) amax = fmaxf(amax, lane_xor16(amax, m));
   const float s = amax / 7.0f;
   uint32_t w0 = 0, w1 = 0;
   if (s != 0.0f) {
-    float n[16];
-    // below 2^-100 the residual could round; such rows take the division
-    bool exact = !(s >= 0x1p-100f);
-    if (!exact) {
+    uint32_t nib[16];
+    if (s >= 0x1p-100f) {
       const float r = 1.0f / s;
 #pragma unroll
       for (int e = 0; e < 16; e++) {
-        const float y = fma_quotient(x[e], s, r);
-        n[e] = __builtin_rintf(y);
-        exact |= __builtin_fabsf(y - n[e]) >= 0.5f - 0x1p-20f;
+        const float y = x[e] * r;
+        const float t = y + kMagic;
+        const float n = t - kMagic;
+        nib[e] = as_u32(t);
+        if (__builtin_fabsf(y - n) >= 0.5f - 0x1p-19f) {
+          const float q = int4_near_half(x[e], s, n + (y > n ? 0.5f : -0.5f));
+          nib[e] = as_u32(__builtin_amdgcn_fmed3f(q, -7.0f, 7.0f) + kMagic);
+        }
       }
-    }
-    if (exact) {
+    } else {
 #pragma unroll
-      for (int e = 0; e < 16; e++) n[e] = __builtin_rintf(x[e] / s);
+      for (int e = 0; e < 16; e++)
+        nib[e] = as_u32(__builtin_amdgcn_fmed3f(__builtin_rintf(x[e] / s), -7.0f, 7.0f) + kMagic);
     }
 #pragma unroll
-    for (int e = 0; e < 16; e++) {
-      const float c = __builtin_amdgcn_fmed3f(n[e], -7.0f, 7.0f);
-      const uint32_t nib = (uint32_t)(int)c & 0xFu;
-      if (e < 8)
-        w0 |= nib << (4 * e);
-      else
-        w1 |= nib << (4 * (e - 8));
+    for (int e = 0; e < 8; e++) {
+      w0 |= (nib[e] & 0xFu) << (4 * e);
+      w1 |= (nib[e + 8] & 0xFu) << (4 * e);
     }
   }
   if (slot < 0) return;

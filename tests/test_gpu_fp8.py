@@ -63,3 +63,40 @@ def test_fp8_every_code_round_trips():
     codes = got[0, 0, :D * n]
     expect = np.array([c for c in range(0x7F)] + [0x80 | c for c in range(0x7F)], np.uint8)
     assert np.array_equal(codes[:expect.size], expect)
+
+
+@pytest.mark.parametrize("D,P,start,n,skip", [
+    (256, 16, 0, 64, None),    # whole pages: every 16-token run goes through the tiled value store
+    (256, 32, 0, 96, None),    # runs of 16 inside 32-token pages
+    (256, 16, 8, 40, None),    # runs that start mid-way: byte-by-byte value store
+    (128, 16, 0, 64, None),    # two runs per workgroup at head dim 128
+    (128, 48, 24, 80, None),   # runs from an unaligned slot, some across a page boundary
+    (128, 16, 0, 64, 20),      # an aligned run and one with a skipped slot in one workgroup
+    (256, 16, 0, 64, 21),      # a skipped slot: that workgroup stores byte by byte
+])
+def test_fp8_value_rows_tiled_and_scattered(D, P, start, n, skip):
+    # chunked-prefill stores whose 16-token runs fill aligned slot runs of one
+    # page take the LDS-transposed value path, the others the byte scatter;
+    # both must leave the same bytes as the oracle (0xFF poison elsewhere)
+    print(f"case: fp8 value rows D {D} P {P} start {start} n {n} skip {skip}", flush=True)
+    Hkv = 2
+    g = np.random.default_rng(1000 + D + P + start)
+    k = g.standard_normal((n, Hkv, D)).astype(np.float32)
+    v = (g.standard_normal((n, Hkv, D)) * 2.0).astype(np.float32)
+    npages = -(-(start + n) // P) + 1
+    pages = g.permutation(npages).astype(np.int32)  # the sequence's pages, shuffled
+    t = np.arange(start, start + n)
+    slots = (pages[t // P] * P + t % P).astype(np.int32)
+    if skip is not None:
+        slots[skip] = -1
+    cache = kvq.Cache(3, npages, P, Hkv, D, device="cuda", global_scale=(0.05, 0.07))
+    cache.pool.fill_(0xFF)
+    kvq.kvq_quantize_store(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                           torch.from_numpy(slots).cuda())
+    ref = oracle.Pool(3, npages, P, Hkv, D, global_scale=(0.05, 0.07), fill=0xFF)
+    ref.quantize_store(k, v, slots)
+    torch.cuda.synchronize()
+    got = cache.pool.cpu().numpy().ravel()
+    want = ref.data.ravel()
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"

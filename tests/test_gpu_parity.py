@@ -189,3 +189,36 @@ def test_store_special_values(fmt, gs):
     if not np.array_equal(got, ref.data):
         diff = np.argwhere(got != ref.data)
         raise AssertionError(f"{len(diff)} bytes differ, first {diff[:5].tolist()}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_int4_store_quotients_at_half_integers(dtype):
+    # rows where many x / s land on or next to half-integers: x = amax (2k+1)/14
+    # (exactly amax / 2 among them, common with bf16 inputs) -- rint(RN(x / s))
+    # is then decided by the last bits of the quotient, ties to even; the
+    # packed codes and scales must match the oracle bit for bit
+    import oracle
+    from bit_quantized_kv_amd import kvq
+    print(f"case: int4 half-integer quotients {dtype}", flush=True)
+    D, Hkv, P, n = 256, 2, 16, 96
+    g = np.random.default_rng(77 if dtype == torch.bfloat16 else 78)
+    x = g.standard_normal((2, n, Hkv, D)).astype(np.float32)
+    amax = np.abs(x).max(axis=3, keepdims=True)
+    k_odd = g.integers(0, 7, size=x.shape) * 2 + 1
+    planted = (amax * k_odd / 14.0).astype(np.float32) * np.where(g.random(x.shape) < 0.5, -1.0, 1.0)
+    mask = g.random(x.shape) < 0.3
+    x = np.where(mask, planted, x).astype(np.float32)
+    x[..., 5] = amax[..., 0] / 2.0
+    xt = torch.from_numpy(x).to(dtype)
+    x_in = xt.float().numpy()  # the values the kernel sees
+    slots = np.arange(n, dtype=np.int32)
+    cache = kvq.Cache(2, n // P, P, Hkv, D, device="cuda")
+    cache.pool.fill_(0x5A)
+    kvq.kvq_quantize_store(cache, xt[0].cuda(), xt[1].cuda(), torch.from_numpy(slots).cuda())
+    ref = oracle.Pool(2, n // P, P, Hkv, D, fill=0x5A)
+    ref.quantize_store(x_in[0], x_in[1], slots)
+    torch.cuda.synchronize()
+    got = cache.pool.cpu().numpy().ravel()
+    want = ref.data.ravel()
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"

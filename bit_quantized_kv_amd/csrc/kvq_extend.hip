@@ -9,16 +9,18 @@
 // attends causally to keys 0 .. prefix_len + i.
 //
 // Structure: the (chunk token, query head) pairs of one KV head are flattened
-// into query rows r = i * G + h; a workgroup of 8 wavefronts takes 128
-// consecutive rows (16 per wavefront, the MFMA's column dimension) and walks
-// the keys its rows can see in 32-token steps.  Each step's K rows and V
-// rows are staged once in LDS and read by all 8 wavefronts.  LDS holds four
-// steps (step s in buffer s mod 4): one step is computed while the next is
-// staged, its global loads in flight in registers; on the paged variant's
+// into query rows r = i * G + h; a workgroup takes 16 consecutive rows per
+// wavefront (the MFMA's column dimension) -- 12 wavefronts, 192 rows, in the
+// paged variant, 8 wavefronts, 128 rows, over the workspace -- and walks the
+// keys its rows can see in 32-token steps.  Each step's K rows and V rows are
+// staged once in LDS, by the first 8 wavefronts, and read by all.  LDS holds
+// four steps (step s in buffer s mod 4): one step is computed while the next
+// is staged, its global loads in flight in registers; on the paged variant's
 // prefix steps, two steps are computed per barrier while the next two are
 // staged, from two sets of loads issued a pair of steps ahead.  At head dim
-// 256 the workgroup fills a compute unit (two wavefronts per SIMD, 140 KB of
-// LDS), so every wavefront of the unit shares one staging:
+// 256 the workgroup fills a compute unit (three wavefronts per SIMD in the
+// paged variant, two over the workspace; 140 KB of LDS), so every wavefront
+// of the unit shares one staging:
 //   QK  S^T[token][row] = K[token][ch] Q^T[ch][row] on v_mfma_f32_16x16x32_bf16
 //       (bf16 K and q exactly, fp32 accumulation);
 //   online softmax in base 2 per row, lazily rescaled as in decode;
@@ -48,8 +50,7 @@ namespace kvq {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kExtThreads = 512;  // 8 wavefronts per workgroup
-constexpr int kExtRows = 128;     // query rows per workgroup, 16 per wavefront
+constexpr int kExtStagers = 512;  // threads that stage K/V (wavefronts 0..7)
 constexpr int kExtStep = 32;   // key tokens per step
 constexpr int kExtBufs = 4;    // staged steps in LDS (step s in buffer s mod 4)
 constexpr int kExtFlush = 32;  // steps an MFMA accumulator runs before it is added into the total
@@ -80,8 +81,24 @@ typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
 
 constexpr int kExtWorkspace = 0;  // SRC: every key from the bf16 workspace (else the cache format)
 
+// Wavefronts per workgroup, 16 query rows each.  The paged variant runs 12,
+// three per SIMD: the first 8 stage and compute, the other 4 only compute,
+// and fill the issue slots where the others wait on their products and
+// operand reads (measured 5-6 % faster than 8 at head dim 256, with the
+// paged kernels held to 168 registers; their few spills sit in the bf16 and
+// single-step loops, not in the paired fp16 loop).  The workspace variant
+// (238 registers: its two-level output sums) keeps 8.
+template <int SRC>
+struct ExtCfg {
+  static constexpr int WAVES = SRC == kExtWorkspace ? 8 : 12;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int ROWS = 16 * WAVES;
+  static constexpr int WPE = WAVES / 4;
+};
+
 template <int D, int SRC>
-__global__ __launch_bounds__(kExtThreads) __attribute__((amdgpu_waves_per_eu(2))) void extend_kernel(const ExtendParams p) {
+__global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_per_eu(ExtCfg<SRC>::WPE))) void extend_kernel(const ExtendParams p) {
+  constexpr int kExtRows = ExtCfg<SRC>::ROWS;
   using Lds = ExtLds<D>;
   constexpr bool PAGED = SRC != kExtWorkspace;
   constexpr int KCH = D / 32, VT = D / 16;
@@ -190,7 +207,8 @@ __global__ __launch_bounds__(kExtThreads) __attribute__((amdgpu_waves_per_eu(2))
   // thread (krow0, kseg) takes the 8 elements from 8 kseg + v D/2 in pass v,
   // i.e. one 4-byte code word and (NVFP4) one E4M3 block scale per pass.
   // V rows are staged exactly like K rows.
-  constexpr int KSEG = PAGED ? 16 : D / 8, KRP = kExtThreads / KSEG;
+  constexpr int KSEG = PAGED ? 16 : D / 8, KRP = kExtStagers / KSEG;
+  const bool stager = wave < kExtStagers / 64;  // wave-uniform
   const int krow0 = tid / KSEG, kseg = tid % KSEG;
   // bit position of this thread's NVFP4 block-scale byte (block kseg / 2 +
   // v D/32) in the aligned dword load_paged_row reads
@@ -244,6 +262,7 @@ __global__ __launch_bounds__(kExtThreads) __attribute__((amdgpu_waves_per_eu(2))
       (void*)p.pages, (short)0, PAGED ? (int)min(4 * ((Lp + p.page_size - 1) / p.page_size), (int64_t)0x7FFFFFF0) : 0,
       0x00020000);
   auto page_id = [&](int step) -> int {
+    if (!stager) return 0;
     if (!PAGED) return 0;
     const int64_t t0 = min((int64_t)step * kExtStep, (int64_t)0x7FFFFFC0);
     int off;
@@ -273,6 +292,7 @@ __global__ __launch_bounds__(kExtThreads) __attribute__((amdgpu_waves_per_eu(2))
   // page and bf16 rows, so the loads land in their staging registers (a
   // register copy after a branch would wait for the load it copies)
   auto gload16 = [&](u32x4_t(&kr)[KV16], u32x4_t(&vr)[KV16], int step, int pid) {
+    if (!stager) return;
     const int64_t t0 = (int64_t)step * kExtStep;
     load_paged_row(kr, 0, t0, pid);
     load_paged_row(vr, 1, t0, pid);
@@ -285,6 +305,7 @@ __global__ __launch_bounds__(kExtThreads) __attribute__((amdgpu_waves_per_eu(2))
       reg[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, kvo + (PAGED ? D * v : v * KRP * rowb), 0, 0);
   };
   auto gload = [&](int step, int pid) {
+    if (!stager) return;
     const int64_t t0 = (int64_t)step * kExtStep;
     // one row's staging registers: K (kv 0) or V (kv 1)
     auto rows = [&](u32x4_t(&reg)[KV16], int kv) {
@@ -299,6 +320,7 @@ __global__ __launch_bounds__(kExtThreads) __attribute__((amdgpu_waves_per_eu(2))
   // the loads of a step whose rows all lie in the chunk (paged variant): bf16
   // rows only, no branch (as gload16 for the prefix)
   auto gloadc = [&](int step) {
+    if (!stager) return;
     const int64_t t0 = (int64_t)step * kExtStep;
     load_bf16_row(kreg, 0, t0);
     load_bf16_row(vreg, 1, t0);
@@ -326,6 +348,7 @@ __global__ __launch_bounds__(kExtThreads) __attribute__((amdgpu_waves_per_eu(2))
     }
   };
   auto lstore = [&](int buf, int64_t t0) {
+    if (!stager) return;
     uint8_t* base = lds + buf * Lds::BUF;
     float* fac = (float*)(base + Lds::KB + Lds::VB);  // [K factors][V factors], one per token
     auto stage = [&](u32x4_t(&reg)[KV16], int kv) {
@@ -359,6 +382,7 @@ __global__ __launch_bounds__(kExtThreads) __attribute__((amdgpu_waves_per_eu(2))
   // (q + 8), less 1032: q exactly, three instructions per pair; the token's
   // scale is staged as on the bf16 steps.
   auto lstore16 = [&](u32x4_t(&kr)[KV16], u32x4_t(&vr)[KV16], int buf) {
+    if (!stager) return;
     uint8_t* base = lds + buf * Lds::BUF;
     float* fac = (float*)(base + Lds::KB + Lds::VB);
     auto stage = [&](u32x4_t(&reg)[KV16], int kv) {
@@ -592,10 +616,10 @@ __global__ __launch_bounds__(kExtThreads) __attribute__((amdgpu_waves_per_eu(2))
       gload16(kreg2, vreg2, 3, page_id(3));
       int pid_a = page_id(4), pid_b = page_id(5);
       __syncthreads();
-      // the two wavefronts of a SIMD (w and w + 4) take the pair in opposite
-      // orders -- stage then compute, compute then stage -- so one's
+      // the two staging wavefronts of a SIMD (w and w + 4) take the pair in
+      // opposite orders -- stage then compute, compute then stage -- so one's
       // conversions overlap the other's products instead of both queuing for
-      // the matrix core at once
+      // the matrix core at once (w + 8, in the paged variant, only computes)
       const bool stage_first = wave >= 4;
       auto stage_pair = [&](int st) {
         lstore16(kreg, vreg, (st + 2) & 3);
@@ -712,7 +736,8 @@ static hipError_t extend_lds_limit() {
 template <int D, int SRC>
 static hipError_t launch_extend_t(const ExtendParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.chunk_len * p.group;
-  const dim3 grid((unsigned)((rows + kExtRows - 1) / kExtRows), (unsigned)p.num_kv_heads), block(kExtThreads);
+  constexpr int R = ExtCfg<SRC>::ROWS;
+  const dim3 grid((unsigned)((rows + R - 1) / R), (unsigned)p.num_kv_heads), block(ExtCfg<SRC>::THREADS);
   const hipError_t e = extend_lds_limit<D, SRC>();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((extend_kernel<D, SRC>), grid, block, ExtLds<D>::TOTAL, stream, p);

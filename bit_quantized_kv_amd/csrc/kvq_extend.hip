@@ -82,12 +82,16 @@ typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
 constexpr int kExtWorkspace = 0;  // SRC: every key from the bf16 workspace (else the cache format)
 
 // Wavefronts per workgroup, 16 query rows each.  The paged variant runs 12,
-// three per SIMD: the first 8 stage and compute, the other 4 only compute,
-// and fill the issue slots where the others wait on their products and
-// operand reads (measured 5-6 % faster than 8 at head dim 256, with the
-// paged kernels held to 168 registers; their few spills sit in the bf16 and
-// single-step loops, not in the paired fp16 loop).  The workspace variant
-// (238 registers: its two-level output sums) keeps 8.
+// three per SIMD: the first 8 stage and compute, the other 4 compute and fill
+// the issue slots where the others wait on their products and operand
+// reads.  Those 4 still issue the staging loads -- the same addresses as the
+// first 4, lines the caches already hold -- and skip only the conversions
+// and LDS writes: with the loads behind a branch, every wavefront ran one
+// load sequence or another and the compiler waited for all loads in flight
+// where the paths joined.  (Measured against 8 wavefronts, 32K prefix: NVFP4
+// 4.60 -> 4.36 ms, INT4 4.91 -> 4.51 ms; INT4 220K prefix 30.2 -> 27.5 ms.)
+// The paged kernels are held to 168 registers, with a few spills; the
+// workspace variant (238 registers: its two-level output sums) keeps 8.
 template <int SRC>
 struct ExtCfg {
   static constexpr int WAVES = SRC == kExtWorkspace ? 8 : 12;
@@ -209,7 +213,8 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
   // V rows are staged exactly like K rows.
   constexpr int KSEG = PAGED ? 16 : D / 8, KRP = kExtStagers / KSEG;
   const bool stager = wave < kExtStagers / 64;  // wave-uniform
-  const int krow0 = tid / KSEG, kseg = tid % KSEG;
+  const int stid = tid % kExtStagers;  // wavefronts 8.. load what wavefronts 0.. load, then drop it
+  const int krow0 = stid / KSEG, kseg = stid % KSEG;
   // bit position of this thread's NVFP4 block-scale byte (block kseg / 2 +
   // v D/32) in the aligned dword load_paged_row reads
   const int nv_sshift = 8 * ((kseg >> 1) & 3);
@@ -262,7 +267,6 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
       (void*)p.pages, (short)0, PAGED ? (int)min(4 * ((Lp + p.page_size - 1) / p.page_size), (int64_t)0x7FFFFFF0) : 0,
       0x00020000);
   auto page_id = [&](int step) -> int {
-    if (!stager) return 0;
     if (!PAGED) return 0;
     const int64_t t0 = min((int64_t)step * kExtStep, (int64_t)0x7FFFFFC0);
     int off;
@@ -292,7 +296,6 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
   // page and bf16 rows, so the loads land in their staging registers (a
   // register copy after a branch would wait for the load it copies)
   auto gload16 = [&](u32x4_t(&kr)[KV16], u32x4_t(&vr)[KV16], int step, int pid) {
-    if (!stager) return;
     const int64_t t0 = (int64_t)step * kExtStep;
     load_paged_row(kr, 0, t0, pid);
     load_paged_row(vr, 1, t0, pid);
@@ -305,7 +308,6 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
       reg[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, kvo + (PAGED ? D * v : v * KRP * rowb), 0, 0);
   };
   auto gload = [&](int step, int pid) {
-    if (!stager) return;
     const int64_t t0 = (int64_t)step * kExtStep;
     // one row's staging registers: K (kv 0) or V (kv 1)
     auto rows = [&](u32x4_t(&reg)[KV16], int kv) {
@@ -320,7 +322,6 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
   // the loads of a step whose rows all lie in the chunk (paged variant): bf16
   // rows only, no branch (as gload16 for the prefix)
   auto gloadc = [&](int step) {
-    if (!stager) return;
     const int64_t t0 = (int64_t)step * kExtStep;
     load_bf16_row(kreg, 0, t0);
     load_bf16_row(vreg, 1, t0);
@@ -619,7 +620,8 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
       // the two staging wavefronts of a SIMD (w and w + 4) take the pair in
       // opposite orders -- stage then compute, compute then stage -- so one's
       // conversions overlap the other's products instead of both queuing for
-      // the matrix core at once (w + 8, in the paged variant, only computes)
+      // the matrix core at once (w + 8, in the paged variant, computes; its
+      // loads repeat w's and nothing is staged from them)
       const bool stage_first = wave >= 4;
       auto stage_pair = [&](int st) {
         lstore16(kreg, vreg, (st + 2) & 3);

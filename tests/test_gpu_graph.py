@@ -1,6 +1,6 @@
 """The decode step captured in a HIP graph: quantize-store of the new token
-plus decode attention (and an extend call) recorded once with
-torch.cuda.graph, then replayed several times with eager work in between
+plus decode attention (and two extend calls: over a bf16 workspace, and fused
+over the first sequence's cached pages) recorded once with torch.cuda.graph, then replayed several times with eager work in between
 (new queries written in place); every replay must equal the eager calls on
 the same inputs bit for bit (same split plan, same kernels)."""
 import numpy as np
@@ -39,11 +39,19 @@ def test_decode_step_graph_replays_match_eager(fmt):
     vw = torch.randn((Lp + n, c.Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
     qe = torch.randn((n, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
     oe = torch.empty((n, Hq, D), dtype=torch.float32, device="cuda")
+    # the fused extend of the same chunk over sequence 0's 300 cached tokens
+    # (the step's stores go to a spare page, outside that prefix; NVFP4 and
+    # INT4 caches)
+    fused = fmt in (1, 2)
+    of = torch.zeros((n, Hq, D), dtype=torch.float32, device="cuda")
+    lf = torch.zeros((n, Hq), dtype=torch.float32, device="cuda")
 
     def step():
         kvq.kvq_quantize_store(c.cache, k_new, v_new, slots)
         kvq.kvq_decode_attention(c.cache, q, c.bt_dev, c.lens_dev, max_len, out=out, lse=lse, workspace=ws)
         kvq.kvq_extend_attention(qe, kw, vw, Lp, out=oe)
+        if fused:
+            kvq.kvq_extend_attention_paged(c.cache, c.bt_dev[0], 300, qe, kw[Lp:], vw[Lp:], out=of, lse=lf)
 
     # warm up on a side stream, as torch requires before capture
     s = torch.cuda.Stream()
@@ -63,14 +71,17 @@ def test_decode_step_graph_replays_match_eager(fmt):
         torch.cuda.synchronize()
         step()
         torch.cuda.synchronize()
-        want = (out.clone(), lse.clone(), oe.clone(), c.cache.pool.clone())
+        want = (out.clone(), lse.clone(), oe.clone(), c.cache.pool.clone(), of.clone(), lf.clone())
         out.zero_()
         lse.zero_()
         oe.zero_()
+        of.zero_()
+        lf.zero_()
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, want[0]) and torch.equal(lse, want[1]), f"replay {r}: decode differs"
         assert torch.equal(oe, want[2]), f"replay {r}: extend differs"
+        assert torch.equal(of, want[4]) and torch.equal(lf, want[5]), f"replay {r}: fused extend differs"
         assert torch.equal(c.cache.pool, want[3]), f"replay {r}: cache bytes differ"
         assert np.isfinite(out.cpu().numpy()).all()

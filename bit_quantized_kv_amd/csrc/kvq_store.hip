@@ -156,14 +156,18 @@ __device__ inline void nvfp4_block(const float x[16], float gs, uint32_t& w0, ui
 
 // FP8 E4M3 of 16 values with a per-tensor scale s: code = E4M3(fp32(x / s))
 // with the sign kept, saturating at 448; four words, element 0 in the low byte.
+// The quotient is IEEE division; the code comes from gfx950's
+// v_cvt_pk_fp8_f32 after a clamp to [-448, 448], which matches that rule for
+// every fp32 input (round to nearest, ties to the even code, the sign kept;
+// checked exhaustively), two codes per instruction.
 __device__ inline void fp8_block(const float x[16], float s, uint32_t w[4]) {
+  float y[16];
 #pragma unroll
-  for (int e = 0; e < 4; e++) w[e] = 0u;
+  for (int e = 0; e < 16; e++) y[e] = __builtin_amdgcn_fmed3f(x[e] / s, -448.0f, 448.0f);
 #pragma unroll
-  for (int e = 0; e < 16; e++) {
-    const float y = x[e] / s;
-    const uint32_t code = e4m3_encode(__builtin_fabsf(y)) | ((as_u32(y) >> 24) & 0x80u);
-    w[e / 4] |= code << (8 * (e % 4));
+  for (int k = 0; k < 4; k++) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * k], y[4 * k + 1], 0, false);
+    w[k] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * k + 2], y[4 * k + 3], lo, true);
   }
 }
 

@@ -21,7 +21,11 @@
 //     positions, against the E2M1 value set;
 //   - v_cvt_pk_f32_fp8 and v_cvt_scalef32_pk_f16_fp8 at scale 1 (E4M3 scale
 //     and FP8 value decoders): all 256 codes in both byte halves, against the
-//     OCP E4M3 definition (0x7F and 0xFF NaN).
+//     OCP E4M3 definition (0x7F and 0xFF NaN);
+//   - v_cvt_pk_fp8_f32 after a clamp to [-448, 448] (the FP8 value encoder):
+//     every fp32 bit pattern but NaN, in both bytes of both halves of the
+//     word, against round-to-nearest with ties to the even code, saturation
+//     at 448 and the sign kept.
 // A sweep writes, per workgroup, the number of mismatches and the smallest
 // mismatching input (0xFFFFFFFF if none); nothing is atomic.
 #include <hip/hip_runtime.h>
@@ -222,12 +226,62 @@ __global__ __launch_bounds__(kThreads) void fp8_decode_sweep(uint32_t* count, ui
   finish(bad, first, count, first_out);
 }
 
+// E4M3 code of fp32 bits u (not NaN), the rule of the FP8 values: the sign
+// bit kept; magnitudes of 448 and beyond (and infinity) saturate to 448
+// (0x7E); normal results (>= 2^-6) keep 3 mantissa bits, rounded to nearest
+// with ties to the even code (a carry moves into the exponent); below 2^-6
+// the subnormal codes m 2^-9, m = rint(|x| 2^9), ties to even.
+__device__ inline uint32_t e4m3_ref(uint32_t u) {
+  const uint32_t sign = (u >> 24) & 0x80u, a = u & 0x7FFFFFFFu;
+  uint32_t c;
+  if (bits_f(a) >= 448.0f) {
+    c = 0x7Eu;
+  } else if (bits_f(a) >= 0x1p-6f) {
+    const uint32_t e = (a >> 23) - 127u + 7u, m = a & 0x7FFFFFu;
+    const uint32_t q = m >> 20, rem = m & 0xFFFFFu;
+    c = (e << 3) + q + ((rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u);
+  } else {
+    c = (uint32_t)__builtin_rintf(bits_f(a) * 512.0f);  // exact scaling; rint ties to even
+  }
+  return c | sign;
+}
+
+// Every fp32 input u but NaN, clamped to [-448, 448] as the library clamps
+// before converting, in byte 0 and 1 of the low half and byte 2 and 3 of the
+// high half (the other byte of the pair holds 1.0, code 0x38; the other half
+// of the old word is kept).
+__global__ __launch_bounds__(kThreads) void fp8_encode_sweep(uint32_t* count, uint32_t* first_out) {
+  uint32_t bad = 0, first = 0xFFFFFFFFu;
+  const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
+  const float partner = 1.0f;
+  const uint32_t old = 0xC3A5E15Au;
+  for (int i = 0; i < kPerThread; i++) {
+    const uint32_t u = t + (uint32_t)i * kStride;
+    if (is_nan_bits(u)) continue;
+    const uint32_t want = e4m3_ref(u);
+    const float y = __builtin_amdgcn_fmed3f(bits_f(u), -448.0f, 448.0f);
+    const uint32_t lo0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, partner, (int)old, false);
+    const uint32_t lo1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(partner, y, (int)old, false);
+    const uint32_t hi0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, partner, (int)old, true);
+    const uint32_t hi1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(partner, y, (int)old, true);
+    const bool ok = lo0 == ((old & 0xFFFF0000u) | want | (0x38u << 8)) &&
+                    lo1 == ((old & 0xFFFF0000u) | 0x38u | (want << 8)) &&
+                    hi0 == ((old & 0xFFFFu) | (want << 16) | (0x38u << 24)) &&
+                    hi1 == ((old & 0xFFFFu) | (0x38u << 16) | (want << 24));
+    if (!ok) {
+      bad++;
+      first = min(first, u);
+    }
+  }
+  finish(bad, first, count, first_out);
+}
+
 }  // namespace
 
 // Each entry runs one sweep on `stream` and writes per-workgroup results into
 // count[] and first[] (device uint32 arrays of kvqc_workgroups(which) entries).
-// which: 0 fp4 encode, 1 bf16 rounding, 2 fp4 decode, 3 fp8 decode.
-extern "C" int kvqc_workgroups(int which) { return which <= 1 ? kWorkgroups : 1; }
+// which: 0 fp4 encode, 1 bf16 rounding, 2 fp4 decode, 3 fp8 decode, 4 fp8 encode.
+extern "C" int kvqc_workgroups(int which) { return which <= 1 || which == 4 ? kWorkgroups : 1; }
 
 extern "C" int kvqc_run(int which, uint32_t* count, uint32_t* first, void* stream) {
   hipStream_t s = (hipStream_t)stream;
@@ -236,6 +290,7 @@ extern "C" int kvqc_run(int which, uint32_t* count, uint32_t* first, void* strea
     case 1: hipLaunchKernelGGL(bf16_round_sweep, dim3(kWorkgroups), dim3(kThreads), 0, s, count, first); break;
     case 2: hipLaunchKernelGGL(fp4_decode_sweep, dim3(1), dim3(kThreads), 0, s, count, first); break;
     case 3: hipLaunchKernelGGL(fp8_decode_sweep, dim3(1), dim3(kThreads), 0, s, count, first); break;
+    case 4: hipLaunchKernelGGL(fp8_encode_sweep, dim3(kWorkgroups), dim3(kThreads), 0, s, count, first); break;
     default: return -1;
   }
   return (int)hipGetLastError();

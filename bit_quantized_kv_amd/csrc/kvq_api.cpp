@@ -376,6 +376,7 @@ kvq_status kvq_extend_attention_paged(const kvq_cache* cache, const int32_t* blo
   const int64_t rows = (int64_t)chunk_len * (num_q_heads / Hkv);
   if ((rows + 63) / 64 > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
   const kvq::SlabLayout lay = kvq::slab_layout(cache->fmt, cache->page_size, D);
+  if (lay.slab > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;  // a page's slab is addressed with 32-bit offsets
   kvq::ExtendParams p;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k_chunk;

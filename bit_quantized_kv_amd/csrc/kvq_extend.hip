@@ -292,13 +292,47 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
         reg[v].y = ld_global<uint32_t>(sc + (int64_t)off * 4);
     }
   };
+  // Steps whose rows all lie in the prefix: every 16-row half of such a step
+  // lies in one page (pages hold a multiple of 16 rows and steps start at
+  // multiples of 32), and the rows a wavefront stages are one half
+  // (wavefronts w mod 8 < 4: rows 0..15), so the half's page, its slab and
+  // the row offset are wave-uniform, scalar, and each lane adds a constant.
+  const int hs = (wave & 7) >> 2;
+  const int cvo = (krow0 & 15) * (D / 2) + 4 * kseg;  // lane's code bytes in its half's first row
+  const int svo = SRC == FMT_NVFP4 ? (krow0 & 15) * (D / 16) + ((kseg >> 1) & ~3) : (krow0 & 15) * 4;
+  auto half_slot = [&](int step, int& off) -> int {
+    const uint32_t t = (uint32_t)min((int64_t)step * kExtStep, (int64_t)0x7FFFFFC0) + 16u * (uint32_t)hs;
+    uint32_t pi = __umulhi(t, pmagic);
+    uint32_t o = t - pi * psz;
+    if (o >= psz) { o -= psz; pi++; }
+    off = (int)o;
+    return (int)pi;
+  };
+  // the page of this wavefront's half of a step, as page_id (the same value in every lane)
+  auto page_id16 = [&](int step) -> int {
+    int off;
+    return __builtin_amdgcn_raw_buffer_load_b32(pages_rsrc, 4 * half_slot(step, off), 0, 0);
+  };
+  auto load_paged_half = [&](u32x4_t(&reg)[KV16], int kv, int step, int pid) {
+    int off;
+    (void)half_slot(step, off);
+    const int spid = __builtin_amdgcn_readfirstlane(pid);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.pool + ((int64_t)spid * p.num_kv_heads + g) * p.slab), (short)0, (int)p.slab, 0x00020000);
+    const int cso = kv * (int)p.half + off * (D / 2);
+    const int sso = kv * (int)p.half + (int)p.scales_off + off * (SRC == FMT_NVFP4 ? D / 16 : 4);
+#pragma unroll
+    for (int v = 0; v < KV16; v++) {
+      reg[v].x = __builtin_amdgcn_raw_buffer_load_b32(rs, cvo + (D / 4) * v, cso, 0);
+      reg[v].y = __builtin_amdgcn_raw_buffer_load_b32(rs, svo + (SRC == FMT_NVFP4 ? (D / 32) * v : 0), sso, 0);
+    }
+  };
   // the loads of a step whose rows all lie in the prefix: no branch between
   // page and bf16 rows, so the loads land in their staging registers (a
   // register copy after a branch would wait for the load it copies)
   auto gload16 = [&](u32x4_t(&kr)[KV16], u32x4_t(&vr)[KV16], int step, int pid) {
-    const int64_t t0 = (int64_t)step * kExtStep;
-    load_paged_row(kr, 0, t0, pid);
-    load_paged_row(vr, 1, t0, pid);
+    load_paged_half(kr, 0, step, pid);
+    load_paged_half(vr, 1, step, pid);
   };
   // a bf16 row's staging registers (K: kv 0, V: kv 1)
   auto load_bf16_row = [&](u32x4_t(&reg)[KV16], int kv, int64_t t0) {
@@ -614,8 +648,8 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
       // entering: buffer 0 holds step 0, the first set the loads of step 1
       lstore16(kreg, vreg, 1);
       gload16(kreg, vreg, 2, pid);
-      gload16(kreg2, vreg2, 3, page_id(3));
-      int pid_a = page_id(4), pid_b = page_id(5);
+      gload16(kreg2, vreg2, 3, page_id16(3));
+      int pid_a = page_id16(4), pid_b = page_id16(5);
       __syncthreads();
       // the two staging wavefronts of a SIMD (w and w + 4) take the pair in
       // opposite orders -- stage then compute, compute then stage -- so one's
@@ -626,10 +660,10 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
       auto stage_pair = [&](int st) {
         lstore16(kreg, vreg, (st + 2) & 3);
         gload16(kreg, vreg, st + 4, pid_a);
-        pid_a = page_id(st + 6);
+        pid_a = page_id16(st + 6);
         lstore16(kreg2, vreg2, (st + 3) & 3);
         gload16(kreg2, vreg2, st + 5, pid_b);
-        pid_b = page_id(st + 7);
+        pid_b = page_id16(st + 7);
       };
       for (; st + 5 < nsteps16; st += 2) {
         if (stage_first) stage_pair(st);

@@ -266,7 +266,9 @@ kvq_status kvq_extend_attention(const void* q, int64_t q_token_stride, int32_t n
  * and values enter at their exact dequantized value; 32-key steps wholly inside
  * the prefix multiply in fp16 with each probability rounded to fp16 (relative
  * error at most 2^-12), later steps in bf16 with each probability split into
- * two bf16 terms; products are exact and accumulate in fp32. */
+ * two bf16 terms; products are exact and accumulate in fp32.  A page's slab
+ * (kvq_slab_bytes) must fit in 2^31 - 1 bytes, page sizes up to about seven
+ * million tokens (else KVQ_ERR_UNSUPPORTED). */
 kvq_status kvq_extend_attention_paged(const kvq_cache* cache, const int32_t* block_table_row, int32_t prefix_len,
                                       const void* q, int64_t q_token_stride, int32_t num_q_heads, const void* k_chunk,
                                       const void* v_chunk, int64_t chunk_token_stride, int32_t chunk_len,

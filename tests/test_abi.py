@@ -309,3 +309,7 @@ def test_extend_attention_paged_validation(lib):
     args = list(a)
     args[0] = ctypes.byref(bad)
     assert f(*args) != OK
+    huge = cache(P=16 * 1024 * 1024)                              # a slab past 2^31 bytes
+    args = list(a)
+    args[0] = ctypes.byref(huge)
+    assert f(*args) == ERR_UNSUPPORTED

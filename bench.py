@@ -703,6 +703,36 @@ def read_ceiling(torch, kvq, steps):
             "kernel": "kvq_stream_read: grid-stride 16-byte buffer loads (sc0 nt, as decode), 2048 workgroups"}
 
 
+def mfma_ceilings(torch, kvq, steps):
+    """Practical matrix-core ceilings of the extend kernels' product
+    (v_mfma_f32_16x16x32_f16, the fused extend's occupancy: 768-thread
+    workgroups, one per compute unit): operands in registers, and each
+    product's first operand read from LDS as the extend kernels read their key
+    and value rows.  512 workgroups x 2,000 iterations per call, timed like
+    the decode call."""
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wgs, iters = 512, 2000
+    flops = 16384.0 * 16 * 12 * iters * wgs
+    out = {}
+    for name, lds in (("registers", 0), ("lds_operand_per_product", 1)):
+        for _ in range(2):
+            kvq.kvq_mfma_rate(lds, iters, wgs, sink)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            kvq.kvq_mfma_rate(lds, iters, wgs, sink)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / steps * 1e3
+        tf = flops / (us * 1e-6) / 1e12
+        out[name] = {"tflops": tf, "frac_of_peak": tf / 2500.0, "us": us, "flops": flops}
+    out["kernel"] = ("kvq_mfma_rate: v_mfma_f32_16x16x32_f16, 512 workgroups of 768 threads, 16 products per "
+                     "wavefront and iteration into 4 accumulators; operands in registers, or the first from a "
+                     "16-byte LDS read per product")
+    return out
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -981,6 +1011,10 @@ def main():
     wc = write_copy_ceilings(torch, kvq, args.steps)
     print(f"[bench] plain streaming read: {ceiling['gbs']:.0f} GB/s, write {wc['write']['gbs']:.0f} GB/s, "
           f"copy {wc['copy']['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    mfma = mfma_ceilings(torch, kvq, args.steps)
+    print(f"[bench] f16 MFMA: {mfma['registers']['tflops']:.0f} TFLOP/s from registers, "
+          f"{mfma['lds_operand_per_product']['tflops']:.0f} TFLOP/s with one LDS operand per product",
+          file=sys.stderr, flush=True)
     secondary = {}
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
         t1 = time.time()
@@ -1021,6 +1055,12 @@ def main():
             dq = res["dequant_prefix"]
             dq["frac_of_copy_ceiling"] = dq["gbs"] / wc["copy"]["gbs"]
             dq["frac_of_write_ceiling"] = dq["gbs"] / wc["write"]["gbs"]
+    # the extend kernels against the measured matrix-core ceilings
+    for res in [main_res] + list(secondary.values()):
+        for k in ("extend_attention", "extend_attention_fused"):
+            for e in res.get(k, {}).values():
+                e["frac_of_register_mfma_ceiling"] = e["tflops"] / mfma["registers"]["tflops"]
+                e["frac_of_lds_fed_mfma_ceiling"] = e["tflops"] / mfma["lds_operand_per_product"]["tflops"]
     w = WORKLOADS[args.workload]
     r = main_res
     counters, counters_note = load_counter_summary(args.workload)
@@ -1055,6 +1095,7 @@ def main():
         "hbm_read_ceiling": ceiling,
         "hbm_write_ceiling": wc["write"],
         "hbm_copy_ceiling": wc["copy"],
+        "mfma_f16_ceiling": mfma,
         "cpu_baseline": cpu,
         "cpu_baseline_per_workload": {
             name: {k: res["cpu_baseline"][k] for k in ("value", "unit", "cores", "sample")}

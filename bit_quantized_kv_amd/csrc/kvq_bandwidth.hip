@@ -1,6 +1,9 @@
 // kvq_bandwidth.hip -- plain streaming read, write and copy kernels: the
 // practical HBM ceilings that the decode kernel (read), the bulk store and
-// the prefix dequantization (read + write, write-dominated) are compared with.
+// the prefix dequantization (read + write, write-dominated) are compared with;
+// and the matrix-core ceilings of the extend kernel's product.
+#include <mutex>
+
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -62,6 +65,95 @@ hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int wor
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t stream) {
   hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(256), 0, stream, (const uint8_t*)buf, bytes / 16,
                      sink);
+  return hipGetLastError();
+}
+
+// The extend kernel's product, v_mfma_f32_16x16x32_f16, at the extend
+// kernel's occupancy: 768-thread workgroups, three wavefronts per SIMD, one
+// workgroup per compute unit (96 KiB of LDS each).  Each wavefront issues 16
+// products per iteration into four independent accumulators.  LDS_FED = 0:
+// both operands in registers, the matrix cores' own ceiling.  LDS_FED = 1:
+// every product's first operand is a 16-byte LDS read per lane -- the extend
+// kernel's feed, which reads one such operand per product (its key rows for
+// QK, its value rows for PV) -- laid out as the extend kernel lays out its
+// key rows (rows 544 bytes apart, conflict-free), eight reads in flight.
+// Nothing leaves the kernel but a store to sink[0] that the sum practically
+// never triggers.
+constexpr int kMfmaRateThreads = 768;
+constexpr int kMfmaRateLds = 96 * 1024;
+
+template <int LDS_FED>
+__global__ __launch_bounds__(kMfmaRateThreads) void mfma_rate_kernel(int iters, uint32_t* sink) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_mem[];
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  lds_u8* const lds = (lds_u8*)lds_mem;
+  const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, n = lane & 15;
+  // three 32-row buffers of 544-byte rows: fp16 ones, slightly perturbed
+  for (int i = tid; i < 3 * 32 * 544 / 16; i += kMfmaRateThreads)
+    *(lds_u32x4*)(lds + 16 * i) = (u32x4_t){0x3C003C00u ^ (uint32_t)(i & 7), 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+  __syncthreads();
+  half8_t a, b;
+  for (int i = 0; i < 8; i++) {
+    a[i] = (_Float16)(0.001f * (float)(lane + i));
+    b[i] = (_Float16)(0.002f * (float)(lane - i));
+  }
+  float4_t acc[4];
+  for (int c = 0; c < 4; c++) acc[c] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  const int base = n * 544 + 16 * j;
+  for (int it = 0; it < iters; it++) {
+    const lds_u8* p = lds + (it % 3) * (32 * 544) + base;
+#pragma unroll
+    for (int m = 0; m < 16; m++) {
+      half8_t x = a;
+      if (LDS_FED) x = __builtin_bit_cast(half8_t, *(const lds_u32x4*)(p + 64 * (m & 7) + (m >> 3) * 16 * 544));
+      acc[m & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, b, acc[m & 3], 0, 0, 0);
+    }
+    if (LDS_FED) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+  }
+  float sum = 0.0f;
+  for (int c = 0; c < 4; c++) sum += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  if (sum == 1.0e-30f) sink[0] = 1u;
+}
+
+// The 96 KiB of dynamic LDS exceed HIP's default 64 KiB limit: raised once
+// per kernel and device, on its first launch there (the result is kept and
+// returned by every later launch).
+template <int LDS_FED>
+static hipError_t mfma_rate_lds_limit() {
+  constexpr int kDevices = 64;
+  static std::once_flag once[kDevices];
+  static hipError_t result[kDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) {
+    (void)hipGetLastError();
+    return hipFuncSetAttribute((const void*)mfma_rate_kernel<LDS_FED>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               kMfmaRateLds);
+  }
+  std::call_once(once[dev], [dev] {
+    result[dev] = hipFuncSetAttribute((const void*)mfma_rate_kernel<LDS_FED>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaRateLds);
+  });
+  return result[dev];
+}
+
+hipError_t launch_mfma_rate(int lds_fed, int iters, int workgroups, uint32_t* sink, hipStream_t stream) {
+  const hipError_t e = lds_fed ? mfma_rate_lds_limit<1>() : mfma_rate_lds_limit<0>();
+  if (e != hipSuccess) return e;
+  if (lds_fed)
+    hipLaunchKernelGGL(mfma_rate_kernel<1>, dim3(workgroups), dim3(kMfmaRateThreads), kMfmaRateLds, stream, iters,
+                       sink);
+  else
+    hipLaunchKernelGGL(mfma_rate_kernel<0>, dim3(workgroups), dim3(kMfmaRateThreads), kMfmaRateLds, stream, iters,
+                       sink);
   return hipGetLastError();
 }
 

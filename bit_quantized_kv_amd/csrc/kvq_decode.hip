@@ -534,7 +534,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
           // exponent (frexp: scale < 2^e) is an upper bound of its log2 that
           // keeps p * scale below 2^slack; clamped so tiny scales cannot push
           // exp2(s - max) out of fp32 range
-          cand[h][q] = x + (float)max(__builtin_amdgcn_frexp_exp(vsc[q]), -64);
+          cand[h][q] = x + (float)max(__builtin_amdgcn_frexp_expf(vsc[q]), -64);
         }
       }
     }

@@ -78,6 +78,12 @@ struct ExtLds {
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
+// LDS pointers typed in the LDS address space, so that offsets into the
+// staging buffers stay 32-bit (generic pointers carry 64-bit offsets,
+// which cost registers)
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 constexpr int kExtWorkspace = 0;  // SRC: every key from the bf16 workspace (else the cache format)
 
@@ -107,7 +113,8 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
   constexpr bool PAGED = SRC != kExtWorkspace;
   constexpr int KCH = D / 32, VT = D / 16;
   constexpr int KV16 = D / 128;      // 16-byte K vectors (staging passes) per thread and step
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_mem[];
+  lds_u8* const lds = (lds_u8*)lds_mem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane >> 4, n = lane & 15;
@@ -384,8 +391,8 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
   };
   auto lstore = [&](int buf, int64_t t0) {
     if (!stager) return;
-    uint8_t* base = lds + buf * Lds::BUF;
-    float* fac = (float*)(base + Lds::KB + Lds::VB);  // [K factors][V factors], one per token
+    lds_u8* base = lds + buf * Lds::BUF;
+    lds_f32* fac = (lds_f32*)(base + Lds::KB + Lds::VB);  // [K factors][V factors], one per token
     auto stage = [&](u32x4_t(&reg)[KV16], int kv) {
       if (PAGED) {
         const bool pg = t0 + krow0 < Lp;
@@ -400,10 +407,10 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
         }
         if (kseg == 0) fac[kv * kExtStep + krow0] = pg ? (SRC == FMT_NVFP4 ? gsf[kv] : as_f32(rs)) : 1.0f;
       }
-      uint8_t* rbase = base + kv * Lds::KB;
+      lds_u8* rbase = base + kv * Lds::KB;
 #pragma unroll
       for (int v = 0; v < KV16; v++)
-        *(u32x4_t*)(rbase + (krow_of(v) * Lds::KPD + kel_of(v) / 2) * 4) = reg[v];
+        *(lds_u32x4*)(rbase + (krow_of(v) * Lds::KPD + kel_of(v) / 2) * 4) = reg[v];
     };
     stage(kreg, 0);
     stage(vreg, 1);
@@ -418,8 +425,8 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
   // scale is staged as on the bf16 steps.
   auto lstore16 = [&](u32x4_t(&kr)[KV16], u32x4_t(&vr)[KV16], int buf) {
     if (!stager) return;
-    uint8_t* base = lds + buf * Lds::BUF;
-    float* fac = (float*)(base + Lds::KB + Lds::VB);
+    lds_u8* base = lds + buf * Lds::BUF;
+    lds_f32* fac = (lds_f32*)(base + Lds::KB + Lds::VB);
     auto stage = [&](u32x4_t(&reg)[KV16], int kv) {
       const uint32_t rs = reg[0].y;  // INT4 row scale
 #pragma unroll
@@ -443,10 +450,10 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
         }
       }
       if (SRC == FMT_INT4 && kseg == 0) fac[kv * kExtStep + krow0] = as_f32(rs);
-      uint8_t* rbase = base + kv * Lds::KB;
+      lds_u8* rbase = base + kv * Lds::KB;
 #pragma unroll
       for (int v = 0; v < KV16; v++)
-        *(u32x4_t*)(rbase + (krow_of(v) * Lds::KPD + kel_of(v) / 2) * 4) = reg[v];
+        *(lds_u32x4*)(rbase + (krow_of(v) * Lds::KPD + kel_of(v) / 2) * 4) = reg[v];
     };
     stage(kr, 0);
     stage(vr, 1);
@@ -485,8 +492,8 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
   // one step: F16 (a std::bool_constant) selects the fp16 prefix form
   auto compute = [&](auto f16_tag, int buf, int64_t t0) {
     constexpr bool F16 = decltype(f16_tag)::value;
-    const uint8_t* kb = lds + buf * Lds::BUF;
-    const uint8_t* vrows = kb + Lds::KB;
+    const lds_u8* kb = lds + buf * Lds::BUF;
+    const lds_u8* vrows = kb + Lds::KB;
     // the two 16-token halves are independent accumulation chains: their
     // products alternate, so neither waits on its own previous product
     float4_t sacc[2];
@@ -495,7 +502,7 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
     for (int m = 0; m < KCH; m++) {
 #pragma unroll
       for (int hh = 0; hh < 2; hh++) {
-        const u32x4_t a = *(const u32x4_t*)(kb + (16 * hh + n) * Lds::KPD * 4 + 16 * j + 64 * m);
+        const u32x4_t a = *(const lds_u32x4*)(kb + (16 * hh + n) * Lds::KPD * 4 + 16 * j + 64 * m);
         if constexpr (F16)
           sacc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
                                                             __builtin_bit_cast(half8_t, qw[m]), sacc[hh], 0, 0, 0);
@@ -513,8 +520,8 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     float s[8], vf[8], cand[8];
-    const float* kfac = (const float*)(kb + Lds::KB + Lds::VB);
-    const float* vfac = kfac + kExtStep;
+    const lds_f32* kfac = (const lds_f32*)(kb + Lds::KB + Lds::VB);
+    const lds_f32* vfac = kfac + kExtStep;
     float cmax = -__builtin_inff();
     // fp16 steps lie below every row's causal limit
     const bool masked = !F16 && t0 + kExtStep - 1 > lim_min;  // workgroup-uniform
@@ -533,7 +540,7 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
       // the product p' stays below 2^slack in fp16; the scale's binary
       // exponent (scale < 2^e) is the bound, clamped so that tiny scales
       // cannot push p out of fp32 range
-      if (F16 && SRC == FMT_INT4) cand[e] = x + (float)max(__builtin_amdgcn_frexp_exp(vf[e]), -64) * inv_sm;
+      if (F16 && SRC == FMT_INT4) cand[e] = x + (float)max(__builtin_amdgcn_frexp_expf(vf[e]), -64) * inv_sm;
     }
     // only steps that reach a row's causal limit need the mask (a
     // workgroup-uniform test, so the others skip it)
@@ -592,7 +599,7 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
     // and 16+4j..16+4j+3 (the order of P's k index), by two transposing reads:
     // lane (j, n) names channels 16t + 4(n%4) .. +3 of token row 4j + n/4
     // (then 16 + 4j + n/4) and receives channel 16t + n of the group's 4 rows
-    const uint8_t* vop = vrows + ((4 * j + (n >> 2)) * Lds::KPD + 2 * (n & 3)) * 4;
+    const lds_u8* vop = vrows + ((4 * j + (n >> 2)) * Lds::KPD + 2 * (n & 3)) * 4;
 #pragma unroll
     for (int t = 0; t < VT; t++) {
       const v4i16_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vop + 32 * t));
@@ -619,6 +626,8 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
   pid = page_id(1);
   if (nsteps > 1) gload(1, pid);
   pid = page_id(2);
+  // the page entry of step 3's half, for the second staging set of the paired prefix loop below
+  const int pid3 = PAGED ? page_id16(3) : 0;
   __syncthreads();
   // stage step st + 1 (in its own form) and issue the loads of step st + 2
   auto advance = [&](int st) {
@@ -645,11 +654,19 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
   int st = 0;
   if constexpr (F16P) {
     if (nsteps16 > 6) {
-      // entering: buffer 0 holds step 0, the first set the loads of step 1
+      // entering: buffer 0 holds step 0, the first set the loads of step 1.
+      // The loads leave in the loop's own order -- a set's 8 loads, then
+      // the page entry it uses next, then the other set's -- so that the
+      // compiler's wait counts, which must hold for the first iteration as
+      // for the others, wait for the entry alone and not for the other
+      // set's loads as well (the scheduling barriers keep the order).
       lstore16(kreg, vreg, 1);
       gload16(kreg, vreg, 2, pid);
-      gload16(kreg2, vreg2, 3, page_id16(3));
-      int pid_a = page_id16(4), pid_b = page_id16(5);
+      int pid_a = page_id16(4);
+      __builtin_amdgcn_sched_barrier(0);
+      gload16(kreg2, vreg2, 3, pid3);
+      int pid_b = page_id16(5);
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       // the two staging wavefronts of a SIMD (w and w + 4) take the pair in
       // opposite orders -- stage then compute, compute then stage -- so one's

@@ -94,5 +94,6 @@ hipError_t launch_extend(const ExtendParams& p, int head_dim, int src_fmt, hipSt
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
 hipError_t launch_stream_write(void* buf, int64_t bytes, uint32_t value, int workgroups, hipStream_t stream);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int workgroups, hipStream_t stream);
+hipError_t launch_mfma_rate(int lds_fed, int iters, int workgroups, uint32_t* sink, hipStream_t stream);
 
 }  // namespace kvq

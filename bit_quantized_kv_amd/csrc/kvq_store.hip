@@ -309,7 +309,7 @@ __global__ __launch_bounds__(256) void k8v4_store_kernel(StoreParams p) {
 __device__ inline float int4_near_half(float x, float s, float h) {
   const float d = __builtin_fmaf(-h, s, x);
   const float ah = __builtin_fabsf(h);
-  const int e = __builtin_amdgcn_frexp_exp(ah) - 1;  // ah in [2^e, 2^(e+1))
+  const int e = __builtin_amdgcn_frexp_expf(ah) - 1;  // ah in [2^e, 2^(e+1))
   const bool toward_zero = (d < 0.0f) == (h > 0.0f);
   const bool pow2 = ah == __builtin_ldexpf(1.0f, e);
   const float half_ulp_s = __builtin_ldexpf(s, e - 24 - ((toward_zero && pow2) ? 1 : 0));

@@ -66,6 +66,7 @@ def lib():
         "kvq_stream_read": (i32, [P, sz, P, i32, P]),
         "kvq_stream_write": (i32, [P, sz, ctypes.c_uint32, i32, P]),
         "kvq_stream_copy": (i32, [P, P, sz, i32, P]),
+        "kvq_mfma_rate": (i32, [i32, i32, i32, P, P]),
         "kvq_calibrate_amax": (i32, [C, P, P, i32, i64, i32, P, P]),
         "kvq_calibrate_global_scale": (i32, [C, P, P]),
         "kvq_hadamard_rotate": (i32, [P, i32, i64, P, i32, i64, i32, i32, P]),
@@ -232,6 +233,14 @@ def kvq_stream_copy(src: torch.Tensor, dst: torch.Tensor, num_workgroups: int = 
     assert dst.numel() * dst.element_size() == nbytes
     _check("kvq_stream_copy", lib().kvq_stream_copy(_ptr(src), _ptr(dst), nbytes // 16 * 16, int(num_workgroups),
                                                     _stream(stream)))
+
+
+def kvq_mfma_rate(lds_operands: int, iterations: int, num_workgroups: int, sink: torch.Tensor, stream=None):
+    """Matrix-core ceiling run: 16 v_mfma_f32_16x16x32_f16 per wavefront and iteration (16,384 flops each)
+    in num_workgroups 768-thread workgroups; lds_operands = 1 reads each product's first operand from LDS."""
+    assert sink.dtype in (torch.int32, torch.uint32) and sink.numel() >= 1
+    _check("kvq_mfma_rate", lib().kvq_mfma_rate(int(lds_operands), int(iterations), int(num_workgroups), _ptr(sink),
+                                                _stream(stream)))
 
 
 def kvq_calibrate_amax(cache: Cache, k: torch.Tensor, v: torch.Tensor, running_amax: torch.Tensor, stream=None):

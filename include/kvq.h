@@ -319,6 +319,21 @@ kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_
 kvq_status kvq_stream_write(void* buf, size_t bytes, uint32_t value, int32_t num_workgroups, void* stream);
 kvq_status kvq_stream_copy(const void* src, void* dst, size_t bytes, int32_t num_workgroups, void* stream);
 
+/* Measurement aid, likewise: the matrix-core ceilings against which the
+ * extend kernels' products are judged.  Runs num_workgroups workgroups of 768
+ * threads (three wavefronts per SIMD, one workgroup per compute unit, as the
+ * fused extend runs), each wavefront issuing 16 v_mfma_f32_16x16x32_f16 per
+ * iteration: 16 x 16 x 32 x 2 = 16,384 flops each, so one call is
+ * 16,384 x 16 x 12 x iterations x num_workgroups flops.  lds_operands = 0:
+ * operands in registers; 1: each product's first operand read from LDS
+ * (16 bytes per lane), as the extend kernels read their key and value rows.
+ * sink: device word, written only in the practically impossible case that the
+ * sum is 1e-30.  KVQ_ERR_NULL, KVQ_ERR_UNSUPPORTED (lds_operands not 0 or 1),
+ * KVQ_ERR_SHAPE (iterations or num_workgroups <= 0).  Asynchronous on
+ * `stream`. */
+kvq_status kvq_mfma_rate(int32_t lds_operands, int32_t iterations, int32_t num_workgroups, uint32_t* sink,
+                         void* stream);
+
 /* Static description of a status code. */
 const char* kvq_status_string(int32_t status);
 

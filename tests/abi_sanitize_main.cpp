@@ -205,6 +205,10 @@ int main() {
   CHECK("write null", kvq_stream_write(nullptr, 4096, 7u, 0, nullptr), KVQ_ERR_NULL, 0);
   CHECK("copy ok", kvq_stream_copy(F, off(F, 4096), 4096, 0, nullptr), KVQ_OK, 10);
   CHECK("copy align", kvq_stream_copy(F, off(F, 8), 4096, 0, nullptr), KVQ_ERR_ALIGN, 0);
+  CHECK("mfma ok", kvq_mfma_rate(1, 10, 4, (uint32_t*)F, nullptr), KVQ_OK, 11);
+  CHECK("mfma null", kvq_mfma_rate(0, 10, 4, nullptr, nullptr), KVQ_ERR_NULL, 0);
+  CHECK("mfma mode", kvq_mfma_rate(2, 10, 4, (uint32_t*)F, nullptr), KVQ_ERR_UNSUPPORTED, 0);
+  CHECK("mfma shape", kvq_mfma_rate(0, 0, 4, (uint32_t*)F, nullptr), KVQ_ERR_SHAPE, 0);
   for (int s = -8; s <= 1; s++) {
     const char* str = kvq_status_string(s);
     if (str == nullptr || str[0] == 0) {

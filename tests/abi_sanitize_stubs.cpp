@@ -10,7 +10,7 @@
 
 int g_launch_count = 0;
 int g_last_launch = 0;  // 1 store, 2 dequant, 3 amax, 4 global scale, 5 hadamard, 6 decode, 7 extend, 8 read,
-                        // 9 write, 10 copy
+                        // 9 write, 10 copy, 11 mfma rate
 
 namespace {
 hipError_t record(int kind) {
@@ -34,6 +34,7 @@ hipError_t launch_extend(const ExtendParams&, int, int, hipStream_t) { return re
 hipError_t launch_stream_read(const void*, int64_t, uint32_t*, int, hipStream_t) { return record(8); }
 hipError_t launch_stream_write(void*, int64_t, uint32_t, int, hipStream_t) { return record(9); }
 hipError_t launch_stream_copy(const void*, void*, int64_t, int, hipStream_t) { return record(10); }
+hipError_t launch_mfma_rate(int, int, int, uint32_t*, hipStream_t) { return record(11); }
 hipError_t decode_scratch(void** ptr) {
   *ptr = (void*)(uintptr_t)0x200000;  // a stand-in device address, never dereferenced
   return hipSuccess;

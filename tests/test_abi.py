@@ -190,6 +190,15 @@ def test_stream_read_validation(lib):
     assert lib.kvq_stream_read(FAKE, 64, FAKE + 2, 0, None) == ERR_ALIGN
 
 
+def test_mfma_rate_validation(lib):
+    f = lib.kvq_mfma_rate
+    assert f(0, 10, 4, None, None) == ERR_NULL
+    assert f(2, 10, 4, FAKE, None) == ERR_UNSUPPORTED
+    assert f(-1, 10, 4, FAKE, None) == ERR_UNSUPPORTED
+    assert f(1, 0, 4, FAKE, None) == ERR_SHAPE
+    assert f(1, 10, 0, FAKE, None) == ERR_SHAPE
+
+
 def test_calibration_validation(lib):
     c = cache()
     f = lib.kvq_calibrate_amax

@@ -78,9 +78,9 @@ struct ExtLds {
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
-// LDS pointers typed in the LDS address space, so that offsets into the
-// staging buffers stay 32-bit (generic pointers carry 64-bit offsets,
-// which cost registers)
+// LDS pointers typed in the LDS address space: every offset into the
+// staging buffers is 32-bit arithmetic by construction, without relying on
+// the compiler to infer the address space of generic pointers
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["kvq_store.hip", "kvq_decode.hip", "kvq_extend.hip", "kvq_bandwidth.hip", "kvq_api.cpp"]
+SOURCES = ["kvq_store.hip", "kvq_decode.hip", "kvq_extend.hip", "kvq_bandwidth.hip", "kvq_debug.hip", "kvq_api.cpp"]
 ARCH = "gfx950"
 
 COMMON = [

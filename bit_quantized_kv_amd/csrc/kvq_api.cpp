@@ -3,10 +3,12 @@
 // before anything touches the GPU, so a rejected call launches nothing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <atomic>
 
 #include "../../include/kvq.h"
+#include "kvq_debug.h"
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -42,6 +44,27 @@ kvq_status hip_status(hipError_t e) {
   if (e == hipSuccess) return KVQ_OK;
   g_last_hip_error = (int32_t)e;
   return KVQ_ERR_HIP;
+}
+
+// KVQ_DEBUG=1 (read on every call): check the device index arrays before
+// launching; the call then waits for its stream.
+bool debug_mode() {
+  const char* e = getenv("KVQ_DEBUG");
+  return e != nullptr && e[0] == '1' && e[1] == '\0';
+}
+
+kvq_status debug_status(hipError_t e, uint32_t bits) {
+  if (e != hipSuccess) return hip_status(e);
+  return bits != 0u ? KVQ_ERR_DEVICE_INPUT : KVQ_OK;
+}
+
+// the page ids of a single prefix row (dequant, fused extend)
+kvq_status debug_prefix_row(const kvq_cache* c, const int32_t* row, int32_t prefix_len, void* stream) {
+  if (!debug_mode() || prefix_len <= 0) return KVQ_OK;
+  uint32_t bits = 0u;
+  const hipError_t e = kvq::debug_check_pages(row, 0, 1, nullptr, prefix_len, prefix_len, c->page_size, c->num_pages,
+                                              (hipStream_t)stream, &bits);
+  return debug_status(e, bits);
 }
 
 // Compute units of the current device (queried once per device; 256, an
@@ -121,6 +144,14 @@ kvq_status decode_launch(const kvq_cache* cache, const void* q, int32_t num_q_he
                          int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                          float sm_scale, int32_t splits, void* out, int32_t out_dtype, float* lse_out,
                          void* workspace, void* stream) {
+  if (debug_mode()) {
+    uint32_t bits = 0u;
+    const kvq_status st = debug_status(
+        kvq::debug_check_pages(block_table, max_pages, batch, seq_lens, 0, max_seq_len, cache->page_size,
+                               cache->num_pages, (hipStream_t)stream, &bits),
+        bits);
+    if (st != KVQ_OK) return st;
+  }
   const kvq::SlabLayout lay = kvq::slab_layout(cache->fmt, cache->page_size, cache->head_dim);
   const int64_t chunks = ((int64_t)max_seq_len + 31) / 32;
   kvq::DecodeParams p;
@@ -176,6 +207,14 @@ kvq_status kvq_quantize_store(const kvq_cache* cache, const void* k, const void*
   if (in_token_stride < (int64_t)cache->num_kv_heads * cache->head_dim) return KVQ_ERR_SHAPE;
   const int64_t esize = in_dtype == KVQ_DT_F32 ? 4 : 2;
   if (!aligned16(k) || !aligned16(v) || (in_token_stride * esize) % 16 != 0) return KVQ_ERR_ALIGN;
+  if (debug_mode()) {
+    uint32_t bits = 0u;
+    const kvq_status dst = debug_status(
+        kvq::debug_check_slots(slot_mapping, num_tokens, (int64_t)cache->num_pages * cache->page_size,
+                               (hipStream_t)stream, &bits),
+        bits);
+    if (dst != KVQ_OK) return dst;
+  }
   const kvq::SlabLayout lay = kvq::slab_layout(cache->fmt, cache->page_size, cache->head_dim);
   kvq::StoreParams p;
   p.pool = (uint8_t*)cache->pool;
@@ -259,6 +298,8 @@ kvq_status kvq_dequant_prefix(const kvq_cache* cache, const int32_t* block_table
   if (block_table_row == nullptr || k_out == nullptr || v_out == nullptr) return KVQ_ERR_NULL;
   if (out_token_stride < (int64_t)cache->num_kv_heads * cache->head_dim) return KVQ_ERR_SHAPE;
   if (!aligned16(k_out) || !aligned16(v_out) || (out_token_stride * 2) % 16 != 0) return KVQ_ERR_ALIGN;
+  st = debug_prefix_row(cache, block_table_row, prefix_len, stream);
+  if (st != KVQ_OK) return st;
   const kvq::SlabLayout lay = kvq::slab_layout(cache->fmt, cache->page_size, cache->head_dim);
   kvq::DequantParams p;
   p.pool = (const uint8_t*)cache->pool;
@@ -377,6 +418,8 @@ kvq_status kvq_extend_attention_paged(const kvq_cache* cache, const int32_t* blo
   if ((rows + 63) / 64 > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
   const kvq::SlabLayout lay = kvq::slab_layout(cache->fmt, cache->page_size, D);
   if (lay.slab > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;  // a page's slab is addressed with 32-bit offsets
+  st = debug_prefix_row(cache, block_table_row, prefix_len, stream);
+  if (st != KVQ_OK) return st;
   kvq::ExtendParams p;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k_chunk;
@@ -472,6 +515,7 @@ const char* kvq_status_string(int32_t status) {
     case KVQ_ERR_WORKSPACE: return "workspace smaller than kvq_decode_workspace_size";
     case KVQ_ERR_HIP: return "HIP launch failed (see kvq_last_hip_error)";
     case KVQ_ERR_SCRATCH: return "decode partials exceed the static scratch of kvq_decode_attention_noalloc";
+    case KVQ_ERR_DEVICE_INPUT: return "a slot, page id or sequence length in a device array is out of range (KVQ_DEBUG)";
     default: return "unknown status";
   }
 }

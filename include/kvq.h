@@ -59,13 +59,14 @@
  * Conventions
  *   - The caller owns all memory.  The library allocates and frees nothing and
  *     keeps no state between calls beyond per-device constants it looks up
- *     once (compute-unit count, kernel attributes) and the static decode
+ *     once (compute-unit count, kernel attributes), the static decode
  *     scratch of kvq_decode_attention_noalloc (16 MiB per device, a device
- *     array of the library itself).
+ *     array of the library itself) and debug mode's 4-byte result word.
  *   - All work is enqueued on the caller's HIP stream (`stream`, a
  *     hipStream_t; NULL = the default stream) and is asynchronous.  The calls
  *     record nothing but kernel launches (no allocation, copy or memset), so
- *     they can be captured into a HIP graph and replayed.
+ *     they can be captured into a HIP graph and replayed (debug mode below
+ *     excepted).
  *   - Every host-checkable condition is validated before any launch; a
  *     failing call returns a negative kvq_status and launches nothing.  A
  *     failed launch returns KVQ_ERR_HIP; kvq_last_hip_error() then gives the
@@ -74,6 +75,17 @@
  *     validated: out-of-range values are undefined behaviour, as an
  *     out-of-bounds index would be.  Two tokens written to one slot in one call
  *     leave an unspecified winner.
+ *   - Debug mode: with the environment variable KVQ_DEBUG set to 1 (read on
+ *     every call), the calls that read device index arrays check them on the
+ *     device first -- kvq_quantize_store: every slot below num_pages *
+ *     page_size; the decode calls: every seq_lens[b] in [0, max_seq_len] and
+ *     the page ids those lengths use in [0, num_pages); kvq_dequant_prefix
+ *     and kvq_extend_attention_paged: the prefix's page ids in [0, num_pages)
+ *     -- then wait for the stream and return KVQ_ERR_DEVICE_INPUT, launching
+ *     nothing else, if any entry is out of range.  The check's result word is
+ *     a device word of the library (one per device, looked up once with
+ *     hipGetSymbolAddress); the call records a copy and a stream
+ *     synchronisation, so debug mode is for eager use, not graph capture.
  *   - Limits: head_dim in {128, 256}; page_size a positive multiple of 16;
  *     num_q_heads a multiple of num_kv_heads with group size <= 16; device
  *     pointers 16-byte aligned; token strides keep rows 16-byte aligned.
@@ -96,8 +108,10 @@ typedef enum {
   KVQ_ERR_ALIGN = -4,       /* a pointer or stride breaks 16-byte alignment */
   KVQ_ERR_WORKSPACE = -5,   /* workspace smaller than kvq_decode_workspace_size */
   KVQ_ERR_HIP = -6,         /* a HIP launch failed; see kvq_last_hip_error() */
-  KVQ_ERR_SCRATCH = -7      /* kvq_decode_attention_noalloc: the shape needs more
+  KVQ_ERR_SCRATCH = -7,     /* kvq_decode_attention_noalloc: the shape needs more
                                than its static scratch (16 MiB) */
+  KVQ_ERR_DEVICE_INPUT = -8 /* KVQ_DEBUG=1 only: a slot, page id or sequence
+                               length in a device array is out of range */
 } kvq_status;
 
 typedef enum { KVQ_FMT_NVFP4 = 1, KVQ_FMT_INT4_TOKHEAD = 2, KVQ_FMT_FP8_E4M3 = 3, KVQ_FMT_K8V4 = 4 } kvq_format;

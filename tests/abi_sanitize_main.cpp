@@ -7,11 +7,14 @@
 // are stand-in addresses that are never dereferenced.
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include "kvq.h"
 
 extern int g_launch_count;
 extern int g_last_launch;
+extern uint32_t g_debug_bits;
+extern int g_debug_checks;
 
 static int failures = 0;
 
@@ -209,6 +212,49 @@ int main() {
   CHECK("mfma null", kvq_mfma_rate(0, 10, 4, nullptr, nullptr), KVQ_ERR_NULL, 0);
   CHECK("mfma mode", kvq_mfma_rate(2, 10, 4, (uint32_t*)F, nullptr), KVQ_ERR_UNSUPPORTED, 0);
   CHECK("mfma shape", kvq_mfma_rate(0, 0, 4, (uint32_t*)F, nullptr), KVQ_ERR_SHAPE, 0);
+  // ---- debug mode: each call that reads device index arrays runs its check
+  // first; reported faults turn into KVQ_ERR_DEVICE_INPUT with no launch
+  {
+    const int32_t* T = (const int32_t*)F;
+    const int checks0 = g_debug_checks;
+    CHECK("no debug: store", kvq_quantize_store(&c, F, F, KVQ_DT_BF16, 1024, T, 4, nullptr), KVQ_OK, 1);
+    if (g_debug_checks != checks0) {
+      fprintf(stderr, "FAIL a check ran without KVQ_DEBUG\n");
+      failures++;
+    }
+    setenv("KVQ_DEBUG", "1", 1);
+    size_t dbytes = 0;
+    (void)kvq_decode_workspace_size(&c, 32, 24, 32768, 0, &dbytes);
+    for (uint32_t bits : {0u, 1u, 2u, 4u}) {
+      g_debug_bits = bits;
+      const int want = bits ? KVQ_ERR_DEVICE_INPUT : KVQ_OK;
+      CHECK("debug store", kvq_quantize_store(&c, F, F, KVQ_DT_BF16, 1024, T, 4, nullptr), want, bits ? 0 : 1);
+      CHECK("debug decode",
+            kvq_decode_attention(&c, F, 24, T, 2048, T, 32, 32768, 0.f, 0, F, 1, nullptr, F, dbytes, nullptr), want,
+            bits ? 0 : 6);
+      CHECK("debug noalloc",
+            kvq_decode_attention_noalloc(&c, F, 24, T, 2048, T, 32, 32768, 0.f, 0, F, 1, nullptr, nullptr), want,
+            bits ? 0 : 6);
+      CHECK("debug dequant", kvq_dequant_prefix(&c, T, 16, F, F, 1024, nullptr), want, bits ? 0 : 2);
+      CHECK("debug extend paged",
+            kvq_extend_attention_paged(&c, T, 100, F, 24 * 256, 24, F, F, 4 * 256, 8, 0.f, F, 1, 24 * 256, nullptr,
+                                       nullptr),
+            want, bits ? 0 : 7);
+    }
+    const int checks1 = g_debug_checks;
+    g_debug_bits = 1u;
+    CHECK("debug: invalid arguments fail before the check",
+          kvq_quantize_store(&c, F, F, 7, 1024, T, 4, nullptr), KVQ_ERR_UNSUPPORTED, 0);
+    CHECK("debug: no prefix, no check", kvq_dequant_prefix(&c, T, 0, F, F, 1024, nullptr), KVQ_OK, 0);
+    if (g_debug_checks != checks1) {
+      fprintf(stderr, "FAIL a check ran for a call rejected or empty on the host\n");
+      failures++;
+    }
+    setenv("KVQ_DEBUG", "0", 1);
+    CHECK("debug 0: store", kvq_quantize_store(&c, F, F, KVQ_DT_BF16, 1024, T, 4, nullptr), KVQ_OK, 1);
+    unsetenv("KVQ_DEBUG");
+    g_debug_bits = 0u;
+  }
   for (int s = -8; s <= 1; s++) {
     const char* str = kvq_status_string(s);
     if (str == nullptr || str[0] == 0) {

@@ -87,6 +87,12 @@ PAGED = [
     (2, 128, 1, 4, 80, 3333, 20, (1.0, 1.0)),
     # head dim 128 over many fp16 prefix steps (the two-deep loop)
     (1, 128, 2, 4, 16, 700, 50, (0.5, 2.0)),
+    # group sizes 1 (one query head per KV head; 200 rows over two workgroups),
+    # 8 (INT4, 32-token pages: a step's halves in one page) and 5 (385 rows: the
+    # last workgroup holds one row; the prefix ends mid-page and mid-step)
+    (1, 256, 4, 1, 16, 500, 200, (1.0, 1.0)),
+    (2, 256, 2, 8, 32, 900, 30, (1.0, 1.0)),
+    (1, 256, 1, 5, 16, 333, 77, (0.5, 1.0)),
 ]
 
 

@@ -93,6 +93,12 @@ PAGED = [
     (1, 256, 4, 1, 16, 500, 200, (1.0, 1.0)),
     (2, 256, 2, 8, 32, 900, 30, (1.0, 1.0)),
     (1, 256, 1, 5, 16, 333, 77, (0.5, 1.0)),
+    # around the paired prefix loop's threshold: 6 fp16 prefix steps (single
+    # steps only), 7 (one paired iteration) and 8 (the pair loop's exit into
+    # single steps)
+    (2, 256, 1, 4, 16, 200, 33, (1.0, 1.0)),
+    (1, 256, 2, 6, 16, 224, 40, (1.0, 1.0)),
+    (1, 128, 1, 6, 32, 256, 24, (0.25, 0.5)),
 ]
 
 

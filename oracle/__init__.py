@@ -30,20 +30,31 @@ K8V4 = 4  # FP8 (E4M3, per-tensor scale) keys with NVFP4 values
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libkvq_oracle.so")
+# KVQ_ORACLE_LIB names another build of the same source to load instead (the
+# test that plants mistakes in copies of the oracle loads each copy this way)
+_OTHER_LIB = os.environ.get("KVQ_ORACLE_LIB")
+_LIB_PATH = _OTHER_LIB or os.path.join(_HERE, "libkvq_oracle.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (IEEE fp32/fp64: no fast-math, no FMA
     contraction) and return the path of the shared library."""
+    if _OTHER_LIB:
+        return _LIB_PATH  # a build made elsewhere: never overwritten from this source
     if not force and os.path.exists(_LIB_PATH):
         return _LIB_PATH
-    cmd = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
-           "-shared", _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
-    subprocess.run(cmd, check=True)
+    compile_source(_SRC, _LIB_PATH + ".tmp")
     os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
     return _LIB_PATH
+
+
+def compile_source(src: str, out: str) -> None:
+    """gcc of one oracle source file into a shared library, with the flags the
+    oracle is always built with."""
+    cmd = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
+           "-shared", src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
 
 
 def _load():

@@ -39,13 +39,14 @@ def student_t4(g, shape):
 class FullLayer:
     """One layer at full size: cache filled on the GPU, inputs regenerable."""
 
-    def __init__(self, wid, fmt, B, L, P, shuffled, kind, chunk=1 << 16):
+    def __init__(self, wid, fmt, B, L, P, shuffled, kind, chunk=1 << 16, rotated=False):
         self.wid, self.fmt, self.B, self.L, self.P, self.kind = wid, fmt, B, L, P, kind
+        self.rotated = rotated
         self.pps = -(-L // P)
         self.num_pages = B * self.pps
         self.bt = inputs.page_tables(wid, B, self.pps, self.num_pages, shuffled=shuffled)
         self.bt_dev = torch.from_numpy(self.bt).cuda()
-        self.cache = kvq.Cache(fmt, self.num_pages, P, HKV, D, device="cuda")
+        self.cache = kvq.Cache(fmt, self.num_pages, P, HKV, D, device="cuda", rotated=rotated)
         self.cache.pool.fill_(0xFF)  # poison: bytes past each sequence stay NaN scales
         self.chunk = chunk
         self.samples = []  # (b, t, k_row [HKV][D], v_row) fp32 values of sampled tokens
@@ -95,6 +96,8 @@ class FullLayer:
             kc, ks, vc, vs = self.slab_rows(pool, b, t)
             for g in range(HKV):
                 for x, codes, scales in ((krow[g], kc[g], ks[g]), (vrow[g], vc[g], vs[g])):
+                    if self.rotated:  # a rotated cache stores the quantized R x
+                        x = oracle.hadamard(x[None])[0]
                     if self.fmt == 1:
                         rc, rs = oracle.nvfp4_quantize_row(x, 1.0)
                         assert np.array_equal(codes, rc) and np.array_equal(scales, rs), (b, t, g)
@@ -104,13 +107,16 @@ class FullLayer:
         return pool
 
     def check_decode(self, pool, seqs, heads_per_group=1, seed=0):
+        # a rotated cache is read with R q (as the bench does, rotated in bf16)
+        # and gives R o: both sides compared in the rotated domain
+        q = kvq.kvq_hadamard_rotate(self.q) if self.rotated else self.q
         out = torch.empty((self.B, HQ, D), dtype=torch.float32, device="cuda")
         lse = torch.empty((self.B, HQ), dtype=torch.float32, device="cuda")
-        kvq.kvq_decode_attention(self.cache, self.q, self.bt_dev, self.lens, self.L, out=out, lse=lse)
+        kvq.kvq_decode_attention(self.cache, q, self.bt_dev, self.lens, self.L, out=out, lse=lse)
         torch.cuda.synchronize()
         out, lse = out.cpu().numpy(), lse.cpu().numpy()
         rng = np.random.default_rng(seed)
-        qh = self.q.float().cpu().numpy()
+        qh = q.float().cpu().numpy()
         for b in seqs:
             heads = [g * G + int(x) for g in range(HKV) for x in rng.choice(G, heads_per_group, replace=False)]
             # the sequence's pages, renumbered, and one query per sampled head
@@ -269,6 +275,14 @@ def test_full_32k_k8v4_batch32():
             assert np.array_equal(vsec[row * (D // 2):(row + 1) * (D // 2)], rc), (b, t, g)
             sc0 = P * (D // 2) + row * (D // 16)
             assert np.array_equal(vsec[sc0:sc0 + D // 16], rs), (b, t, g)
+    lay.check_decode(pool, seqs=[0, 31], heads_per_group=1)
+
+
+def test_full_32k_rotated_nvfp4_batch32():
+    # the rotated workload of the benchmark: the headline shape with Hadamard-rotated rows
+    print("case: full 32K rotated NVFP4 layer", flush=True)
+    lay = FullLayer(10, 1, 32, 32768, 16, False, "lognormal", rotated=True)
+    pool = lay.check_packing()
     lay.check_decode(pool, seqs=[0, 31], heads_per_group=1)
 
 

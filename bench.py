@@ -708,14 +708,15 @@ def mfma_ceilings(torch, kvq, steps):
     (v_mfma_f32_16x16x32_f16, the fused extend's occupancy: 768-thread
     workgroups, one per compute unit): operands in registers, and each
     product's first operand read from LDS as the extend kernels read their key
-    and value rows.  512 workgroups x 2,000 iterations per call, timed like
-    the decode call."""
+    rows (QK), and the extend kernels' own mix of that and the value-row form
+    (PV: two transposing reads per operand).  512 workgroups x 2,000
+    iterations per call, timed like the decode call."""
     stream = torch.cuda.current_stream()
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     wgs, iters = 512, 2000
     flops = 16384.0 * 16 * 12 * iters * wgs
     out = {}
-    for name, lds in (("registers", 0), ("lds_operand_per_product", 1)):
+    for name, lds in (("registers", 0), ("lds_operand_per_product", 1), ("lds_qk_pv_mix", 2)):
         for _ in range(2):
             kvq.kvq_mfma_rate(lds, iters, wgs, sink)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -728,8 +729,9 @@ def mfma_ceilings(torch, kvq, steps):
         tf = flops / (us * 1e-6) / 1e12
         out[name] = {"tflops": tf, "frac_of_peak": tf / 2500.0, "us": us, "flops": flops}
     out["kernel"] = ("kvq_mfma_rate: v_mfma_f32_16x16x32_f16, 512 workgroups of 768 threads, 16 products per "
-                     "wavefront and iteration into 4 accumulators; operands in registers, or the first from a "
-                     "16-byte LDS read per product")
+                     "wavefront and iteration into 4 accumulators; operands in registers, the first from a "
+                     "16-byte LDS read per product, or products alternating between that read and two "
+                     "transposing 8-byte LDS reads (the extend kernels' QK and PV operand forms)")
     return out
 
 
@@ -1013,7 +1015,8 @@ def main():
           f"copy {wc['copy']['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     mfma = mfma_ceilings(torch, kvq, args.steps)
     print(f"[bench] f16 MFMA: {mfma['registers']['tflops']:.0f} TFLOP/s from registers, "
-          f"{mfma['lds_operand_per_product']['tflops']:.0f} TFLOP/s with one LDS operand per product",
+          f"{mfma['lds_operand_per_product']['tflops']:.0f} TFLOP/s with one LDS operand per product, "
+          f"{mfma['lds_qk_pv_mix']['tflops']:.0f} TFLOP/s with the extend's QK/PV operand mix",
           file=sys.stderr, flush=True)
     secondary = {}
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
@@ -1061,6 +1064,7 @@ def main():
             for e in res.get(k, {}).values():
                 e["frac_of_register_mfma_ceiling"] = e["tflops"] / mfma["registers"]["tflops"]
                 e["frac_of_lds_fed_mfma_ceiling"] = e["tflops"] / mfma["lds_operand_per_product"]["tflops"]
+                e["frac_of_operand_mix_mfma_ceiling"] = e["tflops"] / mfma["lds_qk_pv_mix"]["tflops"]
     w = WORKLOADS[args.workload]
     r = main_res
     counters, counters_note = load_counter_summary(args.workload)

@@ -500,7 +500,7 @@ kvq_status kvq_stream_copy(const void* src, void* dst, size_t bytes, int32_t num
 kvq_status kvq_mfma_rate(int32_t lds_operands, int32_t iterations, int32_t num_workgroups, uint32_t* sink,
                          void* stream) {
   if (sink == nullptr) return KVQ_ERR_NULL;
-  if (lds_operands != 0 && lds_operands != 1) return KVQ_ERR_UNSUPPORTED;
+  if (lds_operands < 0 || lds_operands > 2) return KVQ_ERR_UNSUPPORTED;
   if (iterations <= 0 || num_workgroups <= 0) return KVQ_ERR_SHAPE;
   return hip_status(kvq::launch_mfma_rate(lds_operands, iterations, num_workgroups, sink, (hipStream_t)stream));
 }

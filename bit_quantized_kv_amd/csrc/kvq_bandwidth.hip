@@ -71,22 +71,26 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, in
 // The extend kernel's product, v_mfma_f32_16x16x32_f16, at the extend
 // kernel's occupancy: 768-thread workgroups, three wavefronts per SIMD, one
 // workgroup per compute unit (96 KiB of LDS each).  Each wavefront issues 16
-// products per iteration into four independent accumulators.  LDS_FED = 0:
-// both operands in registers, the matrix cores' own ceiling.  LDS_FED = 1:
-// every product's first operand is a 16-byte LDS read per lane -- the extend
-// kernel's feed, which reads one such operand per product (its key rows for
-// QK, its value rows for PV) -- laid out as the extend kernel lays out its
-// key rows (rows 544 bytes apart, conflict-free), eight reads in flight.
-// Nothing leaves the kernel but a store to sink[0] that the sum practically
-// never triggers.
+// products per iteration into four independent accumulators.  MODE 0: both
+// operands in registers, the matrix cores' own ceiling.  MODE 1: every
+// product's first operand is a 16-byte LDS read per lane, laid out as the
+// extend kernel lays out its key rows (rows 544 bytes apart, conflict-free)
+// -- the QK operand form.  MODE 2: the extend kernel's own mix: products
+// alternate between that key-row read and the PV operand form, two
+// transposing 8-byte reads (ds_read_b64_tr_b16) of 4 tokens x 4 channels
+// each from the same token rows, at the extend kernel's lane addresses.
+// Modes 1 and 2 issue their reads eight operands ahead of the products.  Nothing leaves the kernel but
+// a store to sink[0] that the sum practically never triggers.
 constexpr int kMfmaRateThreads = 768;
 constexpr int kMfmaRateLds = 96 * 1024;
 
-template <int LDS_FED>
+template <int MODE>
 __global__ __launch_bounds__(kMfmaRateThreads) void mfma_rate_kernel(int iters, uint32_t* sink) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_mem[];
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  typedef short v4i16_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
   lds_u8* const lds = (lds_u8*)lds_mem;
   const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, n = lane & 15;
   // three 32-row buffers of 544-byte rows: fp16 ones, slightly perturbed
@@ -100,21 +104,42 @@ __global__ __launch_bounds__(kMfmaRateThreads) void mfma_rate_kernel(int iters, 
   }
   float4_t acc[4];
   for (int c = 0; c < 4; c++) acc[c] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-  const int base = n * 544 + 16 * j;
+  // key-row form: lane (j, n) reads 16 bytes at column j of row n.  Value
+  // form: lane (j, n) names 4 channels at byte 8 (n % 4) of token row
+  // 4 j + n / 4, then of row 16 + 4 j + n / 4; operand t adds 32 t bytes.  The
+  // furthest byte read, 2 x 17408 + (15 x 544 + 24) + 32 x 15 + 16 x 544 + 8,
+  // lies inside the three buffers (52,224 bytes).
+  const int kbase = n * 544 + 16 * j;
+  const int vbase = (4 * j + (n >> 2)) * 544 + 8 * (n & 3);
   for (int it = 0; it < iters; it++) {
-    const lds_u8* p = lds + (it % 3) * (32 * 544) + base;
+    const lds_u8* p = lds + (it % 3) * (32 * 544);
 #pragma unroll
     for (int m = 0; m < 16; m++) {
       half8_t x = a;
-      if (LDS_FED) x = __builtin_bit_cast(half8_t, *(const lds_u32x4*)(p + 64 * (m & 7) + (m >> 3) * 16 * 544));
+      if (MODE == 1 || (MODE == 2 && (m & 1) == 0)) {
+        const int k = MODE == 1 ? m : m >> 1;
+        x = __builtin_bit_cast(half8_t, *(const lds_u32x4*)(p + kbase + 64 * (k & 7) + (k >> 3) * 16 * 544));
+      } else if (MODE == 2) {
+        const lds_u8* vop = p + vbase + 32 * (m >> 1);
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)vop);
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vop + 16 * 544));
+        x = __builtin_bit_cast(half8_t, (u32x4_t){__builtin_bit_cast(u32x2_t, lo).x, __builtin_bit_cast(u32x2_t, lo).y,
+                                                  __builtin_bit_cast(u32x2_t, hi).x, __builtin_bit_cast(u32x2_t, hi).y});
+      }
       acc[m & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, b, acc[m & 3], 0, 0, 0);
     }
-    if (LDS_FED) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    // eight operands ahead: reads of operands 0..7 first (mode 2: 4 key-row
+    // reads and 4 x 2 transposing ones), then after each product the reads
+    // of the operand eight further on
+    if (MODE != 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, MODE == 1 ? 8 : 12, 0);
+      constexpr int kOdd = MODE == 1 ? 1 : 2;  // reads of an odd-numbered operand
 #pragma unroll
-      for (int i = 0; i < 8; i++) {
+      for (int i = 0; i < 4; i++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kOdd, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
@@ -127,7 +152,7 @@ __global__ __launch_bounds__(kMfmaRateThreads) void mfma_rate_kernel(int iters, 
 // The 96 KiB of dynamic LDS exceed HIP's default 64 KiB limit: raised once
 // per kernel and device, on its first launch there (the result is kept and
 // returned by every later launch).
-template <int LDS_FED>
+template <int MODE>
 static hipError_t mfma_rate_lds_limit() {
   constexpr int kDevices = 64;
   static std::once_flag once[kDevices];
@@ -135,26 +160,32 @@ static hipError_t mfma_rate_lds_limit() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) {
     (void)hipGetLastError();
-    return hipFuncSetAttribute((const void*)mfma_rate_kernel<LDS_FED>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    return hipFuncSetAttribute((const void*)mfma_rate_kernel<MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                kMfmaRateLds);
   }
   std::call_once(once[dev], [dev] {
-    result[dev] = hipFuncSetAttribute((const void*)mfma_rate_kernel<LDS_FED>,
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaRateLds);
+    result[dev] = hipFuncSetAttribute((const void*)mfma_rate_kernel<MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      kMfmaRateLds);
   });
   return result[dev];
 }
 
-hipError_t launch_mfma_rate(int lds_fed, int iters, int workgroups, uint32_t* sink, hipStream_t stream) {
-  const hipError_t e = lds_fed ? mfma_rate_lds_limit<1>() : mfma_rate_lds_limit<0>();
+template <int MODE>
+static hipError_t mfma_rate_launch(int iters, int workgroups, uint32_t* sink, hipStream_t stream) {
+  const hipError_t e = mfma_rate_lds_limit<MODE>();
   if (e != hipSuccess) return e;
-  if (lds_fed)
-    hipLaunchKernelGGL(mfma_rate_kernel<1>, dim3(workgroups), dim3(kMfmaRateThreads), kMfmaRateLds, stream, iters,
-                       sink);
-  else
-    hipLaunchKernelGGL(mfma_rate_kernel<0>, dim3(workgroups), dim3(kMfmaRateThreads), kMfmaRateLds, stream, iters,
-                       sink);
+  hipLaunchKernelGGL(mfma_rate_kernel<MODE>, dim3(workgroups), dim3(kMfmaRateThreads), kMfmaRateLds, stream, iters,
+                     sink);
   return hipGetLastError();
+}
+
+hipError_t launch_mfma_rate(int mode, int iters, int workgroups, uint32_t* sink, hipStream_t stream) {
+  switch (mode) {
+    case 0: return mfma_rate_launch<0>(iters, workgroups, sink, stream);
+    case 1: return mfma_rate_launch<1>(iters, workgroups, sink, stream);
+    case 2: return mfma_rate_launch<2>(iters, workgroups, sink, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace kvq

@@ -237,7 +237,8 @@ def kvq_stream_copy(src: torch.Tensor, dst: torch.Tensor, num_workgroups: int = 
 
 def kvq_mfma_rate(lds_operands: int, iterations: int, num_workgroups: int, sink: torch.Tensor, stream=None):
     """Matrix-core ceiling run: 16 v_mfma_f32_16x16x32_f16 per wavefront and iteration (16,384 flops each)
-    in num_workgroups 768-thread workgroups; lds_operands = 1 reads each product's first operand from LDS."""
+    in num_workgroups 768-thread workgroups; lds_operands = 1 reads each product's first operand from LDS in
+    the QK form (16-byte reads), 2 alternates that with the PV form (two transposing 8-byte reads)."""
     assert sink.dtype in (torch.int32, torch.uint32) and sink.numel() >= 1
     _check("kvq_mfma_rate", lib().kvq_mfma_rate(int(lds_operands), int(iterations), int(num_workgroups), _ptr(sink),
                                                 _stream(stream)))

@@ -339,10 +339,13 @@ kvq_status kvq_stream_copy(const void* src, void* dst, size_t bytes, int32_t num
  * fused extend runs), each wavefront issuing 16 v_mfma_f32_16x16x32_f16 per
  * iteration: 16 x 16 x 32 x 2 = 16,384 flops each, so one call is
  * 16,384 x 16 x 12 x iterations x num_workgroups flops.  lds_operands = 0:
- * operands in registers; 1: each product's first operand read from LDS
- * (16 bytes per lane), as the extend kernels read their key and value rows.
+ * operands in registers; 1: each product's first operand read from LDS as
+ * the extend kernels read their key rows for QK (one 16-byte read per lane);
+ * 2: the extend kernels' own mix, products alternating between that read and
+ * the PV operand form (two transposing 8-byte reads per lane of the value
+ * rows).  Modes 1 and 2 issue their reads eight operands ahead.
  * sink: device word, written only in the practically impossible case that the
- * sum is 1e-30.  KVQ_ERR_NULL, KVQ_ERR_UNSUPPORTED (lds_operands not 0 or 1),
+ * sum is 1e-30.  KVQ_ERR_NULL, KVQ_ERR_UNSUPPORTED (lds_operands not 0, 1 or 2),
  * KVQ_ERR_SHAPE (iterations or num_workgroups <= 0).  Asynchronous on
  * `stream`. */
 kvq_status kvq_mfma_rate(int32_t lds_operands, int32_t iterations, int32_t num_workgroups, uint32_t* sink,

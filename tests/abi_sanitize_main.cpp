@@ -210,7 +210,8 @@ int main() {
   CHECK("copy align", kvq_stream_copy(F, off(F, 8), 4096, 0, nullptr), KVQ_ERR_ALIGN, 0);
   CHECK("mfma ok", kvq_mfma_rate(1, 10, 4, (uint32_t*)F, nullptr), KVQ_OK, 11);
   CHECK("mfma null", kvq_mfma_rate(0, 10, 4, nullptr, nullptr), KVQ_ERR_NULL, 0);
-  CHECK("mfma mode", kvq_mfma_rate(2, 10, 4, (uint32_t*)F, nullptr), KVQ_ERR_UNSUPPORTED, 0);
+  CHECK("mfma mixed", kvq_mfma_rate(2, 10, 4, (uint32_t*)F, nullptr), KVQ_OK, 11);
+  CHECK("mfma mode", kvq_mfma_rate(3, 10, 4, (uint32_t*)F, nullptr), KVQ_ERR_UNSUPPORTED, 0);
   CHECK("mfma shape", kvq_mfma_rate(0, 0, 4, (uint32_t*)F, nullptr), KVQ_ERR_SHAPE, 0);
   // ---- debug mode: each call that reads device index arrays runs its check
   // first; reported faults turn into KVQ_ERR_DEVICE_INPUT with no launch

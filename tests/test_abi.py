@@ -193,8 +193,9 @@ def test_stream_read_validation(lib):
 def test_mfma_rate_validation(lib):
     f = lib.kvq_mfma_rate
     assert f(0, 10, 4, None, None) == ERR_NULL
-    assert f(2, 10, 4, FAKE, None) == ERR_UNSUPPORTED
+    assert f(3, 10, 4, FAKE, None) == ERR_UNSUPPORTED
     assert f(-1, 10, 4, FAKE, None) == ERR_UNSUPPORTED
+    assert f(2, 0, 4, FAKE, None) == ERR_SHAPE
     assert f(1, 0, 4, FAKE, None) == ERR_SHAPE
     assert f(1, 10, 0, FAKE, None) == ERR_SHAPE
 

@@ -44,10 +44,10 @@ def test_stream_write_and_copy_touch_exactly_their_bytes(n16, wgs):
     assert bool((dst[:n16] == src[:n16]).all()) and bool((dst[n16:] == -7).all())
 
 
-@pytest.mark.parametrize("lds", [0, 1])
+@pytest.mark.parametrize("lds", [0, 1, 2])
 def test_mfma_rate_runs_and_leaves_the_sink(lds):
     """The matrix-core ceiling kernel runs to completion through the C-ABI in
-    both operand modes (96 KiB of LDS per workgroup) and stores nothing: its
+    its three operand modes (96 KiB of LDS per workgroup) and stores nothing: its
     accumulated sum is never the 1e-30 that would write the sink."""
     print(f"case: mfma rate lds_operands {lds}", flush=True)
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")

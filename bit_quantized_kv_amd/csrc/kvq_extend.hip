@@ -90,11 +90,12 @@ constexpr int kExtWorkspace = 0;  // SRC: every key from the bf16 workspace (els
 // Wavefronts per workgroup, 16 query rows each.  The paged variant runs 12,
 // three per SIMD: the first 8 stage and compute, the other 4 compute and fill
 // the issue slots where the others wait on their products and operand
-// reads.  Those 4 still issue the staging loads -- the same addresses as the
-// first 4, lines the caches already hold -- and skip only the conversions
-// and LDS writes: with the loads behind a branch, every wavefront ran one
-// load sequence or another and the compiler waited for all loads in flight
-// where the paths joined.  (Measured against 8 wavefronts, 32K prefix: NVFP4
+// reads.  In the paired prefix loop those 4 run a loop of their own with no
+// loads; elsewhere they still issue the staging loads -- the same addresses
+// as the first 4, lines the caches already hold -- and skip only the
+// conversions and LDS writes: with the loads behind a branch inside a loop,
+// every wavefront ran one load sequence or another and the compiler waited
+// for all loads in flight where the paths joined.  (Measured against 8 wavefronts, 32K prefix: NVFP4
 // 4.60 -> 4.36 ms, INT4 4.91 -> 4.51 ms; INT4 220K prefix 30.2 -> 27.5 ms.)
 // The paged kernels are held to 168 registers, with a few spills; the
 // workspace variant (238 registers: its two-level output sums) keeps 8.
@@ -660,35 +661,51 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
       // compiler's wait counts, which must hold for the first iteration as
       // for the others, wait for the entry alone and not for the other
       // set's loads as well (the scheduling barriers keep the order).
-      lstore16(kreg, vreg, 1);
-      gload16(kreg, vreg, 2, pid);
-      int pid_a = page_id16(4);
-      __builtin_amdgcn_sched_barrier(0);
-      gload16(kreg2, vreg2, 3, pid3);
-      int pid_b = page_id16(5);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      // the two staging wavefronts of a SIMD (w and w + 4) take the pair in
-      // opposite orders -- stage then compute, compute then stage -- so one's
-      // conversions overlap the other's products instead of both queuing for
-      // the matrix core at once (w + 8, in the paged variant, computes; its
-      // loads repeat w's and nothing is staged from them)
-      const bool stage_first = wave >= 4;
-      auto stage_pair = [&](int st) {
-        lstore16(kreg, vreg, (st + 2) & 3);
-        gload16(kreg, vreg, st + 4, pid_a);
-        pid_a = page_id16(st + 6);
-        lstore16(kreg2, vreg2, (st + 3) & 3);
-        gload16(kreg2, vreg2, st + 5, pid_b);
-        pid_b = page_id16(st + 7);
-      };
-      for (; st + 5 < nsteps16; st += 2) {
-        if (stage_first) stage_pair(st);
-        compute(std::true_type{}, st & 3, (int64_t)st * kExtStep);
-        compute(std::true_type{}, (st + 1) & 3, (int64_t)(st + 1) * kExtStep);
-        if ((st + 2) % kExtFlush == 0) flush();  // st is even and kExtFlush a multiple of 2
-        if (!stage_first) stage_pair(st);
+      // Wavefronts 8.. stage nothing and run a loop of their own without the
+      // loads: with no staging registers live through its products, the
+      // compiler keeps four key-operand reads in flight there instead of one.
+      // Their staging registers hold constants on entry, so no loaded value
+      // has to survive their loop; the two loops meet once, after it.
+      if (stager) {
+        lstore16(kreg, vreg, 1);
+        gload16(kreg, vreg, 2, pid);
+        int pid_a = page_id16(4);
+        __builtin_amdgcn_sched_barrier(0);
+        gload16(kreg2, vreg2, 3, pid3);
+        int pid_b = page_id16(5);
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
+        // the two staging wavefronts of a SIMD (w and w + 4) take the pair in
+        // opposite orders -- stage then compute, compute then stage -- so
+        // one's conversions overlap the other's products instead of both
+        // queuing for the matrix core at once
+        const bool stage_first = wave >= 4;
+        auto stage_pair = [&](int st) {
+          lstore16(kreg, vreg, (st + 2) & 3);
+          gload16(kreg, vreg, st + 4, pid_a);
+          pid_a = page_id16(st + 6);
+          lstore16(kreg2, vreg2, (st + 3) & 3);
+          gload16(kreg2, vreg2, st + 5, pid_b);
+          pid_b = page_id16(st + 7);
+        };
+        for (; st + 5 < nsteps16; st += 2) {
+          if (stage_first) stage_pair(st);
+          compute(std::true_type{}, st & 3, (int64_t)st * kExtStep);
+          compute(std::true_type{}, (st + 1) & 3, (int64_t)(st + 1) * kExtStep);
+          if ((st + 2) % kExtFlush == 0) flush();  // st is even and kExtFlush a multiple of 2
+          if (!stage_first) stage_pair(st);
+          __syncthreads();
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < KV16; v++) kreg[v] = vreg[v] = (u32x4_t){0u, 0u, 0u, 0u};
+        __syncthreads();
+        for (; st + 5 < nsteps16; st += 2) {
+          compute(std::true_type{}, st & 3, (int64_t)st * kExtStep);
+          compute(std::true_type{}, (st + 1) & 3, (int64_t)(st + 1) * kExtStep);
+          if ((st + 2) % kExtFlush == 0) flush();
+          __syncthreads();
+        }
       }
       // back to one set: step st is computed here, step st + 1 is staged and
       // the first set holds the loads of step st + 2 (the second set's step

@@ -99,6 +99,11 @@ PAGED = [
     (2, 256, 1, 4, 16, 200, 33, (1.0, 1.0)),
     (1, 256, 2, 6, 16, 224, 40, (1.0, 1.0)),
     (1, 128, 1, 6, 32, 256, 24, (0.25, 0.5)),
+    # one chunk token over a long prefix: 6 rows, so every wavefront but the
+    # first holds padding rows -- the compute-only ones (their own paired loop,
+    # no loads) and the stagers alike
+    (1, 256, 1, 6, 16, 1500, 1, (1.0, 1.0)),
+    (2, 256, 2, 6, 16, 1500, 1, (1.0, 1.0)),
 ]
 
 

@@ -675,11 +675,15 @@ __global__ __launch_bounds__(ExtCfg<SRC>::THREADS) __attribute__((amdgpu_waves_p
         int pid_b = page_id16(5);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        // the two staging wavefronts of a SIMD (w and w + 4) take the pair in
-        // opposite orders -- stage then compute, compute then stage -- so
-        // one's conversions overlap the other's products instead of both
-        // queuing for the matrix core at once
-        const bool stage_first = wave >= 4;
+        // INT4: the two staging wavefronts of a SIMD (w and w + 4) take the
+        // pair in opposite orders -- stage then compute, compute then stage --
+        // so one's conversions overlap the other's products instead of both
+        // queuing for the matrix core at once.  NVFP4, whose compute-only
+        // wavefronts fill the matrix core while both stage: stage first
+        // (measured against the opposite orders in one run: NVFP4 4.10 ->
+        // 4.00 ms at 32K and 26.4 -> 25.8 ms at 256K; INT4 4.14 -> 4.49 ms
+        // at 32K).  Every order computes the same steps from the same buffers.
+        const bool stage_first = SRC == FMT_NVFP4 || wave >= 4;
         auto stage_pair = [&](int st) {
           lstore16(kreg, vreg, (st + 2) & 3);
           gload16(kreg, vreg, st + 4, pid_a);
